@@ -1,0 +1,166 @@
+"""CPU oracle for the future-attention-mass path — TEST INFRASTRUCTURE ONLY.
+
+Thin ctypes wrapper over ``kvp_oracle.cpp`` (plain fp64 C++).  Only the tests,
+the smoke check and the benchmark's CPU-baseline leg import this package; the
+GPU library and its Python binding never do.
+
+Every function cites what it follows in the C++ source header:
+  * logits / LSE: causal scaled softmax (LKV, §3 Preliminaries, Eq. 1) and the
+    per-query log-normaliser reused by KVpop §3.2 (Eq. 8);
+  * mass: KVpop §3.1 Eq. 2 un-normalised (App. B.1), summed over the group;
+  * keep-set: KVpop §3 Eq. 1 budget, Eq. 4 eligible set, Fig. 1.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kvp_oracle.cpp")
+_LIB_PATH = os.path.join(_HERE, "libkvp_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+DTYPE_BF16, DTYPE_F32_AS_BF16, DTYPE_F32_EXACT = 0, 1, 2
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB_PATH,
+          extra_flags: Sequence[str] = ()) -> str:
+    """Compile the oracle with g++ (-O2, no fast-math: IEEE fp64 throughout)."""
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
+        subprocess.check_call(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-pthread",
+                               *extra_flags, src, "-o", tmp])
+        os.replace(tmp, out)
+    return out
+
+
+def _bind(lib):
+    i64, vp, dbl, cint = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double, ctypes.c_int
+    lib.oracle_round_bf16.restype = cint
+    lib.oracle_round_bf16.argtypes = [vp, i64, vp]
+    lib.oracle_future_mass.restype = cint
+    lib.oracle_future_mass.argtypes = [vp, vp, cint, i64, i64, i64, i64, i64, dbl, i64,
+                                       i64, i64, i64, cint, vp, vp, vp, vp]
+    lib.oracle_lse_rows.restype = cint
+    lib.oracle_lse_rows.argtypes = [vp, vp, cint, i64, i64, i64, i64, i64, dbl, vp, i64, cint, vp]
+    lib.oracle_keep_count.restype = i64
+    lib.oracle_keep_count.argtypes = [i64, i64, i64, i64]
+    lib.oracle_select.restype = cint
+    lib.oracle_select.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp]
+    return lib
+
+
+def load(path: Optional[str] = None):
+    """Load the oracle library (building it first if it is missing).  A
+    non-default ``path`` loads a separately built variant (used by the tests
+    that plant mistakes in a copy of the oracle)."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                build(force=False)
+            _lib = _bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def default_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _dtype_code(arr: np.ndarray, f32_exact: bool) -> int:
+    if arr.dtype == np.uint16:
+        return DTYPE_BF16
+    if arr.dtype == np.float32:
+        return DTYPE_F32_EXACT if f32_exact else DTYPE_F32_AS_BF16
+    raise TypeError(f"unsupported input dtype {arr.dtype}")
+
+
+def round_bf16(x: np.ndarray, lib=None) -> np.ndarray:
+    lib = lib or load()
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    rc = lib.oracle_round_bf16(x.ctypes.data, x.size, out.ctypes.data)
+    assert rc == 0
+    return out
+
+
+def future_mass(q: np.ndarray, k: np.ndarray, window: int, scale: float = 0.0, *,
+                b_only: int = -1, h_only: int = -1, row_lo: int = 0,
+                f32_exact: bool = False, nthreads: Optional[int] = None, lib=None,
+                want_rowsum: bool = False, want_winmass: bool = False) -> dict:
+    """Dense causal softmax + future mass.  q: [B,Hq,S,D], k: [B,Hkv,S,D], as
+    bf16 bit patterns (uint16) or float32 (rounded to bf16 unless
+    ``f32_exact``).  Returns dict of fp64 arrays: lse [B,Hq,S], mass
+    [B,Hkv,S] (+ rowsum, winmass).  Entries outside a b_only/h_only/row_lo
+    restriction are NaN."""
+    lib = lib or load()
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    if q.dtype != k.dtype:
+        raise TypeError("q and k must have the same dtype")
+    B, Hq, S, D = q.shape
+    Bk, Hkv, Sk, Dk = k.shape
+    if (B, S, D) != (Bk, Sk, Dk):
+        raise ValueError("q/k shape mismatch")
+    lse = np.full((B, Hq, S), np.nan)
+    mass = np.full((B, Hkv, S), np.nan)
+    rowsum = np.full((B, Hq, S), np.nan) if want_rowsum else None
+    winmass = np.full((B, Hq, S), np.nan) if want_winmass else None
+    rc = lib.oracle_future_mass(
+        q.ctypes.data, k.ctypes.data, _dtype_code(q, f32_exact), B, Hq, Hkv, S, D,
+        float(scale), int(window), int(b_only), int(h_only), int(row_lo),
+        nthreads or default_threads(), lse.ctypes.data, mass.ctypes.data,
+        rowsum.ctypes.data if rowsum is not None else None,
+        winmass.ctypes.data if winmass is not None else None)
+    if rc != 0:
+        raise ValueError(f"oracle_future_mass rejected the arguments (rc={rc})")
+    out = {"lse": lse, "mass": mass}
+    if rowsum is not None:
+        out["rowsum"] = rowsum
+    if winmass is not None:
+        out["winmass"] = winmass
+    return out
+
+
+def lse_rows(q: np.ndarray, k: np.ndarray, rows: np.ndarray, scale: float = 0.0, *,
+             f32_exact: bool = False, nthreads: Optional[int] = None, lib=None) -> np.ndarray:
+    """LSE of selected (b, g, i) rows (int64 [n,3])."""
+    lib = lib or load()
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    out = np.empty(rows.shape[0], dtype=np.float64)
+    rc = lib.oracle_lse_rows(q.ctypes.data, k.ctypes.data, _dtype_code(q, f32_exact), B, Hq, Hkv,
+                             S, D, float(scale), rows.ctypes.data, rows.shape[0],
+                             nthreads or default_threads(), out.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_lse_rows rejected the arguments (rc={rc})")
+    return out
+
+
+def keep_count(S: int, window: int, n_sink: int, top_k: int, lib=None) -> int:
+    lib = lib or load()
+    return int(lib.oracle_keep_count(S, window, n_sink, top_k))
+
+
+def select(mass: np.ndarray, window: int, n_sink: int, top_k: int, lib=None) -> np.ndarray:
+    """Keep-set [B,Hkv,n_keep] (int32, ascending) from mass [B,Hkv,S]."""
+    lib = lib or load()
+    mass = np.ascontiguousarray(mass, dtype=np.float64)
+    B, Hkv, S = mass.shape
+    n_keep = keep_count(S, window, n_sink, top_k, lib)
+    keep = np.empty((B, Hkv, max(n_keep, 0)), dtype=np.int32)
+    rc = lib.oracle_select(mass.ctypes.data, B, Hkv, S, window, n_sink, top_k, keep.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_select failed (rc={rc})")
+    return keep

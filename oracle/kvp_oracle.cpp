@@ -1,0 +1,330 @@
+/*
+ * CPU ORACLE for the future-attention-mass path — TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow fp64 implementation of what the GPU library computes, used
+ * only to check it: the tests, the smoke check and the benchmark's CPU
+ * baseline load it; the library itself never does.  It shares no code,
+ * header, table or constant with the HIP path.
+ *
+ * Sources (cited by page title and section/equation):
+ *   [KVpop] "KVpop — Key-Value Cache Compression with Predictive Online
+ *           Pruning" (arXiv 2607.05061).
+ *   [LKV]   "LKV: End-to-End Learning of Head-wise Budgets and Token Selection
+ *           for LLM KV Cache Eviction" (arXiv 2605.06676).
+ *   [Tut]   the KV-compression tutorial page of the "transformer math" series
+ *           (aicassindra), sections "H2O: evict by accumulated attention" and
+ *           "StreamingLLM and the attention-sink surprise".
+ *
+ * What is computed, and from where:
+ *   logits  l(i,j) = scale * <q_i, k_j>, scale = 1/sqrt(d) by default, over
+ *           the causal prefix j <= i: the scaled dot-product causal softmax of
+ *           [LKV] §3 Preliminaries ("The KV Cache Bottleneck", Eq. 1).
+ *   LSE_i   log of the dense causal softmax normaliser of row i, the
+ *           "log-normalizer" that [KVpop] §3.2 (Eq. 8) reuses.
+ *   p(i->j) = softmax row i at column j = exp(l(i,j) - LSE_i).
+ *   mass    [KVpop] §3.1 Eq. 2 future-attention mass in its un-normalised form
+ *           of App. B.1 (sum of p(d->t) over d = t+w .. S-1, no 1/N_t), summed
+ *           over the G query heads that share KV head h.  App. B.1 averages
+ *           over the G heads; the plain sum ranks identically.
+ *   keep    [KVpop] §3 Eq. 1 (budget B = s + w + k per KV head) with Fig. 1
+ *           (sinks and protected recent window always kept, remaining slots to
+ *           the top-k long-range tokens) and Eq. 4 (eligible set at the last
+ *           query q = S-1: s <= t <= S-1-w).  Ties in mass go to the lower
+ *           index (no page addresses ties).
+ *
+ * Input dtypes: 0 = bfloat16 bit patterns; 1 = float32, rounded to bfloat16
+ * (round to nearest even) by this file's own routine before use, i.e. the
+ * values a bf16 kernel consumes; 2 = float32 used exactly.
+ *
+ * Parallelism does not change the arithmetic of a sum: the query rows of each
+ * (batch, query head) are split into a fixed number of interleaved row
+ * partitions, each with its own fp64 column buffer, and the buffers are added
+ * in a fixed order (query head, then partition).  Results do not depend on
+ * the thread count.
+ */
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <thread>
+#include <utility>
+#include <vector>
+
+namespace {
+
+constexpr int kRowBlock = 64;    // rows per block inside a partition
+constexpr int kPartitions = 16;  // fixed row partitions per (b, query head)
+
+// bfloat16 (bit pattern) -> double, exact.
+double bf16_to_double(uint16_t h) {
+  uint32_t u = static_cast<uint32_t>(h) << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return static_cast<double>(f);
+}
+
+// float32 -> bfloat16 bit pattern, round to nearest, ties to even.
+uint16_t float_to_bf16_rne(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7F800000u) == 0x7F800000u) {  // inf / nan: keep class
+    uint16_t r = static_cast<uint16_t>(u >> 16);
+    if ((u & 0x007FFFFFu) != 0) r |= 0x0040u;
+    return r;
+  }
+  uint32_t upper = u >> 16;
+  uint32_t lower = u & 0xFFFFu;
+  if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1;
+  return static_cast<uint16_t>(upper);
+}
+
+double load_elem(const void* base, int dtype, int64_t idx) {
+  if (dtype == 0) return bf16_to_double(static_cast<const uint16_t*>(base)[idx]);
+  const float f = static_cast<const float*>(base)[idx];
+  if (dtype == 1) return bf16_to_double(float_to_bf16_rne(f));
+  return static_cast<double>(f);
+}
+
+struct Dims {
+  int64_t B, Hq, Hkv, S, D;
+};
+
+// One causal softmax row: logits l(i, 0..i), the LSE and p(i->j) = e_j / Z.
+// kt is K of the row's KV head, transposed to [D][S] (so the dot products
+// for all j are formed column by column; each l(i,j) still accumulates
+// q[0]k[0] + q[1]k[1] + ... in index order).
+struct RowResult {
+  double lse;
+  double rowsum;
+};
+
+RowResult softmax_row(const double* qi, const double* kt, int64_t S, int64_t D, int64_t i,
+                      double scale, std::vector<double>& logit) {
+  const int64_t n = i + 1;
+  for (int64_t j = 0; j < n; ++j) logit[j] = 0.0;
+  for (int64_t c = 0; c < D; ++c) {
+    const double qc = qi[c];
+    const double* kc = kt + c * S;
+    for (int64_t j = 0; j < n; ++j) logit[j] += qc * kc[j];
+  }
+  double m = -INFINITY;
+  for (int64_t j = 0; j < n; ++j) {
+    logit[j] *= scale;
+    m = std::max(m, logit[j]);
+  }
+  double z = 0.0;
+  for (int64_t j = 0; j < n; ++j) {
+    logit[j] = std::exp(logit[j] - m);  // now e_j
+    z += logit[j];
+  }
+  double rowsum = 0.0;
+  for (int64_t j = 0; j < n; ++j) {
+    logit[j] /= z;  // now p(i->j)
+    rowsum += logit[j];
+  }
+  return {m + std::log(z), rowsum};
+}
+
+void widen_head(const void* src, int dtype, int64_t head_offset, int64_t S, int64_t D,
+                std::vector<double>& dst) {
+  dst.resize(static_cast<size_t>(S * D));
+  for (int64_t t = 0; t < S * D; ++t) dst[t] = load_elem(src, dtype, head_offset + t);
+}
+
+void transpose_head(const std::vector<double>& k, int64_t S, int64_t D, std::vector<double>& kt) {
+  kt.resize(static_cast<size_t>(S * D));
+  for (int64_t j = 0; j < S; ++j)
+    for (int64_t c = 0; c < D; ++c) kt[c * S + j] = k[j * D + c];
+}
+
+template <typename F>
+void parallel_items(int64_t n_items, int nthreads, F&& fn) {
+  if (nthreads < 1) nthreads = 1;
+  if (n_items < nthreads) nthreads = static_cast<int>(std::max<int64_t>(n_items, 1));
+  std::atomic<int64_t> next{0};
+  auto worker = [&]() {
+    for (;;) {
+      const int64_t it = next.fetch_add(1);
+      if (it >= n_items) break;
+      fn(it);
+    }
+  };
+  std::vector<std::thread> pool;
+  for (int t = 1; t < nthreads; ++t) pool.emplace_back(worker);
+  worker();
+  for (auto& th : pool) th.join();
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvp_oracle_abi_version() { return 1; }
+
+int oracle_round_bf16(const float* x, int64_t n, uint16_t* out) {
+  if ((!x || !out) && n > 0) return 1;
+  for (int64_t i = 0; i < n; ++i) out[i] = float_to_bf16_rne(x[i]);
+  return 0;
+}
+
+/* Dense causal softmax of every query row, its LSE, and the future mass.
+ *
+ *   lse[b,g,i]     = ln sum_{j<=i} exp(l_g(i,j))                  ([B,Hq,S])
+ *   mass[b,h,j]    = sum_{g: g/G = h} sum_{i >= j+window} p_g(i->j)  ([B,Hkv,S])
+ *   rowsum[b,g,i]  = sum_{j<=i} p_g(i->j)          (should be 1; optional)
+ *   winmass[b,g,i] = sum_{i-window < j <= i} p_g(i->j)  (in-window mass; optional)
+ *
+ * b_only / h_only >= 0 restrict the work to one batch element / KV head (the
+ * other outputs are left untouched); rows below row_lo are skipped, which
+ * leaves mass[j] exact for every j >= row_lo - window.  Any output pointer may
+ * be NULL.  Returns 0, or 1 on invalid arguments. */
+int oracle_future_mass(const void* q, const void* k, int dtype, int64_t B, int64_t Hq,
+                       int64_t Hkv, int64_t S, int64_t D, double scale, int64_t window,
+                       int64_t b_only, int64_t h_only, int64_t row_lo, int nthreads,
+                       double* lse, double* mass, double* rowsum, double* winmass) {
+  if (!q || !k || B < 0 || Hq < 1 || Hkv < 1 || S < 0 || D < 1 || Hq % Hkv != 0 ||
+      window < 0 || dtype < 0 || dtype > 2 || row_lo < 0)
+    return 1;
+  if (!(scale > 0.0)) scale = 1.0 / std::sqrt(static_cast<double>(D));
+  const int64_t G = Hq / Hkv;
+  const Dims dm{B, Hq, Hkv, S, D};
+
+  for (int64_t b = 0; b < dm.B; ++b) {
+    if (b_only >= 0 && b != b_only) continue;
+    for (int64_t h = 0; h < dm.Hkv; ++h) {
+      if (h_only >= 0 && h != h_only) continue;
+      std::vector<double> kh, kt;
+      widen_head(k, dtype, (b * Hkv + h) * S * D, S, D, kh);
+      transpose_head(kh, S, D, kt);
+      std::vector<std::vector<double>> qheads(static_cast<size_t>(G));
+      for (int64_t gg = 0; gg < G; ++gg)
+        widen_head(q, dtype, (b * Hq + h * G + gg) * S * D, S, D, qheads[gg]);
+
+      const int64_t n_items = G * kPartitions;
+      std::vector<std::vector<double>> colbuf(static_cast<size_t>(n_items));
+      parallel_items(n_items, nthreads, [&](int64_t item) {
+        const int64_t gg = item / kPartitions;
+        const int64_t part = item % kPartitions;
+        const int64_t g = h * G + gg;  // query head g uses KV head g / G
+        std::vector<double>& col = colbuf[item];
+        col.assign(static_cast<size_t>(S), 0.0);
+        std::vector<double> p(static_cast<size_t>(S > 0 ? S : 1));
+        const double* qbase = qheads[gg].data();
+        for (int64_t blk = part; blk * kRowBlock < S; blk += kPartitions) {
+          const int64_t i0 = blk * kRowBlock;
+          const int64_t i1 = std::min(S, i0 + kRowBlock);
+          for (int64_t i = std::max(i0, row_lo); i < i1; ++i) {
+            const RowResult rr = softmax_row(qbase + i * D, kt.data(), S, D, i, scale, p);
+            const int64_t o = (b * Hq + g) * S + i;
+            if (lse) lse[o] = rr.lse;
+            if (rowsum) rowsum[o] = rr.rowsum;
+            double win = 0.0;
+            // query i counts for key j iff i >= j + window ([KVpop] Eq. 2 lower limit d = t + w)
+            for (int64_t j = 0; j <= i; ++j) {
+              if (j + window <= i)
+                col[j] += p[j];
+              else
+                win += p[j];
+            }
+            if (winmass) winmass[o] = win;
+          }
+        }
+      });
+      if (mass) {
+        double* out = mass + (b * Hkv + h) * S;
+        for (int64_t j = 0; j < S; ++j) {
+          double acc = 0.0;
+          for (int64_t it = 0; it < n_items; ++it) acc += colbuf[it][j];
+          out[j] = acc;
+        }
+      }
+    }
+  }
+  return 0;
+}
+
+/* LSE of selected rows only: rows[3r .. 3r+2] = (b, g, i).  Each costs one
+ * causal row, O(i * D). */
+int oracle_lse_rows(const void* q, const void* k, int dtype, int64_t B, int64_t Hq, int64_t Hkv,
+                    int64_t S, int64_t D, double scale, const int64_t* rows, int64_t n_rows,
+                    int nthreads, double* lse_out) {
+  if (!q || !k || !rows || !lse_out || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || D < 1 ||
+      dtype < 0 || dtype > 2)
+    return 1;
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const int64_t b = rows[3 * r], g = rows[3 * r + 1], i = rows[3 * r + 2];
+    if (b < 0 || b >= B || g < 0 || g >= Hq || i < 0 || i >= S) return 1;
+  }
+  if (!(scale > 0.0)) scale = 1.0 / std::sqrt(static_cast<double>(D));
+  const int64_t G = Hq / Hkv;
+  parallel_items(n_rows, nthreads, [&](int64_t r) {
+    const int64_t b = rows[3 * r], g = rows[3 * r + 1], i = rows[3 * r + 2];
+    const int64_t h = g / G;
+    std::vector<double> qi(static_cast<size_t>(D));
+    for (int64_t c = 0; c < D; ++c) qi[c] = load_elem(q, dtype, ((b * Hq + g) * S + i) * D + c);
+    std::vector<double> logit(static_cast<size_t>(i + 1));
+    double m = -INFINITY;
+    for (int64_t j = 0; j <= i; ++j) {
+      double dot = 0.0;
+      for (int64_t c = 0; c < D; ++c) dot += qi[c] * load_elem(k, dtype, ((b * Hkv + h) * S + j) * D + c);
+      logit[j] = scale * dot;
+      m = std::max(m, logit[j]);
+    }
+    double z = 0.0;
+    for (int64_t j = 0; j <= i; ++j) z += std::exp(logit[j] - m);
+    lse_out[r] = m + std::log(z);
+  });
+  return 0;
+}
+
+/* Size of every KV head's keep-set: sinks [0, min(s,S)), window
+ * [max(0, S-w), S) and min(k, |eligible|) winners from [s, S-w). */
+int64_t oracle_keep_count(int64_t S, int64_t window, int64_t n_sink, int64_t top_k) {
+  if (S < 0 || window < 0 || n_sink < 0 || top_k < 0) return -1;
+  std::vector<char> kept(static_cast<size_t>(S), 0);
+  for (int64_t j = 0; j < S; ++j) {
+    if (j < n_sink) kept[j] = 1;
+    if (j >= S - window) kept[j] = 1;
+  }
+  int64_t eligible = 0;
+  for (int64_t j = n_sink; j < S - window; ++j) ++eligible;
+  int64_t n = std::min(top_k, eligible);
+  for (int64_t j = 0; j < S; ++j) n += kept[j];
+  return n;
+}
+
+/* Keep-set of every (b, KV head): ascending indices, n_keep per head.
+ * Eligible tokens are ordered by (mass descending, index ascending) with a
+ * full sort; the first min(k, |eligible|) are kept. */
+int oracle_select(const double* mass, int64_t B, int64_t Hkv, int64_t S, int64_t window,
+                  int64_t n_sink, int64_t top_k, int32_t* keep) {
+  if (B < 0 || Hkv < 1 || S < 0 || window < 0 || n_sink < 0 || top_k < 0) return 1;
+  if (S > 0 && B > 0 && (!mass || !keep)) return 1;
+  const int64_t n_keep = oracle_keep_count(S, window, n_sink, top_k);
+  for (int64_t bh = 0; bh < B * Hkv; ++bh) {
+    const double* m = mass + bh * S;
+    std::vector<char> kept(static_cast<size_t>(S), 0);
+    for (int64_t j = 0; j < std::min(n_sink, S); ++j) kept[j] = 1;
+    for (int64_t j = std::max<int64_t>(0, S - window); j < S; ++j) kept[j] = 1;
+    std::vector<std::pair<double, int64_t>> elig;
+    for (int64_t j = n_sink; j < S - window; ++j) elig.emplace_back(m[j], j);
+    std::sort(elig.begin(), elig.end(), [](const std::pair<double, int64_t>& a,
+                                           const std::pair<double, int64_t>& b) {
+      if (a.first != b.first) return a.first > b.first;
+      return a.second < b.second;
+    });
+    const int64_t take = std::min<int64_t>(top_k, static_cast<int64_t>(elig.size()));
+    for (int64_t r = 0; r < take; ++r) kept[elig[r].second] = 1;
+    int64_t w = 0;
+    for (int64_t j = 0; j < S; ++j)
+      if (kept[j]) {
+        if (w >= n_keep) return 2;
+        keep[bh * n_keep + w++] = static_cast<int32_t>(j);
+      }
+    if (w != n_keep) return 2;
+  }
+  return 0;
+}
+
+}  // extern "C"
