@@ -1,0 +1,174 @@
+"""Future-attention mass for KV-cache eviction on AMD MI355X (gfx950).
+
+Thin Python binding of ``libkvp.so`` (HIP kernels behind a C ABI declared in
+``include/kvp.h``).  It only marshals arguments: it checks torch tensors'
+device, dtype, shape and contiguity, and passes raw device pointers and the
+current HIP stream to the library.  Every step of the computation runs in the
+library's kernels; there is no fallback path.  If the library has not been
+built, importing works but every call raises.
+
+    lse  = lse_fwd(q, k)                          # [B, Hq, S]  fp32
+    mass = future_mass(q, k, lse, window)         # [B, Hkv, S] fp32
+    keep = select_topk(mass, window, n_sink, k)   # [B, Hkv, n_keep] int32
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+__all__ = ["lse_fwd", "future_mass", "select_topk", "keep_count", "KvpError", "library_path",
+           "load_library"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvp.so")
+_lock = threading.Lock()
+_lib = None
+
+KVP_BF16, KVP_F32 = 0, 1
+
+
+class KvpError(RuntimeError):
+    pass
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load_library():
+    """Load libkvp.so (built by ``build.py`` / ``__graft_entry__.build()``)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise KvpError(f"libkvp.so is not built ({LIB_PATH}); run build() first")
+            lib = ctypes.CDLL(LIB_PATH)
+            vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+            lib.kvp_lse_fwd.restype = ctypes.c_int
+            lib.kvp_lse_fwd.argtypes = [vp, vp, ctypes.c_int, _Dims, f32, vp, vp]
+            lib.kvp_future_mass.restype = ctypes.c_int
+            lib.kvp_future_mass.argtypes = [vp, vp, vp, ctypes.c_int, _Dims, f32, i32, vp, vp]
+            lib.kvp_keep_count.restype = i64
+            lib.kvp_keep_count.argtypes = [i64, i64, i64, i64]
+            lib.kvp_select_topk.restype = ctypes.c_int
+            lib.kvp_select_topk.argtypes = [vp, _Dims, i32, i32, i32, vp, vp]
+            lib.kvp_status_string.restype = ctypes.c_char_p
+            lib.kvp_status_string.argtypes = [ctypes.c_int]
+            lib.kvp_abi_version.restype = i32
+            lib.kvp_abi_version.argtypes = []
+            _lib = lib
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = load_library().kvp_status_string(status).decode()
+        raise KvpError(f"{what}: {msg} (status {status})")
+
+
+def _stream_ptr(stream: Optional[torch.cuda.Stream]) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KVP_BF16
+    if t.dtype == torch.float32:
+        return KVP_F32
+    raise KvpError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _require_device(*ts: torch.Tensor):
+    for t in ts:
+        if not t.is_cuda:
+            raise KvpError("tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise KvpError("tensors must be contiguous")
+
+
+def _dims(q: torch.Tensor, k: torch.Tensor) -> _Dims:
+    if q.dim() != 4 or k.dim() != 4:
+        raise KvpError("q and k must be [B, H, S, d]")
+    B, Hq, S, D = q.shape
+    Bk, Hkv, Sk, Dk = k.shape
+    if (B, S, D) != (Bk, Sk, Dk):
+        raise KvpError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)}")
+    if q.dtype != k.dtype:
+        raise KvpError("q and k must have the same dtype")
+    return _Dims(B, Hq, Hkv, S, D)
+
+
+def keep_count(seq_len: int, window: int, n_sink: int, top_k: int) -> int:
+    return int(load_library().kvp_keep_count(seq_len, window, n_sink, top_k))
+
+
+def lse_fwd(q: torch.Tensor, k: torch.Tensor, scale: float = 0.0,
+            out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Per-query causal log-sum-exp, fp32 [B, Hq, S] (natural log)."""
+    lib = load_library()
+    _require_device(q, k)
+    d = _dims(q, k)
+    if out is None:
+        out = torch.empty((d.batch, d.n_q_heads, d.seq_len), dtype=torch.float32, device=q.device)
+    _require_device(out)
+    if out.dtype != torch.float32 or tuple(out.shape) != (d.batch, d.n_q_heads, d.seq_len):
+        raise KvpError("lse out must be fp32 [B, Hq, S]")
+    _check(lib.kvp_lse_fwd(q.data_ptr(), k.data_ptr(), _dtype_code(q), d, float(scale),
+                           out.data_ptr(), _stream_ptr(stream)), "kvp_lse_fwd")
+    return out
+
+
+def future_mass(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, window: int,
+                scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """Future-attention mass per key, summed over each GQA group, fp32 [B, Hkv, S]."""
+    lib = load_library()
+    _require_device(q, k, lse)
+    d = _dims(q, k)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (d.batch, d.n_q_heads, d.seq_len):
+        raise KvpError("lse must be fp32 [B, Hq, S]")
+    if out is None:
+        out = torch.empty((d.batch, d.n_kv_heads, d.seq_len), dtype=torch.float32, device=q.device)
+    _require_device(out)
+    if out.dtype != torch.float32 or tuple(out.shape) != (d.batch, d.n_kv_heads, d.seq_len):
+        raise KvpError("mass out must be fp32 [B, Hkv, S]")
+    _check(lib.kvp_future_mass(q.data_ptr(), k.data_ptr(), lse.data_ptr(), _dtype_code(q), d,
+                               float(scale), int(window), out.data_ptr(), _stream_ptr(stream)),
+           "kvp_future_mass")
+    return out
+
+
+def select_topk(mass: torch.Tensor, window: int, n_sink: int, top_k: int,
+                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Keep-set per KV head, int32 [..., n_keep] ascending.  ``mass`` is
+    [B, Hkv, S] (any leading dims are flattened into rows)."""
+    lib = load_library()
+    _require_device(mass)
+    if mass.dtype != torch.float32 or mass.dim() < 1:
+        raise KvpError("mass must be fp32 [..., S]")
+    S = mass.shape[-1]
+    rows = mass.numel() // S if S else 0
+    n_keep = keep_count(S, window, n_sink, top_k)
+    if n_keep < 0:
+        raise KvpError("window, n_sink and top_k must be >= 0")
+    shape = (*mass.shape[:-1], n_keep)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.int32, device=mass.device)
+    _require_device(out)
+    if out.dtype != torch.int32 or tuple(out.shape) != shape:
+        raise KvpError(f"keep out must be int32 {shape}")
+    d = _Dims(rows, 1, 1, S, 128)
+    _check(lib.kvp_select_topk(mass.data_ptr(), d, int(window), int(n_sink), int(top_k),
+                               out.data_ptr(), _stream_ptr(stream)), "kvp_select_topk")
+    return out

@@ -1,0 +1,62 @@
+"""Build libkvp.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree."""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_PATH = os.path.join(HERE, "libkvp.so")
+
+SOURCES = ["kvp_api.cpp", "lse_kernel.hip", "mass_kernel.hip", "select_kernel.hip"]
+ARCH = "gfx950"
+
+# Packed fp32 VALU forms are disabled for every device compilation.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
+          "-Wall", "-Wno-unused-result"]
+
+
+def hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found (ROCm is required to build libkvp)")
+    return path
+
+
+def _run(cmd):
+    proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # hipcc's host pass does not know the device-only feature; drop that note.
+    noise = "packed-fp32-ops' is not a recognized feature"
+    out = "\n".join(l for l in proc.stdout.splitlines() if noise not in l)
+    if proc.returncode != 0:
+        raise RuntimeError(f"command failed ({proc.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source for gfx950 and link libkvp.so next to this file."""
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="kvp_build_") as tmp:
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
+            lang = ["-x", "hip"]
+            out = _run([cc, *lang, *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+            if verbose and out.strip():
+                print(out)
+            objs.append(obj)
+        tmp_lib = os.path.join(tmp, "libkvp.so")
+        _run([cc, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp_lib])
+        shutil.copyfile(tmp_lib, LIB_PATH + ".tmp")
+        os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

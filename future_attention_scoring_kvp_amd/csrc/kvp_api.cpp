@@ -1,0 +1,119 @@
+// C ABI of libkvp: argument validation, status codes and kernel launches.
+// Declarations and the contract of every entry point are in include/kvp.h.
+#include "kvp.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "kvp_launch.h"
+
+namespace {
+
+constexpr int32_t kAbiVersion = 1;
+// Limits that keep every index the kernels form in 32-bit ints.
+constexpr int64_t kMaxSeq = int64_t(1) << 28;
+constexpr int64_t kMaxBlocks = (int64_t(1) << 31) - 1;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Shared validation of the dims.  Returns KVP_OK and fills `sh`, or an error.
+kvp_status check_dims(const kvp_dims& d, bool need_heads_ratio, kvp::Shape& sh) {
+  if (d.batch < 0 || d.seq_len < 0 || d.n_q_heads < 1 || d.n_kv_heads < 1) return KVP_ERR_INVALID;
+  if (need_heads_ratio && d.n_q_heads % d.n_kv_heads != 0) return KVP_ERR_INVALID;
+  if (d.head_dim != 64 && d.head_dim != 128) return KVP_ERR_UNSUPPORTED;
+  if (d.seq_len > kMaxSeq) return KVP_ERR_UNSUPPORTED;
+  const int64_t units = int64_t(d.batch) * d.n_kv_heads;
+  if (units * ((int64_t(d.seq_len) + 63) / 64) * (d.n_q_heads / d.n_kv_heads) > kMaxBlocks)
+    return KVP_ERR_UNSUPPORTED;
+  sh.B = d.batch;
+  sh.Hq = d.n_q_heads;
+  sh.Hkv = d.n_kv_heads;
+  sh.S = d.seq_len;
+  sh.D = d.head_dim;
+  sh.G = d.n_q_heads / d.n_kv_heads;
+  return KVP_OK;
+}
+
+bool valid_dtype(kvp_dtype t) { return t == KVP_BF16 || t == KVP_F32; }
+
+float resolve_scale(float scale, int head_dim) {
+  return scale > 0.f ? scale : 1.0f / std::sqrt(static_cast<float>(head_dim));
+}
+
+kvp_status from_hip(hipError_t e) { return e == hipSuccess ? KVP_OK : KVP_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvp_abi_version(void) { return kAbiVersion; }
+
+const char* kvp_status_string(kvp_status s) {
+  switch (s) {
+    case KVP_OK: return "ok";
+    case KVP_ERR_INVALID: return "invalid argument";
+    case KVP_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVP_ERR_WORKSPACE: return "workspace too small";
+    case KVP_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+int64_t kvp_keep_count(int64_t S, int64_t w, int64_t s, int64_t k) {
+  if (S < 0 || w < 0 || s < 0 || k < 0) return -1;
+  const int64_t sinks = s < S ? s : S;
+  const int64_t win_lo = (S - w > s) ? S - w : s;  // window part not already a sink
+  const int64_t window = S > win_lo ? S - win_lo : 0;
+  const int64_t elig = S - w - s > 0 ? S - w - s : 0;
+  return sinks + window + (k < elig ? k : elig);
+}
+
+kvp_status kvp_lse_fwd(const void* q, const void* k, kvp_dtype dtype, kvp_dims dims, float scale,
+                       float* lse, hipStream_t stream) {
+  kvp::Shape sh;
+  const kvp_status st = check_dims(dims, true, sh);
+  if (st != KVP_OK) return st;
+  if (!valid_dtype(dtype)) return KVP_ERR_UNSUPPORTED;
+  if (std::isnan(scale) || std::isinf(scale)) return KVP_ERR_INVALID;
+  if (sh.B == 0 || sh.S == 0) return KVP_OK;
+  if (!q || !k || !lse || !aligned(q, 16) || !aligned(k, 16) || !aligned(lse, 4))
+    return KVP_ERR_INVALID;
+  return from_hip(kvp::launch_lse(q, k, dtype == KVP_BF16 ? 0 : 1, sh,
+                                  resolve_scale(scale, sh.D), lse, stream));
+}
+
+kvp_status kvp_future_mass(const void* q, const void* k, const float* lse, kvp_dtype dtype,
+                           kvp_dims dims, float scale, int32_t window, float* mass,
+                           hipStream_t stream) {
+  kvp::Shape sh;
+  const kvp_status st = check_dims(dims, true, sh);
+  if (st != KVP_OK) return st;
+  if (!valid_dtype(dtype)) return KVP_ERR_UNSUPPORTED;
+  if (std::isnan(scale) || std::isinf(scale) || window < 0) return KVP_ERR_INVALID;
+  if (sh.B == 0 || sh.S == 0) return KVP_OK;
+  if (!q || !k || !lse || !mass || !aligned(q, 16) || !aligned(k, 16) || !aligned(lse, 4) ||
+      !aligned(mass, 4))
+    return KVP_ERR_INVALID;
+  // A window beyond the sequence leaves no future query for any key.
+  const int w = window > sh.S ? sh.S : window;
+  return from_hip(kvp::launch_mass(q, k, lse, dtype == KVP_BF16 ? 0 : 1, sh,
+                                   resolve_scale(scale, sh.D), w, mass, stream));
+}
+
+kvp_status kvp_select_topk(const float* mass, kvp_dims dims, int32_t window, int32_t n_sink,
+                           int32_t top_k, int32_t* keep, hipStream_t stream) {
+  if (dims.batch < 0 || dims.seq_len < 0 || dims.n_kv_heads < 1) return KVP_ERR_INVALID;
+  if (window < 0 || n_sink < 0 || top_k < 0) return KVP_ERR_INVALID;
+  if (dims.seq_len > kMaxSeq) return KVP_ERR_UNSUPPORTED;
+  const int64_t rows = int64_t(dims.batch) * dims.n_kv_heads;
+  if (rows > kMaxBlocks) return KVP_ERR_UNSUPPORTED;
+  const int64_t n_keep = kvp_keep_count(dims.seq_len, window, n_sink, top_k);
+  if (rows == 0 || dims.seq_len == 0) return KVP_OK;
+  if (!mass || !keep || !aligned(mass, 4) || !aligned(keep, 4)) return KVP_ERR_INVALID;
+  const int S = dims.seq_len;
+  const int w = window > S ? S : window;
+  const int s = n_sink > S ? S : n_sink;
+  return from_hip(kvp::launch_select(mass, rows, S, w, s, top_k, n_keep, keep, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// Device-side building blocks shared by the gfx950 kernels of libkvp.
+//
+// Matrix-core tiles: v_mfma_f32_32x32x16_bf16.  For D = A (32 x 16) * B (16 x 32):
+//   lane l supplies A[l % 32][8*(l/32) + e] and B[8*(l/32) + e][l % 32], e = 0..7,
+//   and receives D[8*(v/4) + 4*(l/32) + (v%4)][l % 32] in result register v = 0..15.
+// Both kernels put KEYS on the rows (A operand) and QUERIES on the columns
+// (B operand), so each lane's 16 results share one query.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvp {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kBlk = 32;          // MFMA tile edge (rows = keys, cols = queries)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Row index (within a 32-row tile) of result register v of lane l.
+__device__ __forceinline__ int mfma_row(int v, int lane) {
+  return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+}
+
+__device__ __forceinline__ f32x16_t mfma_32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Eight consecutive input elements as eight bf16 values (16 bytes).  bf16
+// input is passed through; fp32 input is rounded to nearest even.
+__device__ __forceinline__ u32x4_t load8(const uint16_t* __restrict__ p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+__device__ __forceinline__ u32x4_t load8(const float* __restrict__ p) {
+  const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(p);
+  const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(p + 4);
+  bf16x8_t r;
+  r[0] = (__bf16)lo[0]; r[1] = (__bf16)lo[1]; r[2] = (__bf16)lo[2]; r[3] = (__bf16)lo[3];
+  r[4] = (__bf16)hi[0]; r[5] = (__bf16)hi[1]; r[6] = (__bf16)hi[2]; r[7] = (__bf16)hi[3];
+  return __builtin_bit_cast(u32x4_t, r);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Blocks are dispatched round-robin over the 8 XCDs (each with its own L2).
+// Map block `bid` to (unit, tile) so that every tile of a unit runs on one
+// XCD (units u with u % 8 == bid % 8) and each XCD receives tiles in order
+// 0, 1, 2, ... (tile 0 = the longest).  Falls back to tile-major order when
+// the unit count is not a multiple of 8.
+__device__ __forceinline__ void xcd_map(int bid, int n_units, int& unit, int& tile) {
+  if ((n_units & 7) == 0) {
+    const int xcd = bid & 7;
+    const int slot = bid >> 3;
+    const int per_xcd = n_units >> 3;
+    tile = slot / per_xcd;
+    unit = (slot - tile * per_xcd) * 8 + xcd;
+  } else {
+    tile = bid / n_units;
+    unit = bid - tile * n_units;
+  }
+}
+
+}  // namespace kvp

@@ -1,0 +1,23 @@
+// Internal launcher interface between the C ABI (kvp_api.cpp) and the kernel
+// translation units.  Arguments are already validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvp {
+
+struct Shape {
+  int B, Hq, Hkv, S, D;
+  int G;  // Hq / Hkv
+};
+
+// dtype: 0 = bf16, 1 = fp32 (rounded to bf16 on load).
+hipError_t launch_lse(const void* q, const void* k, int dtype, const Shape& sh, float scale,
+                      float* lse, hipStream_t stream);
+hipError_t launch_mass(const void* q, const void* k, const float* lse, int dtype, const Shape& sh,
+                       float scale, int window, float* mass, hipStream_t stream);
+hipError_t launch_select(const float* mass, int64_t rows, int S, int window, int n_sink,
+                         int top_k, int64_t n_keep, int32_t* keep, hipStream_t stream);
+
+}  // namespace kvp

@@ -1,0 +1,303 @@
+// Causal log-sum-exp pass for gfx950.
+//
+//   lse[b, g, i] = ln sum_{j <= i} exp(scale * <q_i, k_j>)
+// the dense causal normaliser of every query row (LKV §3 Eq. 1), i.e. the
+// per-query log-normaliser that KVpop §3.2 (Eq. 8) reuses for the future mass.
+//
+// Work decomposition (queries stationary, keys streamed):
+//   * one workgroup = 4 waves; each wave owns 64 consecutive query positions
+//     of one query head (two 32-column MFMA blocks kept as bf16 B-operands in
+//     registers); the 4 waves cover (position block, head) pairs of one GQA
+//     group, heads fastest, so the group's shared keys are staged once;
+//   * keys are streamed in blocks of 32 from position 0 upwards, 4 blocks per
+//     LDS stage, double buffered; every workgroup of a (batch, KV head) walks
+//     the same key sequence (shared L2), and workgroups run longest first;
+//   * per key block and wave: 16 MFMA 32x32x16 give a 32-key x 64-query tile;
+//     each lane (one query column) adds exp2(c*s - u) of its 16 values into
+//     one running sum.
+// The shift u of a row is the largest logit of its first key block (which
+// always holds key 0, valid for every row), so the running sum is >= 1 and
+// cannot underflow; it could only overflow if a later logit exceeded that by
+// more than ~88 (natural units).  Such rows are flagged (LSE = +inf) and
+// recomputed exactly by lse_fix_kernel, a max-then-sum pass per row.
+#include "kvp_device.h"
+#include "kvp_launch.h"
+
+namespace kvp {
+namespace {
+
+template <int D>
+struct LseCfg {
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = kWaves * kWave;
+  static constexpr int kQueriesPerWave = 64;
+  static constexpr int kSlots = 4;  // key blocks per LDS stage
+  static constexpr int kKSteps = D / 16;
+  static constexpr int kChunks = D / 8;
+  static constexpr int kRowStride = D * 2 + 16;
+  static constexpr int kSlotBytes = kBlk * kRowStride;
+  static constexpr int kStageBytes = kSlots * kSlotBytes;
+  static constexpr int kStageChunks = kSlots * kBlk * kChunks;
+  static constexpr int kChunksPerThread = kStageChunks / kThreads;
+  static_assert(kStageChunks % kThreads == 0, "stage must split evenly");
+};
+
+struct LseArgs {
+  const void* q;
+  const void* k;
+  float* lse;
+  int B, Hq, Hkv, S, G;
+  int n_wg;  // workgroups per (batch, KV head)
+  float c;   // scale * log2(e)
+};
+
+template <int D, typename T>
+__global__ __launch_bounds__(256, 2) void lse_kernel(LseArgs a) {
+  using C = LseCfg<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][C::kStageBytes];
+
+  const int S = a.S, G = a.G;
+  int unit, tile;
+  xcd_map(blockIdx.x, a.B * a.Hkv, unit, tile);
+  const int b = unit / a.Hkv;
+  const int h = unit - b * a.Hkv;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+
+  // (position block, head) pairs, heads fastest; tile 0 takes the last pairs
+  // (the longest rows).
+  const int n_pb = (S + C::kQueriesPerWave - 1) / C::kQueriesPerWave;
+  const int n_pairs = n_pb * G;
+  const int pair0 = (a.n_wg - 1 - tile) * C::kWaves;
+  const int my_pair = pair0 + wave;
+  const bool active = my_pair < n_pairs;
+  const int pb = my_pair / G;
+  const int g = my_pair - pb * G;
+  const int p0 = pb * C::kQueriesPerWave;
+
+  // Keys needed by the workgroup: [0, key_end).
+  const int last_pair = min(pair0 + C::kWaves, n_pairs) - 1;
+  const int key_end = min(S, (last_pair / G + 1) * C::kQueriesPerWave);
+  const int n_kb = (key_end + kBlk - 1) / kBlk;
+  const int n_stages = (n_kb + C::kSlots - 1) / C::kSlots;
+
+  const T* __restrict__ kbase = static_cast<const T*>(a.k) + (size_t)(b * a.Hkv + h) * S * D;
+  const T* __restrict__ qrow = static_cast<const T*>(a.q) + (size_t)(b * a.Hq + h * G + g) * S * D;
+
+  // Stationary queries: B-operands of the two 32-column blocks.
+  u32x4_t qf[2][C::kKSteps];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int i = p0 + 32 * cb + (lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < C::kKSteps; ++ks) {
+      const int col = 16 * ks + 8 * (lane >> 5);
+      qf[cb][ks] = (active && i < S) ? load8(qrow + (size_t)i * D + col) : u32x4_t{0, 0, 0, 0};
+    }
+  }
+
+  u32x4_t stage_regs[C::kChunksPerThread];
+  auto load_stage = [&](int st) {
+#pragma unroll
+    for (int t = 0; t < C::kChunksPerThread; ++t) {
+      const int cidx = tid + t * C::kThreads;
+      const int slot = cidx / (kBlk * C::kChunks);
+      const int row = (cidx / C::kChunks) % kBlk;
+      const int ch = cidx % C::kChunks;
+      const int j = (st * C::kSlots + slot) * kBlk + row;
+      stage_regs[t] = j < key_end ? load8(kbase + (size_t)j * D + ch * 8) : u32x4_t{0, 0, 0, 0};
+    }
+  };
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int t = 0; t < C::kChunksPerThread; ++t) {
+      const int cidx = tid + t * C::kThreads;
+      const int slot = cidx / (kBlk * C::kChunks);
+      const int row = (cidx / C::kChunks) % kBlk;
+      const int ch = cidx % C::kChunks;
+      *reinterpret_cast<u32x4_t*>(&k_lds[buf][slot * C::kSlotBytes + row * C::kRowStride + ch * 16]) =
+          stage_regs[t];
+    }
+  };
+
+  const float c = a.c;
+  float u0 = 0.f, u1 = 0.f;      // per-row shifts (log2 units)
+  float sum0 = 0.f, sum1 = 0.f;  // running sums of exp2(c*s - u)
+  const int iq0 = p0 + (lane & 31);
+  const int iq1 = iq0 + 32;
+
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+
+  for (int st = 0; st < n_stages; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < n_stages) load_stage(st + 1);
+
+#pragma unroll
+    for (int slot = 0; slot < C::kSlots; ++slot) {
+      const int kb = st * C::kSlots + slot;
+      if (kb >= n_kb) break;
+      const int k0 = kb * kBlk;
+      if (!active || k0 > p0 + C::kQueriesPerWave - 1) continue;  // above this wave's diagonal
+      const bool full = (k0 + kBlk - 1 <= p0) && (k0 + kBlk <= S);
+
+      const unsigned char* sbase = &k_lds[buf][slot * C::kSlotBytes + (lane & 31) * C::kRowStride];
+      f32x16_t s0 = {}, s1 = {};
+#pragma unroll
+      for (int ks = 0; ks < C::kKSteps; ++ks) {
+        const u32x4_t ak = *reinterpret_cast<const u32x4_t*>(sbase + (2 * ks + (lane >> 5)) * 16);
+        s0 = mfma_32x32x16(ak, qf[0][ks], s0);
+        s1 = mfma_32x32x16(ak, qf[1][ks], s1);
+      }
+
+      if (kb == 0) {
+        // Shift of each row: its largest valid logit in this first block.
+        float m0 = -__builtin_inff(), m1 = -__builtin_inff();
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int j = mfma_row(v, lane);
+          if (j <= iq0 && j < S) m0 = fmaxf(m0, s0[v]);
+          if (j <= iq1 && j < S) m1 = fmaxf(m1, s1[v]);
+        }
+        m0 = fmaxf(m0, __shfl_xor(m0, 32));
+        m1 = fmaxf(m1, __shfl_xor(m1, 32));
+        u0 = m0 * c;
+        u1 = m1 * c;
+      }
+
+      if (full) {
+        float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          t0 += fast_exp2(__builtin_fmaf(s0[v], c, -u0));
+          t1 += fast_exp2(__builtin_fmaf(s1[v], c, -u1));
+        }
+        sum0 += t0;
+        sum1 += t1;
+      } else {
+        float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int j = k0 + mfma_row(v, lane);
+          const float x0 = __builtin_fmaf(s0[v], c, -u0);
+          const float x1 = __builtin_fmaf(s1[v], c, -u1);
+          t0 += fast_exp2((j <= iq0 && j < S) ? x0 : -__builtin_inff());
+          t1 += fast_exp2((j <= iq1 && j < S) ? x1 : -__builtin_inff());
+        }
+        sum0 += t0;
+        sum1 += t1;
+      }
+    }
+
+    if (st + 1 < n_stages) store_stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Combine the two half-columns (lanes l and l^32 hold the same query).
+  sum0 += __shfl_xor(sum0, 32);
+  sum1 += __shfl_xor(sum1, 32);
+  if (active && lane < 32) {
+    float* out = a.lse + (size_t)(b * a.Hq + h * G + g) * S;
+    const float l0 = (u0 + __log2f(sum0)) * kLn2;
+    const float l1 = (u1 + __log2f(sum1)) * kLn2;
+    // A non-finite sum (overflow) is flagged as +inf for the exact fallback.
+    if (iq0 < S) out[iq0] = (sum0 < __builtin_inff() && l0 == l0) ? l0 : __builtin_inff();
+    if (iq1 < S) out[iq1] = (sum1 < __builtin_inff() && l1 == l1) ? l1 : __builtin_inff();
+  }
+}
+
+// Exact recomputation of the rows flagged +inf (or NaN) by lse_kernel: one
+// wave per flagged row, max pass then sum pass, fp32.  Rows that are finite
+// are left as they are; the kernel only reads them when nothing is flagged.
+template <int D, typename T>
+__global__ __launch_bounds__(256) void lse_fix_kernel(LseArgs a, float scale) {
+  const int64_t rows = (int64_t)a.B * a.Hq * a.S;
+  const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  bool flagged = false;
+  if (row < rows) {
+    const float v = a.lse[row];
+    flagged = !(v < __builtin_inff());
+  }
+  uint64_t mask = __ballot(flagged);
+  const int64_t wave_row0 = row - lane;
+  while (mask) {
+    const int bit = __builtin_ctzll(mask);
+    mask &= mask - 1;
+    const int64_t r = wave_row0 + bit;
+    const int i = (int)(r % a.S);
+    const int64_t bg = r / a.S;
+    const int gq = (int)(bg % a.Hq);
+    const int bb = (int)(bg / a.Hq);
+    const int hh = gq / a.G;
+    const T* qi = static_cast<const T*>(a.q) + ((size_t)(bb * a.Hq + gq) * a.S + i) * D;
+    const T* kh = static_cast<const T*>(a.k) + (size_t)(bb * a.Hkv + hh) * a.S * D;
+    float qv[D];
+#pragma unroll
+    for (int c8 = 0; c8 < D / 8; ++c8) {
+      const bf16x8_t e = __builtin_bit_cast(bf16x8_t, load8(qi + c8 * 8));
+#pragma unroll
+      for (int e8 = 0; e8 < 8; ++e8) qv[c8 * 8 + e8] = (float)e[e8];
+    }
+    auto logit = [&](int j) {
+      const T* kj = kh + (size_t)j * D;
+      float dot = 0.f;
+#pragma unroll
+      for (int c8 = 0; c8 < D / 8; ++c8) {
+        const bf16x8_t e = __builtin_bit_cast(bf16x8_t, load8(kj + c8 * 8));
+#pragma unroll
+        for (int e8 = 0; e8 < 8; ++e8) dot = __builtin_fmaf(qv[c8 * 8 + e8], (float)e[e8], dot);
+      }
+      return dot * scale;
+    };
+    float m = -__builtin_inff();
+    for (int j = lane; j <= i; j += 64) m = fmaxf(m, logit(j));
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    float s = 0.f;
+    for (int j = lane; j <= i; j += 64) s += __expf(logit(j) - m);
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) a.lse[r] = m + __logf(s);
+  }
+}
+
+template <int D, typename T>
+hipError_t launch_lse_t(const void* q, const void* k, const Shape& sh, float scale, float* lse,
+                        hipStream_t stream) {
+  using C = LseCfg<D>;
+  LseArgs a;
+  a.q = q;
+  a.k = k;
+  a.lse = lse;
+  a.B = sh.B;
+  a.Hq = sh.Hq;
+  a.Hkv = sh.Hkv;
+  a.S = sh.S;
+  a.G = sh.G;
+  a.c = scale * kLog2e;
+  const int64_t n_pb = (sh.S + C::kQueriesPerWave - 1) / C::kQueriesPerWave;
+  a.n_wg = (int)((n_pb * sh.G + C::kWaves - 1) / C::kWaves);
+  const int64_t blocks = (int64_t)a.n_wg * sh.B * sh.Hkv;
+  hipLaunchKernelGGL((lse_kernel<D, T>), dim3((unsigned)blocks), dim3(C::kThreads), 0, stream, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t rows = (int64_t)sh.B * sh.Hq * sh.S;
+  const int64_t fix_blocks = (rows + 255) / 256;
+  hipLaunchKernelGGL((lse_fix_kernel<D, T>), dim3((unsigned)fix_blocks), dim3(256), 0, stream, a,
+                     scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_lse(const void* q, const void* k, int dtype, const Shape& sh, float scale,
+                      float* lse, hipStream_t stream) {
+  if (sh.D == 128)
+    return dtype == 0 ? launch_lse_t<128, uint16_t>(q, k, sh, scale, lse, stream)
+                      : launch_lse_t<128, float>(q, k, sh, scale, lse, stream);
+  return dtype == 0 ? launch_lse_t<64, uint16_t>(q, k, sh, scale, lse, stream)
+                    : launch_lse_t<64, float>(q, k, sh, scale, lse, stream);
+}
+
+}  // namespace kvp

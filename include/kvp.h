@@ -1,0 +1,138 @@
+/*
+ * kvp.h — C ABI of the future-attention-mass library (libkvp.so), AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Three entry points compute the hot path of KVpop-style KV-cache eviction
+ * scoring for one attention layer, from its post-RoPE queries Q and keys K:
+ *
+ *   kvp_lse_fwd      per-query log-sum-exp of the dense causal attention row;
+ *   kvp_future_mass  future-attention mass of every key, summed over the query
+ *                    heads of its GQA group, without an S x S map;
+ *   kvp_select_topk  per-KV-head keep-set: sinks, recent window and the top-k
+ *                    older tokens by mass.
+ *
+ * Sources, cited by page title and section/equation:
+ *   [KVpop] "KVpop — Key-Value Cache Compression with Predictive Online
+ *           Pruning" (arXiv 2607.05061);
+ *   [LKV]   "LKV: End-to-End Learning of Head-wise Budgets and Token
+ *           Selection for LLM KV Cache Eviction" (arXiv 2605.06676);
+ *   [Tut]   the "transformer math" KV-compression tutorial (aicassindra),
+ *           sections "H2O: evict by accumulated attention" and
+ *           "StreamingLLM and the attention-sink surprise".
+ *
+ * Common conventions
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronises device memory; every call only
+ *     enqueues kernels on `stream` (NULL = the default stream) and returns.
+ *     Results are valid once the caller has synchronised that stream.
+ *   - Layouts are dense row-major: Q [B, Hq, S, d], K [B, Hkv, S, d] (d
+ *     fastest), LSE [B, Hq, S], mass [B, Hkv, S], keep [B, Hkv, n_keep].
+ *   - GQA: query head g reads KV head g / G, G = Hq / Hkv (contiguous groups;
+ *     [LKV] §3 "Problem Formulation": one retention mask per KV head, shared
+ *     by the query heads of its group).
+ *   - Logits are l(i, j) = scale * <q_i, k_j> with scale = 1/sqrt(d) when the
+ *     `scale` argument is <= 0 ([LKV] §3 Eq. 1).
+ *   - bf16 inputs are multiplied exactly and accumulated in fp32 on the
+ *     matrix cores; fp32 inputs are first rounded to bf16 (round to nearest
+ *     even) as they are loaded, so both dtypes run the same bf16 arithmetic.
+ *   - Validation is synchronous and happens before any launch; a rejected
+ *     call enqueues nothing.  No function prints, throws or aborts, and all
+ *     are thread-safe (no global state).
+ *   - Sizes: batch >= 0 and seq_len >= 0 (0 = empty input: nothing to do,
+ *     KVP_OK); n_q_heads, n_kv_heads >= 1 and n_q_heads % n_kv_heads == 0;
+ *     head_dim in {64, 128}.  Pointers must be 16-byte aligned.
+ */
+#ifndef KVP_H_
+#define KVP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVP_OK = 0,
+  KVP_ERR_INVALID = 1,      /* null/misaligned pointer, negative size, Hq % Hkv != 0, ... */
+  KVP_ERR_UNSUPPORTED = 2,  /* head_dim not in {64, 128}, unknown dtype, size beyond limits */
+  KVP_ERR_WORKSPACE = 3,    /* workspace too small */
+  KVP_ERR_HIP = 4           /* a kernel launch failed (hipGetLastError) */
+} kvp_status;
+
+typedef enum { KVP_BF16 = 0, KVP_F32 = 1 } kvp_dtype;
+
+typedef struct {
+  int32_t batch;       /* B  */
+  int32_t n_q_heads;   /* Hq */
+  int32_t n_kv_heads;  /* Hkv */
+  int32_t seq_len;     /* S  */
+  int32_t head_dim;    /* d  */
+} kvp_dims;
+
+/* Stage 1 — causal log-sum-exp.
+ *   lse[b, g, i] = ln sum_{j <= i} exp(scale * <q[b,g,i], k[b, g/G, j]>)
+ * The dense causal normaliser of each query row: the per-query
+ * log-normaliser that [KVpop] §3.2 (Eq. 8) reuses to recover attention
+ * probabilities, computed here for the dense causal softmax of [LKV] §3 Eq. 1
+ * (keys j <= i, diagonal included).  Natural log.
+ *   q, k  : device, dtype `dtype`, layouts above.
+ *   lse   : device fp32 [B, Hq, S], written entirely.
+ * Rows whose logits span more than the fp32 exponent range are recomputed by
+ * an exact per-row fallback, so every finite input yields a finite LSE. */
+kvp_status kvp_lse_fwd(const void* q, const void* k, kvp_dtype dtype, kvp_dims dims,
+                       float scale, float* lse, hipStream_t stream);
+
+/* Stage 2 — transposed future-attention-mass pass.
+ *   mass[b, h, j] = sum_{g : g/G = h} sum_{i = j + window}^{S-1}
+ *                     exp(scale * <q[b,g,i], k[b,h,j]> - lse[b,g,i])
+ * [KVpop] §3.1 Eq. 2 in the un-normalised form of App. B.1 (no 1/N_t),
+ * recovered from the LSE as in §3.2 Eq. 8, and summed over the G query heads
+ * of the group (App. B.1 averages; the sum ranks identically).  Query i
+ * counts for key j iff i >= j + window; mass[j] = 0 for j >= S - window.
+ * With window = 0 this is H2O accumulated attention ([Tut], "H2O").
+ *   lse    : device fp32 [B, Hq, S] as written by kvp_lse_fwd (natural log).
+ *   window : w >= 0.
+ *   mass   : device fp32 [B, Hkv, S], written entirely.
+ * Each key is owned by one workgroup, which reduces over all its future
+ * queries on chip: no atomics, and the result is bitwise reproducible. */
+kvp_status kvp_future_mass(const void* q, const void* k, const float* lse, kvp_dtype dtype,
+                           kvp_dims dims, float scale, int32_t window, float* mass,
+                           hipStream_t stream);
+
+/* Size of every KV head's keep-set ([KVpop] §3 Eq. 1, budget B = s + w + k,
+ * clipped to the sequence):
+ *   min(s, S) + |[max(s, S - w), S)| + min(k, max(0, S - w - s)).
+ * Pure host function; returns -1 for negative arguments. */
+int64_t kvp_keep_count(int64_t seq_len, int64_t window, int64_t n_sink, int64_t top_k);
+
+/* Stage 3 — per-KV-head keep-set.
+ *   keep[b, h, :] = ascending( [0, min(s, S))                       sinks
+ *                            U [max(0, S - w), S)                  window
+ *                            U top-k of { mass[b,h,j] : s <= j < S - w } )
+ * [KVpop] Fig. 1 (sinks and the protected window are always retained, the
+ * remaining budget goes to the top-k long-range tokens), Eq. 1 (budget) and
+ * Eq. 4 (eligible set at the last query: s <= t <= S-1-w); the StreamingLLM
+ * sink rule of [Tut].  Order: mass descending, equal masses by ascending
+ * index (lower index wins).  Masses must be >= 0 and not NaN (as written by
+ * kvp_future_mass); selection compares their fp32 bit patterns exactly.
+ *   mass : device fp32 [B, Hkv, S] (the batch dimension may also stack
+ *          layers: any number of independent [Hkv, S] rows).
+ *   keep : device int32 [B, Hkv, kvp_keep_count(S, window, n_sink, top_k)].
+ *   dims : only batch, n_kv_heads and seq_len are read. */
+kvp_status kvp_select_topk(const float* mass, kvp_dims dims, int32_t window, int32_t n_sink,
+                           int32_t top_k, int32_t* keep, hipStream_t stream);
+
+/* Static string for a status code. */
+const char* kvp_status_string(kvp_status status);
+
+/* Library ABI version (incremented on any signature change). */
+int32_t kvp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVP_H_ */

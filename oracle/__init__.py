@@ -31,10 +31,10 @@ DTYPE_BF16, DTYPE_F32_AS_BF16, DTYPE_F32_EXACT = 0, 1, 2
 
 def build(force: bool = True, src: str = _SRC, out: str = _LIB_PATH,
           extra_flags: Sequence[str] = ()) -> str:
-    """Compile the oracle with g++ (-O2, no fast-math: IEEE fp64 throughout)."""
+    """Compile the oracle with g++ (-O3, no fast-math, no FMA contraction: plain IEEE fp64)."""
     if force or not os.path.exists(out):
         tmp = out + ".tmp"
-        subprocess.check_call(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-pthread",
+        subprocess.check_call(["g++", "-O3", "-ffp-contract=off", "-std=c++17", "-fPIC", "-shared", "-pthread",
                                *extra_flags, src, "-o", tmp])
         os.replace(tmp, out)
     return out

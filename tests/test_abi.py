@@ -1,0 +1,125 @@
+"""C ABI of libkvp.so, checked without a GPU: the library loads, exports every
+function declared in include/kvp.h, and rejects invalid arguments before any
+launch.  No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import future_attention_scoring_kvp_amd as kvp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvp.h")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+FAKE = 0x100000  # never dereferenced: every call below fails validation or is empty
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvp_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kvp.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return kvp.load_library()
+
+
+def test_header_declares_the_three_stages():
+    names = declared_functions()
+    for n in ("kvp_lse_fwd", "kvp_future_mass", "kvp_select_topk", "kvp_keep_count",
+              "kvp_status_string", "kvp_abi_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in kvp.h but not exported"
+
+
+def test_abi_version_and_strings(lib):
+    assert lib.kvp_abi_version() == 1
+    for code in range(5):
+        assert lib.kvp_status_string(code)
+    assert lib.kvp_status_string(99) == b"unknown status"
+
+
+def dims(B=1, Hq=4, Hkv=2, S=64, D=128):
+    return kvp._Dims(B, Hq, Hkv, S, D)
+
+
+def lse_call(lib, q=FAKE, k=FAKE, dtype=0, d=None, scale=0.0, out=FAKE):
+    return lib.kvp_lse_fwd(q, k, dtype, d or dims(), scale, out, None)
+
+
+def mass_call(lib, q=FAKE, k=FAKE, lse=FAKE, dtype=0, d=None, scale=0.0, w=4, out=FAKE):
+    return lib.kvp_future_mass(q, k, lse, dtype, d or dims(), scale, w, out, None)
+
+
+def test_lse_validation(lib):
+    assert lse_call(lib, q=None) == INVALID
+    assert lse_call(lib, k=None) == INVALID
+    assert lse_call(lib, out=None) == INVALID
+    assert lse_call(lib, q=FAKE + 8) == INVALID           # q not 16-byte aligned
+    assert lse_call(lib, out=FAKE + 2) == INVALID         # lse not 4-byte aligned
+    assert lse_call(lib, d=dims(Hq=3, Hkv=2)) == INVALID  # Hq % Hkv
+    assert lse_call(lib, d=dims(Hkv=0)) == INVALID
+    assert lse_call(lib, d=dims(B=-1)) == INVALID
+    assert lse_call(lib, d=dims(S=-5)) == INVALID
+    assert lse_call(lib, d=dims(D=96)) == UNSUPPORTED
+    assert lse_call(lib, d=dims(D=256)) == UNSUPPORTED
+    assert lse_call(lib, dtype=7) == UNSUPPORTED
+    assert lse_call(lib, scale=float("nan")) == INVALID
+    assert lse_call(lib, scale=float("inf")) == INVALID
+    assert lse_call(lib, d=dims(S=(1 << 28) + 1)) == UNSUPPORTED
+
+
+def test_mass_validation(lib):
+    assert mass_call(lib, lse=None) == INVALID
+    assert mass_call(lib, out=None) == INVALID
+    assert mass_call(lib, w=-1) == INVALID
+    assert mass_call(lib, k=FAKE + 4) == INVALID
+    assert mass_call(lib, d=dims(Hq=6, Hkv=4)) == INVALID
+    assert mass_call(lib, d=dims(D=32)) == UNSUPPORTED
+
+
+def test_empty_inputs_are_noops(lib):
+    # nothing to compute: OK without touching the (fake or null) pointers
+    assert lse_call(lib, q=None, k=None, out=None, d=dims(B=0)) == OK
+    assert lse_call(lib, d=dims(S=0)) == OK
+    assert mass_call(lib, d=dims(S=0)) == OK
+    assert lib.kvp_select_topk(None, dims(B=0), 4, 4, 8, None, None) == OK
+    assert lib.kvp_select_topk(None, dims(S=0), 4, 4, 8, None, None) == OK
+
+
+def test_select_validation(lib):
+    sel = lib.kvp_select_topk
+    assert sel(None, dims(), 4, 4, 8, FAKE, None) == INVALID
+    assert sel(FAKE, dims(), 4, 4, 8, None, None) == INVALID
+    assert sel(FAKE, dims(), -1, 4, 8, FAKE, None) == INVALID
+    assert sel(FAKE, dims(), 4, -1, 8, FAKE, None) == INVALID
+    assert sel(FAKE, dims(), 4, 4, -8, FAKE, None) == INVALID
+    assert sel(FAKE + 1, dims(), 4, 4, 8, FAKE, None) == INVALID
+    assert sel(FAKE, dims(Hkv=0), 4, 4, 8, FAKE, None) == INVALID
+
+
+def test_keep_count_matches_oracle(lib, orc):
+    for S in (0, 1, 5, 52, 256, 1000):
+        for w in (0, 1, 16, 300, 1000, 1200):
+            for s in (0, 4, 60):
+                for k in (0, 1, 32, 5000):
+                    assert lib.kvp_keep_count(S, w, s, k) == orc.keep_count(S, w, s, k)
+    assert lib.kvp_keep_count(-1, 0, 0, 0) == -1
+    assert kvp.keep_count(256, 16, 4, 32) == 52
+
+
+def test_binding_rejects_cpu_tensors(lib):
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(kvp.KvpError):
+        kvp.lse_fwd(q, q)
