@@ -1,0 +1,229 @@
+"""Benchmark of the future-attention-mass path on one MI355X.
+
+One step = the whole path over one batch of synthetic input: for every layer
+of the workload, the causal LSE pass and the transposed future-mass pass, then
+one keep-set selection over all (layer, batch, KV head) rows.  Inputs are
+generated on the host from seeded recipes, uploaded once and resident in HBM
+before the timed region starts.
+
+The default workload is the Qwen3-4B-shaped stack: 36 layers, 32 query / 8 KV
+heads, d = 128, batch 1, S = 32768, w = 512, 4 sinks, k = 16384.
+
+Prints ONE JSON line on stdout (everything else goes to stderr):
+  value        future-mass query-key pairs per second over whole steps
+               (pairs = B * Hq * L * (S - w)(S - w + 1) / 2 per step)
+  roofline     the mass kernel alone: algorithmic flops (2 d per pair) per
+               launch over its average launch time, measured with HIP events
+               on the stream it runs on, against the bf16 dense MFMA peak
+  cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
+
+    python bench.py [--steps K] [--warmup W] [--workload N] [--no-cpu-baseline]
+    python bench.py --copy-probe BYTES   # plain copy kernel, for counter scaling
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X bf16 dense matrix peak: 256 CUs x 4 SIMDs x 1024 flop/clk x 2.4 GHz.
+PEAK_BF16_TFLOPS = 2516.58
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def mass_pairs(B: int, Hq: int, S: int, w: int) -> int:
+    """Query-key pairs of the future-mass pass of one layer: every (query
+    head, query i, key j) with j + w <= i."""
+    n = max(S - w, 0)
+    return B * Hq * n * (n + 1) // 2
+
+
+def copy_probe(nbytes: int, reps: int) -> None:
+    import torch
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    log(f"copy probe: {reps} copies of {nbytes} bytes")
+    print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}))
+
+
+def cpu_baseline(wl, li0, n_heads: int) -> dict:
+    """The CPU oracle (dense fp64 softmax rows + explicit column sums), as it
+    stands, on whole (batch 0, KV head) units 0 .. n_heads-1 of layer 0: every
+    query row of their G query heads.  Returns the future-mass pairs per
+    second the sample covers (its LSE work included in the time)."""
+    import oracle
+    S, w, G = wl.S, wl.window, wl.G
+    n_heads = max(1, min(n_heads, wl.Hkv))
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    for h in range(n_heads):
+        oracle.future_mass(li0.q, li0.k, w, b_only=0, h_only=h, nthreads=threads)
+    dt = time.perf_counter() - t0
+    pairs = n_heads * mass_pairs(1, G, S, w)
+    return {"value": pairs / dt / 1e9, "unit": "G query-key pairs/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": (f"layer 0, batch 0, KV heads 0..{n_heads - 1} ({n_heads * G} query heads), "
+                       f"all {S} query rows: {pairs} future-mass pairs, LSE included")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=4)
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=2,
+                    help="whole KV heads of layer 0 in the oracle sample")
+    ap.add_argument("--copy-probe", type=int, default=0)
+    ap.add_argument("--copy-reps", type=int, default=5)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the path has no multi-GPU mode "
+              "(each (layer, batch, KV head) unit is independent; see the sharding notes)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    if args.copy_probe:
+        copy_probe(args.copy_probe, args.copy_reps)
+        return 0
+
+    import future_attention_scoring_kvp_amd as kvp
+    import kvp_inputs
+
+    kvp.load_library()  # fails loudly if the HIP library is not built
+    wl = kvp_inputs.workload(args.workload)
+    L = args.layers or wl.layers
+    B, Hq, Hkv, S, D, G = wl.B, wl.Hq, wl.Hkv, wl.S, wl.D, wl.G
+    w, s, k = wl.window, wl.n_sink, wl.top_k
+    dev = torch.device("cuda:0")
+    tdtype = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+    log(f"bench: workload {wl.name}, {L} layers, B={B} Hq={Hq} Hkv={Hkv} S={S} d={D} "
+        f"w={w} s={s} k={k}")
+    q_all = torch.empty((L, B, Hq, S, D), dtype=tdtype, device=dev)
+    k_all = torch.empty((L, B, Hkv, S, D), dtype=tdtype, device=dev)
+    li0 = None
+    t0 = time.perf_counter()
+    for l in range(L):
+        li = kvp_inputs.make_layer(wl, layer=l)
+        if l == 0:
+            li0 = li
+        for src, dst in ((li.q, q_all[l]), (li.k, k_all[l])):
+            t = torch.from_numpy(src.view("int16") if src.dtype.name == "uint16" else src)
+            dst.copy_(t.view(tdtype) if src.dtype.name == "uint16" else t)
+        if l % 6 == 5 or l == L - 1:
+            log(f"bench: generated and uploaded {l + 1}/{L} layers ({time.perf_counter() - t0:.1f} s)")
+    lse_all = torch.empty((L, B, Hq, S), dtype=torch.float32, device=dev)
+    mass_all = torch.empty((L, B, Hkv, S), dtype=torch.float32, device=dev)
+    n_keep = kvp.keep_count(S, w, s, k)
+    keep_all = torch.empty((L * B, Hkv, n_keep), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        for l in range(L):
+            if events is not None:
+                events[l][0].record(stream)
+            kvp.lse_fwd(q_all[l], k_all[l], out=lse_all[l])
+            if events is not None:
+                events[l][1].record(stream)
+            kvp.future_mass(q_all[l], k_all[l], lse_all[l], w, out=mass_all[l])
+            if events is not None:
+                events[l][2].record(stream)
+        kvp.select_topk(mass_all.view(L * B, Hkv, S), w, s, k, out=keep_all)
+        if events is not None:
+            events[L][0].record(stream)
+
+    log(f"bench: {args.warmup} warmup steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(L + 1)]
+          for _ in range(args.steps)]
+    log(f"bench: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for it in range(args.steps):
+        step(ev[it])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    lse_ms = mass_ms = sel_ms = 0.0
+    for it in range(args.steps):
+        e = ev[it]
+        for l in range(L):
+            lse_ms += e[l][0].elapsed_time(e[l][1])
+            mass_ms += e[l][1].elapsed_time(e[l][2])
+        sel_ms += e[L - 1][2].elapsed_time(e[L][0])
+    n_mass = args.steps * L
+    mass_launch_ms = mass_ms / n_mass
+    lse_launch_ms = lse_ms / n_mass
+    sel_launch_ms = sel_ms / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    pairs_layer = mass_pairs(B, Hq, S, w)
+    pairs_step = pairs_layer * L
+    value = pairs_step / (ms_per_step * 1e-3) / 1e9
+    flops_launch = pairs_layer * 2 * D
+    achieved = flops_launch / (mass_launch_ms * 1e-3) / 1e12
+    lse_pairs = B * Hq * S * (S + 1) // 2
+    sel_bytes = 4 * L * B * Hkv * S + 4 * L * B * Hkv * n_keep
+    log(f"bench: step {ms_per_step:.3f} ms; per layer LSE {lse_launch_ms:.3f} ms, mass "
+        f"{mass_launch_ms:.3f} ms ({achieved:.1f} TFLOP/s, "
+        f"{100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak); select {sel_launch_ms:.3f} ms")
+
+    out = {
+        "metric": "future-mass G query-key pairs/s per GPU; % of bf16 MFMA peak",
+        "value": round(value, 3),
+        "unit": "G query-key pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K with the workload's heavy-hitter recipe)",
+        "config": {"workload": wl.name, "layers": L, "batch": B, "n_q_heads": Hq,
+                   "n_kv_heads": Hkv, "seq_len": S, "head_dim": D, "window": w,
+                   "n_sink": s, "top_k": k, "parallelism": "none (1 GPU)"},
+        "stages_ms": {"lse_per_layer": round(lse_launch_ms, 4),
+                      "mass_per_layer": round(mass_launch_ms, 4),
+                      "select_all_layers": round(sel_launch_ms, 4)},
+        "mass_pass_gpairs_per_s": round(pairs_layer / (mass_launch_ms * 1e-3) / 1e9, 3),
+        "lse_pass_gpairs_per_s": round(lse_pairs / (lse_launch_ms * 1e-3) / 1e9, 3),
+        "select_gbs": round(sel_bytes / (sel_launch_ms * 1e-3) / 1e9, 2),
+        "roofline": {"kernel": "mass_kernel", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(wl, li0, args.cpu_heads)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
