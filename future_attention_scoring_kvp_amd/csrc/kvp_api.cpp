@@ -10,8 +10,9 @@
 namespace {
 
 constexpr int32_t kAbiVersion = 1;
-// Limits that keep every index the kernels form in 32-bit ints.
-constexpr int64_t kMaxSeq = int64_t(1) << 28;
+// Limits that keep every index the kernels form in 32-bit ints, and the bytes
+// of one head (S * d * 4 at most) within a 32-bit buffer range.
+constexpr int64_t kMaxSeq = int64_t(1) << 22;
 constexpr int64_t kMaxBlocks = (int64_t(1) << 31) - 1;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }

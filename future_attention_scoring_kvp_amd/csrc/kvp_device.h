@@ -1,10 +1,15 @@
 // Device-side building blocks shared by the gfx950 kernels of libkvp.
 //
-// Matrix-core tiles: v_mfma_f32_32x32x16_bf16.  For D = A (32 x 16) * B (16 x 32):
-//   lane l supplies A[l % 32][8*(l/32) + e] and B[8*(l/32) + e][l % 32], e = 0..7,
-//   and receives D[8*(v/4) + 4*(l/32) + (v%4)][l % 32] in result register v = 0..15.
-// Both kernels put KEYS on the rows (A operand) and QUERIES on the columns
-// (B operand), so each lane's 16 results share one query.
+// Matrix-core tiles (both kernels put KEYS on the rows = A operand and
+// QUERIES on the columns = B operand):
+//   v_mfma_f32_32x32x16_bf16, D = A (32 x 16) * B (16 x 32):
+//     lane l supplies A[l % 32][8*(l/32) + e] and B[8*(l/32) + e][l % 32],
+//     e = 0..7, and receives D[8*(v/4) + 4*(l/32) + (v%4)][l % 32] in result
+//     register v = 0..15;
+//   v_mfma_f32_16x16x32_bf16, D = A (16 x 32) * B (32 x 16):
+//     lane l supplies A[l % 16][8*(l/16) + e] and B[8*(l/16) + e][l % 16],
+//     e = 0..7, and receives D[4*(l/16) + v][l % 16] in result register
+//     v = 0..3.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -30,6 +35,49 @@ __device__ __forceinline__ int mfma_row(int v, int lane) {
 __device__ __forceinline__ f32x16_t mfma_32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t mfma_16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Buffer resource (raw, stride 0) over `bytes` bytes from `base`.  Loads whose
+// per-lane offset is at or beyond `bytes` return zeros instead of touching
+// memory (the check covers the per-lane offset only, so every offset here is
+// passed per lane with a zero scalar offset).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Direct global -> LDS copy of 16 bytes per lane: lane l's 16 bytes at byte
+// `offset` of the resource land at lds_base + 16 * l (lds_base is uniform).
+// Out-of-range lanes write zeros.  Completion is tracked by vmcnt.
+__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, void* lds_base,
+                                              uint32_t offset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_base, 16, offset, 0, 0, 0);
+}
+
+// Eight elements at element offset `elem` of a buffer, as eight bf16 values
+// (16 bytes): bf16 is passed through, fp32 is rounded to nearest even.
+// Out-of-range reads give zeros.
+__device__ __forceinline__ u32x4_t buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t elem,
+                                             const uint16_t*) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, elem * 2, 0, 0));
+}
+__device__ __forceinline__ u32x4_t buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t elem,
+                                             const float*) {
+  const f32x4_t lo =
+      __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, elem * 4, 0, 0));
+  const f32x4_t hi =
+      __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, elem * 4 + 16, 0, 0));
+  bf16x8_t v;
+  v[0] = (__bf16)lo[0]; v[1] = (__bf16)lo[1]; v[2] = (__bf16)lo[2]; v[3] = (__bf16)lo[3];
+  v[4] = (__bf16)hi[0]; v[5] = (__bf16)hi[1]; v[6] = (__bf16)hi[2]; v[7] = (__bf16)hi[3];
+  return __builtin_bit_cast(u32x4_t, v);
 }
 
 // Eight consecutive input elements as eight bf16 values (16 bytes).  bf16

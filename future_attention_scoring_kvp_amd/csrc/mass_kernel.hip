@@ -9,20 +9,30 @@
 //
 // Work decomposition (keys stationary, queries streamed):
 //   * one workgroup = 4 waves = 256 consecutive keys of one (batch, KV head);
-//     each wave keeps its 64 keys (two 32-row MFMA blocks) as bf16 A-operands
-//     in registers for the whole sweep;
-//   * the workgroup sweeps the future query blocks (32 queries each) of all G
-//     heads of the group, from the end of the sequence backwards, staging
-//     4 (query block, head) pairs per LDS stage, double buffered;
+//     each wave keeps its 64 keys (two 32-row MFMA blocks, all of d) as bf16
+//     A operands in registers for the whole sweep;
+//   * the workgroup sweeps the future (query block, head) pairs of its group
+//     -- query blocks of 32 from the end of the sequence backwards, the G
+//     heads of a block consecutively -- four pairs per LDS stage, double
+//     buffered; wave w stages pair w of every stage;
+//   * in LDS a pair is stored as the MFMA B operands themselves: per 16-wide
+//     slice of d, 1 KB holding lane l's 16 bytes at 16 l.  bf16 Q is copied
+//     there straight from HBM by buffer loads to LDS (no VGPR staging) and
+//     every operand read is one contiguous, bank-conflict-free ds_read_b128;
 //   * per pair and wave: 16 MFMA 32x32x16 give a 64 x 32 logit tile; each
 //     lane applies fma + exp2 + add to its 32 values and keeps 32 per-key
 //     partial sums (its query column) in registers;
+//   * software pipeline inside each wave: the MFMAs of pair p+1 are issued
+//     between the VALU operations of pair p (one MFMA per six VALU
+//     operations), so the matrix cores and the VALU work at the same time;
 //   * at the end the 32 column partials of each key are added in LDS in a
 //     fixed order and each key's mass is written once: no atomics, bitwise
 //     reproducible.
 // Blocks are mapped XCD-aware: all tiles of one (batch, KV head) run on the
 // same XCD and sweep the same Q rows in the same order (shared L2), longest
 // tiles first so the triangular work load balances.
+#include <type_traits>
+
 #include "kvp_device.h"
 #include "kvp_launch.h"
 
@@ -35,15 +45,18 @@ struct MassCfg {
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kKeysPerWave = 64;
   static constexpr int kKeysPerWG = kWaves * kKeysPerWave;
-  static constexpr int kSlots = 4;  // (query block, head) pairs per LDS stage
-  static constexpr int kKSteps = D / 16;
-  static constexpr int kChunks = D / 8;               // 16-byte chunks per row
-  static constexpr int kRowStride = D * 2 + 16;       // padded row pitch (bytes)
-  static constexpr int kSlotBytes = kBlk * kRowStride;
+  static constexpr int kKSteps = D / 16;                // 16-wide slices of d
+  static constexpr int kFragBytes = kWave * 16;         // one B operand (1 KB)
+  static constexpr int kSlotBytes = kKSteps * kFragBytes;
+  static constexpr int kSlots = kWaves;                 // wave w stages slot w
   static constexpr int kStageBytes = kSlots * kSlotBytes;
-  static constexpr int kStageChunks = kSlots * kBlk * kChunks;
-  static constexpr int kChunksPerThread = kStageChunks / kThreads;
-  static_assert(kStageChunks % kThreads == 0, "stage must split evenly");
+  static constexpr int kMfmaPerPair = 2 * kKSteps;
+  static constexpr int kValuPerPair = 3 * 32;           // fma + exp + add per value
+  static constexpr int kRedStride = 33;                 // column partials per key (+1 pad)
+  static constexpr int kRedWaveFloats = kKeysPerWave * kRedStride;
+  // the final reduction reuses the stage buffers (two waves per buffer) when
+  // they are large enough
+  static constexpr bool kRedInStage = 2 * kRedWaveFloats * 4 <= kStageBytes;
 };
 
 struct MassArgs {
@@ -55,11 +68,19 @@ struct MassArgs {
   float c;  // scale * log2(e)
 };
 
+struct Tile {
+  f32x16_t s0, s1;  // logits of key blocks 0 / 1 (rows) x 32 queries (columns)
+  float l2;         // lse2 of this lane's query column
+};
+
 template <int D, typename T>
 __global__ __launch_bounds__(256, 2) void mass_kernel(MassArgs a) {
   using C = MassCfg<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char q_lds[2][C::kStageBytes];
-  __shared__ float l_lds[2][C::kSlots * kBlk];
+  __shared__ __attribute__((aligned(1024))) unsigned char q_lds0[C::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char q_lds1[C::kStageBytes];
+  __shared__ float l_lds0[C::kSlots * kBlk];
+  __shared__ float l_lds1[C::kSlots * kBlk];
+  __shared__ float red_extra[C::kRedInStage ? 1 : C::kWaves * C::kRedWaveFloats];
 
   const int S = a.S, G = a.G, w = a.window;
   int unit, tile;
@@ -67,25 +88,31 @@ __global__ __launch_bounds__(256, 2) void mass_kernel(MassArgs a) {
   const int b = unit / a.Hkv;
   const int h = unit - b * a.Hkv;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
+  const int l32 = lane & 31;  // query column / key row within a 32-block
+  const int h32 = lane >> 5;  // which 8-element half of a 16-wide slice of d
   const int tile_key0 = tile * C::kKeysPerWG;
   const int key0 = tile_key0 + wave * C::kKeysPerWave;
 
   const T* __restrict__ kbase = static_cast<const T*>(a.k) + (size_t)(b * a.Hkv + h) * S * D;
-  const T* __restrict__ qbase = static_cast<const T*>(a.q) + (size_t)(b * a.Hq + h * G) * S * D;
-  const float* __restrict__ lbase = a.lse + (size_t)(b * a.Hq + h * G) * S;
+  const T* __restrict__ qgroup = static_cast<const T*>(a.q) + (size_t)(b * a.Hq + h * G) * S * D;
+  const float* __restrict__ lgroup = a.lse + (size_t)(b * a.Hq + h * G) * S;
+  const uint32_t head_bytes = (uint32_t)S * D * sizeof(T);
 
-  // Stationary keys: A-operands of the two 32-row blocks, all k-steps.
+  // Stationary keys: A operands of the two 32-row blocks, all slices of d.
   u32x4_t kf[2][C::kKSteps];
+  {
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase, head_bytes);
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int key = key0 + 32 * rb + (lane & 31);
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int ks = 0; ks < C::kKSteps; ++ks) {
-      const int col = 16 * ks + 8 * (lane >> 5);
-      kf[rb][ks] = key < S ? load8(kbase + (size_t)key * D + col) : u32x4_t{0, 0, 0, 0};
-    }
+      for (int ks = 0; ks < C::kKSteps; ++ks)  // keys >= S read 0
+        kf[rb][ks] = buf_load8(kr, (uint32_t)(key0 + 32 * rb + l32) * D + 16 * ks + 8 * h32,
+                               static_cast<const T*>(nullptr));
+    // wait here once, so that no use of the keys inside the sweep waits on
+    // the loads of the stage copies in flight
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   }
 
   f32x16_t acc0 = {}, acc1 = {};
@@ -97,115 +124,174 @@ __global__ __launch_bounds__(256, 2) void mass_kernel(MassArgs a) {
     const int qb_lo = q_first / kBlk;
     const int n_pairs = (qb_hi - qb_lo + 1) * G;
     const int n_stages = (n_pairs + C::kSlots - 1) / C::kSlots;
+    // Pair p is (query block qb_hi - p / G, head p % G).  For this wave,
+    // pairs [p_full_lo, p_full) see every key with every query (no mask),
+    // the other pairs below p_end need the mask, pairs >= p_end see nothing.
+    // A partial last block (rows >= S) is masked too.
+    const int p_full_lo = (S % kBlk) ? G : 0;
+    const int qb_full = (key0 + C::kKeysPerWave - 1 + w + kBlk - 1) / kBlk;
+    const int p_full = max(0, min(n_pairs, (qb_hi - qb_full + 1) * G));
+    const int qb_min = (key0 + w) / kBlk;  // first block with a query i >= key0 + w
+    const int p_end = max(0, min(n_pairs, (qb_hi - qb_min + 1) * G));
 
-    // Stage loader: pair p -> query block qb_hi - p / G, head p % G.
-    u32x4_t stage_regs[C::kChunksPerThread];
-    auto load_stage = [&](int st) {
-#pragma unroll
-      for (int t = 0; t < C::kChunksPerThread; ++t) {
-        const int cidx = tid + t * C::kThreads;
-        const int slot = cidx / (kBlk * C::kChunks);
-        const int row = (cidx / C::kChunks) % kBlk;
-        const int ch = cidx % C::kChunks;
-        const int p = st * C::kSlots + slot;
-        u32x4_t v = {0, 0, 0, 0};
-        if (p < n_pairs) {
-          const int qb = qb_hi - p / G;
-          const int g = p - (p / G) * G;
-          const int i = qb * kBlk + row;
-          if (i < S) v = load8(qbase + ((size_t)g * S + i) * D + ch * 8);
-        }
-        stage_regs[t] = v;
+    // ---- staging: this wave copies pair 4 * st + wave of stage st
+    int ld_qb = qb_hi - wave / G;
+    int ld_g = wave % G;
+    auto advance = [&](int& qb, int& g) __attribute__((always_inline)) {
+      g += C::kSlots;
+      while (g >= G) {
+        g -= G;
+        --qb;
       }
     };
-    auto store_stage = [&](int st, int buf) {
-#pragma unroll
-      for (int t = 0; t < C::kChunksPerThread; ++t) {
-        const int cidx = tid + t * C::kThreads;
-        const int slot = cidx / (kBlk * C::kChunks);
-        const int row = (cidx / C::kChunks) % kBlk;
-        const int ch = cidx % C::kChunks;
-        *reinterpret_cast<u32x4_t*>(&q_lds[buf][slot * C::kSlotBytes + row * C::kRowStride + ch * 16]) =
-            stage_regs[t];
+    // Copies go HBM -> VGPR -> LDS in two halves of the d slices, so that
+    // only 4 x 16 bytes per lane are in flight in registers at a time.
+    constexpr int kHalf = C::kKSteps / 2;
+    u32x4_t stage_regs[kHalf];
+    float lse_pref = 0.f;
+    auto issue_loads = [&](int st, int half) __attribute__((always_inline)) {
+      if (st * C::kSlots + wave >= n_pairs) return;
+      if (half == 0 && lane < kBlk) {
+        const int i = ld_qb * kBlk + lane;
+        lse_pref = i < S ? lgroup[(size_t)ld_g * S + i] : 0.f;
       }
-      if (tid < C::kSlots * kBlk) {
-        const int slot = tid / kBlk;
-        const int row = tid % kBlk;
-        const int p = st * C::kSlots + slot;
-        float l2 = __builtin_inff();  // no query: exp2(x - inf) = 0
-        if (p < n_pairs) {
-          const int qb = qb_hi - p / G;
-          const int g = p - (p / G) * G;
-          const int i = qb * kBlk + row;
-          if (i < S) l2 = lbase[(size_t)g * S + i] * kLog2e;
+      const __amdgpu_buffer_rsrc_t qr = make_rsrc(qgroup + (size_t)ld_g * S * D, head_bytes);
+      const uint32_t e0 = (uint32_t)(ld_qb * kBlk + l32) * D + 8 * h32;
+#pragma unroll
+      for (int t = 0; t < kHalf; ++t)  // rows >= S read 0
+        stage_regs[t] = buf_load8(qr, e0 + 16 * (half * kHalf + t), static_cast<const T*>(nullptr));
+    };
+    auto store_half = [&](int st, int half, unsigned char* qdst) __attribute__((always_inline)) {
+      if (st * C::kSlots + wave >= n_pairs) return;
+      unsigned char* slot = qdst + wave * C::kSlotBytes + lane * 16;
+#pragma unroll
+      for (int t = 0; t < kHalf; ++t)
+        *reinterpret_cast<u32x4_t*>(slot + (half * kHalf + t) * C::kFragBytes) = stage_regs[t];
+    };
+    auto finish_loads = [&](int st, float* ldst) __attribute__((always_inline)) {
+      const bool valid = st * C::kSlots + wave < n_pairs;
+      if (lane < kBlk) {
+        const int i = ld_qb * kBlk + lane;
+        // no query (row beyond S or no pair): exp2(x - inf) = 0
+        ldst[wave * kBlk + lane] = (valid && i < S) ? lse_pref * kLog2e : __builtin_inff();
+      }
+      advance(ld_qb, ld_g);  // the pair this wave stages in the next stage
+    };
+
+    // ---- compute
+    auto mfma_pair = [&](Tile& t, const unsigned char* qsrc, const float* lsrc, int slot)
+                         __attribute__((always_inline)) {
+      const unsigned char* src = qsrc + slot * C::kSlotBytes + lane * 16;
+      t.l2 = lsrc[slot * kBlk + l32];
+#pragma unroll
+      for (int ks = 0; ks < C::kKSteps; ++ks) {
+        const u32x4_t bq = *reinterpret_cast<const u32x4_t*>(src + ks * C::kFragBytes);
+        t.s0 = mfma_32x32x16(kf[0][ks], bq, ks ? t.s0 : f32x16_t{});
+        t.s1 = mfma_32x32x16(kf[1][ks], bq, ks ? t.s1 : f32x16_t{});
+      }
+    };
+    auto exp_full = [&](const Tile& t) __attribute__((always_inline)) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        acc0[v] += fast_exp2(__builtin_fmaf(t.s0[v], c, -t.l2));
+        acc1[v] += fast_exp2(__builtin_fmaf(t.s1[v], c, -t.l2));
+      }
+    };
+    auto exp_masked = [&](const Tile& t, int p) __attribute__((always_inline)) {
+      const int i = (qb_hi - p / G) * kBlk + l32;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int j = key0 + mfma_row(v, lane);
+        const float x0 = __builtin_fmaf(t.s0[v], c, -t.l2);
+        const float x1 = __builtin_fmaf(t.s1[v], c, -t.l2);
+        acc0[v] += fast_exp2(i >= j + w ? x0 : -__builtin_inff());
+        acc1[v] += fast_exp2(i >= j + 32 + w ? x1 : -__builtin_inff());
+      }
+    };
+    // Exponentials of pair p (in cur) and MFMAs of pair p + 1 (into nxt).
+    auto step = [&](Tile& cur, Tile& nxt, int p, const unsigned char* nq, const float* nl,
+                    int nslot) __attribute__((always_inline)) {
+      const bool m_ok = p + 1 < p_end;
+      const bool full = p >= p_full_lo && p < p_full;
+      if (m_ok && full) {
+        mfma_pair(nxt, nq, nl, nslot);
+        exp_full(cur);
+        // issue order: operand reads ahead, then each MFMA followed by six
+        // VALU operations, one more operand read after every second MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+        for (int m = 0; m < C::kMfmaPerPair; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, C::kValuPerPair / C::kMfmaPerPair, 0);
+          if ((m & 1) == 1 && m < 2 * C::kKSteps - 4)
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        l_lds[buf][tid] = l2;
+      } else {
+        if (m_ok) mfma_pair(nxt, nq, nl, nslot);
+        if (full)
+          exp_full(cur);
+        else if (p < p_end)
+          exp_masked(cur, p);
       }
     };
 
-    load_stage(0);
-    store_stage(0, 0);
-    __syncthreads();
-
-    for (int st = 0; st < n_stages; ++st) {
-      const int buf = st & 1;
-      if (st + 1 < n_stages) load_stage(st + 1);
-
-#pragma unroll
-      for (int slot = 0; slot < C::kSlots; ++slot) {
-        const int p = st * C::kSlots + slot;
-        if (p >= n_pairs) break;
-        const int q0 = (qb_hi - p / G) * kBlk;
-        if (q0 + kBlk - 1 < key0 + w) continue;           // no query of this block reaches these keys
-        const bool full = q0 >= key0 + C::kKeysPerWave - 1 + w;
-
-        const unsigned char* sbase = &q_lds[buf][slot * C::kSlotBytes + (lane & 31) * C::kRowStride];
-        f32x16_t s0 = {}, s1 = {};
-#pragma unroll
-        for (int ks = 0; ks < C::kKSteps; ++ks) {
-          const u32x4_t bq = *reinterpret_cast<const u32x4_t*>(sbase + (2 * ks + (lane >> 5)) * 16);
-          s0 = mfma_32x32x16(kf[0][ks], bq, s0);
-          s1 = mfma_32x32x16(kf[1][ks], bq, s1);
-        }
-        const float l2 = l_lds[buf][slot * kBlk + (lane & 31)];
-        if (full) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            acc0[v] += fast_exp2(__builtin_fmaf(s0[v], c, -l2));
-            acc1[v] += fast_exp2(__builtin_fmaf(s1[v], c, -l2));
-          }
-        } else {
-          const int i = q0 + (lane & 31);
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int j = key0 + mfma_row(v, lane);
-            const float x0 = __builtin_fmaf(s0[v], c, -l2);
-            const float x1 = __builtin_fmaf(s1[v], c, -l2);
-            acc0[v] += fast_exp2(i >= j + w ? x0 : -__builtin_inff());
-            acc1[v] += fast_exp2(i >= j + 32 + w ? x1 : -__builtin_inff());
-          }
-        }
+    Tile t0, t1;
+    auto stage = [&](auto bufc, int st) __attribute__((always_inline)) {
+      constexpr int kBuf = decltype(bufc)::value;
+      unsigned char* cq = kBuf ? q_lds1 : q_lds0;
+      unsigned char* nq = kBuf ? q_lds0 : q_lds1;
+      float* cl = kBuf ? l_lds1 : l_lds0;
+      float* nl = kBuf ? l_lds0 : l_lds1;
+      const bool more = st + 1 < n_stages;
+      if (more) issue_loads(st + 1, 0);
+      const int p0 = st * C::kSlots;
+      step(t0, t1, p0 + 0, cq, cl, 1);
+      if (more) {
+        store_half(st + 1, 0, nq);
+        issue_loads(st + 1, 1);
       }
-
-      if (st + 1 < n_stages) store_stage(st + 1, buf ^ 1);
+      step(t1, t0, p0 + 1, cq, cl, 2);
+      step(t0, t1, p0 + 2, cq, cl, 3);
+      if (more) {
+        store_half(st + 1, 1, nq);
+        finish_loads(st + 1, nl);
+      }
       __syncthreads();
+      step(t1, t0, p0 + 3, nq, nl, 0);
+    };
+
+    issue_loads(0, 0);
+    store_half(0, 0, q_lds0);
+    issue_loads(0, 1);
+    store_half(0, 1, q_lds0);
+    finish_loads(0, l_lds0);
+    __syncthreads();
+    if (0 < p_end) mfma_pair(t0, q_lds0, l_lds0, 0);
+    for (int st = 0; st < n_stages; st += 2) {
+      stage(std::integral_constant<int, 0>{}, st);
+      if (st + 1 >= n_stages) break;
+      stage(std::integral_constant<int, 1>{}, st + 1);
     }
   }
 
   // Column reduction: each lane holds one query column's partial sums for 32
-  // keys; add the 32 columns of every key in LDS in a fixed order.
+  // keys per block; add the 32 columns of every key in LDS in a fixed order.
   __syncthreads();
-  float* red = reinterpret_cast<float*>(&q_lds[0][0]) + wave * (C::kKeysPerWave * 33);
+  float* red;
+  if constexpr (C::kRedInStage)
+    red = reinterpret_cast<float*>(wave < 2 ? q_lds0 : q_lds1) + (wave & 1) * C::kRedWaveFloats;
+  else
+    red = red_extra + wave * C::kRedWaveFloats;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int kl = mfma_row(v, lane);
-    red[kl * 33 + (lane & 31)] = acc0[v];
-    red[(kl + 32) * 33 + (lane & 31)] = acc1[v];
+    red[kl * C::kRedStride + l32] = acc0[v];
+    red[(kl + 32) * C::kRedStride + l32] = acc1[v];
   }
   __syncthreads();
   float tot = 0.f;
 #pragma unroll
-  for (int cidx = 0; cidx < 32; ++cidx) tot += red[lane * 33 + cidx];
+  for (int col = 0; col < 32; ++col) tot += red[lane * C::kRedStride + col];
   const int key = key0 + lane;
   if (key < S) a.mass[(size_t)(b * a.Hkv + h) * S + key] = tot;
 }

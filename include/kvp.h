@@ -38,9 +38,10 @@
  *   - Validation is synchronous and happens before any launch; a rejected
  *     call enqueues nothing.  No function prints, throws or aborts, and all
  *     are thread-safe (no global state).
- *   - Sizes: batch >= 0 and seq_len >= 0 (0 = empty input: nothing to do,
- *     KVP_OK); n_q_heads, n_kv_heads >= 1 and n_q_heads % n_kv_heads == 0;
- *     head_dim in {64, 128}.  Pointers must be 16-byte aligned.
+ *   - Sizes: batch >= 0 and 0 <= seq_len <= 2^22 (0 = empty input: nothing
+ *     to do, KVP_OK; longer sequences give KVP_ERR_UNSUPPORTED);
+ *     n_q_heads, n_kv_heads >= 1 and n_q_heads % n_kv_heads == 0; head_dim
+ *     in {64, 128}.  Pointers must be 16-byte aligned.
  */
 #ifndef KVP_H_
 #define KVP_H_

@@ -76,7 +76,7 @@ def test_lse_validation(lib):
     assert lse_call(lib, dtype=7) == UNSUPPORTED
     assert lse_call(lib, scale=float("nan")) == INVALID
     assert lse_call(lib, scale=float("inf")) == INVALID
-    assert lse_call(lib, d=dims(S=(1 << 28) + 1)) == UNSUPPORTED
+    assert lse_call(lib, d=dims(S=(1 << 22) + 1)) == UNSUPPORTED
 
 
 def test_mass_validation(lib):
