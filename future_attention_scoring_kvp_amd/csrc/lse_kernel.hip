@@ -6,20 +6,29 @@
 //
 // Work decomposition (queries stationary, keys streamed):
 //   * one workgroup = 4 waves; each wave owns 64 consecutive query positions
-//     of one query head (two 32-column MFMA blocks kept as bf16 B-operands in
+//     of one query head (two 32-column MFMA blocks kept as bf16 B operands in
 //     registers); the 4 waves cover (position block, head) pairs of one GQA
 //     group, heads fastest, so the group's shared keys are staged once;
-//   * keys are streamed in blocks of 32 from position 0 upwards, 4 blocks per
-//     LDS stage, double buffered; every workgroup of a (batch, KV head) walks
-//     the same key sequence (shared L2), and workgroups run longest first;
-//   * per key block and wave: 16 MFMA 32x32x16 give a 32-key x 64-query tile;
-//     each lane (one query column) adds exp2(c*s - u) of its 16 values into
-//     one running sum.
+//   * keys are streamed in blocks of 32 from position 0 upwards, four blocks
+//     per LDS stage, double buffered; wave w stages block w of every stage.
+//     In LDS a key block is stored as the MFMA A operands themselves (per
+//     16-wide slice of d, 1 KB with lane l's 16 bytes at 16 l), copied from
+//     HBM through VGPRs in two halves, so every operand read is one
+//     contiguous ds_read_b128;
+//   * per key block and wave: 16 MFMA 32x32x16 give a 32-key x 64-query
+//     tile; each lane (one query column per 32-query half) adds exp2(c*s - u)
+//     of its 16 values into one running sum per half;
+//   * software pipeline inside each wave: the MFMAs of block p+1 are issued
+//     between the VALU operations of block p;
+//   * every workgroup of a (batch, KV head) walks the same key sequence
+//     (shared L2), and workgroups run longest first.
 // The shift u of a row is the largest logit of its first key block (which
 // always holds key 0, valid for every row), so the running sum is >= 1 and
 // cannot underflow; it could only overflow if a later logit exceeded that by
 // more than ~88 (natural units).  Such rows are flagged (LSE = +inf) and
 // recomputed exactly by lse_fix_kernel, a max-then-sum pass per row.
+#include <type_traits>
+
 #include "kvp_device.h"
 #include "kvp_launch.h"
 
@@ -31,15 +40,13 @@ struct LseCfg {
   static constexpr int kWaves = 4;
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kQueriesPerWave = 64;
-  static constexpr int kSlots = 4;  // key blocks per LDS stage
-  static constexpr int kKSteps = D / 16;
-  static constexpr int kChunks = D / 8;
-  static constexpr int kRowStride = D * 2 + 16;
-  static constexpr int kSlotBytes = kBlk * kRowStride;
+  static constexpr int kKSteps = D / 16;          // 16-wide slices of d
+  static constexpr int kFragBytes = kWave * 16;   // one A operand (1 KB)
+  static constexpr int kSlotBytes = kKSteps * kFragBytes;
+  static constexpr int kSlots = kWaves;           // wave w stages slot w
   static constexpr int kStageBytes = kSlots * kSlotBytes;
-  static constexpr int kStageChunks = kSlots * kBlk * kChunks;
-  static constexpr int kChunksPerThread = kStageChunks / kThreads;
-  static_assert(kStageChunks % kThreads == 0, "stage must split evenly");
+  static constexpr int kMfmaPerBlock = 2 * kKSteps;
+  static constexpr int kValuPerBlock = 3 * 32;    // fma + exp + add per value
 };
 
 struct LseArgs {
@@ -51,10 +58,15 @@ struct LseArgs {
   float c;   // scale * log2(e)
 };
 
+struct LTile {
+  f32x16_t s0, s1;  // logits: 32 keys (rows) x query half 0 / 1 (columns)
+};
+
 template <int D, typename T>
 __global__ __launch_bounds__(256, 2) void lse_kernel(LseArgs a) {
   using C = LseCfg<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][C::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[C::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[C::kStageBytes];
 
   const int S = a.S, G = a.G;
   int unit, tile;
@@ -62,8 +74,10 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(LseArgs a) {
   const int b = unit / a.Hkv;
   const int h = unit - b * a.Hkv;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int h32 = lane >> 5;
 
   // (position block, head) pairs, heads fastest; tile 0 takes the last pairs
   // (the longest rows).
@@ -81,118 +95,162 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(LseArgs a) {
   const int key_end = min(S, (last_pair / G + 1) * C::kQueriesPerWave);
   const int n_kb = (key_end + kBlk - 1) / kBlk;
   const int n_stages = (n_kb + C::kSlots - 1) / C::kSlots;
+  // For this wave: key blocks [0, kb_full) are entirely at or below every
+  // query of the wave and inside the sequence (no mask); blocks [kb_full,
+  // kb_end) need the mask; blocks >= kb_end hold no key for these queries.
+  const int kb_end = active ? min(n_kb, (min(p0 + C::kQueriesPerWave, S) + kBlk - 1) / kBlk) : 0;
+  const int kb_full = active ? min(kb_end, min(p0 + 1, S) / kBlk) : 0;
 
   const T* __restrict__ kbase = static_cast<const T*>(a.k) + (size_t)(b * a.Hkv + h) * S * D;
   const T* __restrict__ qrow = static_cast<const T*>(a.q) + (size_t)(b * a.Hq + h * G + g) * S * D;
+  const uint32_t head_bytes = (uint32_t)S * D * sizeof(T);
 
-  // Stationary queries: B-operands of the two 32-column blocks.
+  // Stationary queries: B operands of the two 32-column blocks.
   u32x4_t qf[2][C::kKSteps];
+  {
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(qrow, active ? head_bytes : 0u);
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int i = p0 + 32 * cb + (lane & 31);
+    for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-    for (int ks = 0; ks < C::kKSteps; ++ks) {
-      const int col = 16 * ks + 8 * (lane >> 5);
-      qf[cb][ks] = (active && i < S) ? load8(qrow + (size_t)i * D + col) : u32x4_t{0, 0, 0, 0};
-    }
+      for (int ks = 0; ks < C::kKSteps; ++ks)  // rows >= S (or no pair) read 0
+        qf[cb][ks] = buf_load8(qr, (uint32_t)(p0 + 32 * cb + l32) * D + 16 * ks + 8 * h32,
+                               static_cast<const T*>(nullptr));
+    // wait here once, so that no use of the queries inside the sweep waits on
+    // the loads of the stage copies in flight
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   }
-
-  u32x4_t stage_regs[C::kChunksPerThread];
-  auto load_stage = [&](int st) {
-#pragma unroll
-    for (int t = 0; t < C::kChunksPerThread; ++t) {
-      const int cidx = tid + t * C::kThreads;
-      const int slot = cidx / (kBlk * C::kChunks);
-      const int row = (cidx / C::kChunks) % kBlk;
-      const int ch = cidx % C::kChunks;
-      const int j = (st * C::kSlots + slot) * kBlk + row;
-      stage_regs[t] = j < key_end ? load8(kbase + (size_t)j * D + ch * 8) : u32x4_t{0, 0, 0, 0};
-    }
-  };
-  auto store_stage = [&](int buf) {
-#pragma unroll
-    for (int t = 0; t < C::kChunksPerThread; ++t) {
-      const int cidx = tid + t * C::kThreads;
-      const int slot = cidx / (kBlk * C::kChunks);
-      const int row = (cidx / C::kChunks) % kBlk;
-      const int ch = cidx % C::kChunks;
-      *reinterpret_cast<u32x4_t*>(&k_lds[buf][slot * C::kSlotBytes + row * C::kRowStride + ch * 16]) =
-          stage_regs[t];
-    }
-  };
 
   const float c = a.c;
   float u0 = 0.f, u1 = 0.f;      // per-row shifts (log2 units)
   float sum0 = 0.f, sum1 = 0.f;  // running sums of exp2(c*s - u)
-  const int iq0 = p0 + (lane & 31);
+  const int iq0 = p0 + l32;
   const int iq1 = iq0 + 32;
 
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-
-  for (int st = 0; st < n_stages; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < n_stages) load_stage(st + 1);
-
+  // ---- staging: wave w copies key block 4 * st + w of stage st, in halves
+  constexpr int kHalf = C::kKSteps / 2;
+  u32x4_t stage_regs[kHalf];
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase, head_bytes);
+  auto issue_loads = [&](int st, int half) __attribute__((always_inline)) {
+    const int kb = st * C::kSlots + wave;
+    if (kb >= n_kb) return;
+    const uint32_t e0 = (uint32_t)(kb * kBlk + l32) * D + 8 * h32;
 #pragma unroll
-    for (int slot = 0; slot < C::kSlots; ++slot) {
-      const int kb = st * C::kSlots + slot;
-      if (kb >= n_kb) break;
-      const int k0 = kb * kBlk;
-      if (!active || k0 > p0 + C::kQueriesPerWave - 1) continue;  // above this wave's diagonal
-      const bool full = (k0 + kBlk - 1 <= p0) && (k0 + kBlk <= S);
+    for (int t = 0; t < kHalf; ++t)  // keys >= S read 0
+      stage_regs[t] = buf_load8(kr, e0 + 16 * (half * kHalf + t), static_cast<const T*>(nullptr));
+  };
+  auto store_half = [&](int st, int half, unsigned char* kdst) __attribute__((always_inline)) {
+    if (st * C::kSlots + wave >= n_kb) return;
+    unsigned char* slot = kdst + wave * C::kSlotBytes + lane * 16;
+#pragma unroll
+    for (int t = 0; t < kHalf; ++t)
+      *reinterpret_cast<u32x4_t*>(slot + (half * kHalf + t) * C::kFragBytes) = stage_regs[t];
+  };
 
-      const unsigned char* sbase = &k_lds[buf][slot * C::kSlotBytes + (lane & 31) * C::kRowStride];
-      f32x16_t s0 = {}, s1 = {};
+  // ---- compute
+  auto mfma_block = [&](LTile& t, const unsigned char* ksrc, int slot) __attribute__((always_inline)) {
+    const unsigned char* src = ksrc + slot * C::kSlotBytes + lane * 16;
 #pragma unroll
-      for (int ks = 0; ks < C::kKSteps; ++ks) {
-        const u32x4_t ak = *reinterpret_cast<const u32x4_t*>(sbase + (2 * ks + (lane >> 5)) * 16);
-        s0 = mfma_32x32x16(ak, qf[0][ks], s0);
-        s1 = mfma_32x32x16(ak, qf[1][ks], s1);
-      }
-
-      if (kb == 0) {
-        // Shift of each row: its largest valid logit in this first block.
-        float m0 = -__builtin_inff(), m1 = -__builtin_inff();
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int j = mfma_row(v, lane);
-          if (j <= iq0 && j < S) m0 = fmaxf(m0, s0[v]);
-          if (j <= iq1 && j < S) m1 = fmaxf(m1, s1[v]);
-        }
-        m0 = fmaxf(m0, __shfl_xor(m0, 32));
-        m1 = fmaxf(m1, __shfl_xor(m1, 32));
-        u0 = m0 * c;
-        u1 = m1 * c;
-      }
-
-      if (full) {
-        float t0 = 0.f, t1 = 0.f;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          t0 += fast_exp2(__builtin_fmaf(s0[v], c, -u0));
-          t1 += fast_exp2(__builtin_fmaf(s1[v], c, -u1));
-        }
-        sum0 += t0;
-        sum1 += t1;
-      } else {
-        float t0 = 0.f, t1 = 0.f;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int j = k0 + mfma_row(v, lane);
-          const float x0 = __builtin_fmaf(s0[v], c, -u0);
-          const float x1 = __builtin_fmaf(s1[v], c, -u1);
-          t0 += fast_exp2((j <= iq0 && j < S) ? x0 : -__builtin_inff());
-          t1 += fast_exp2((j <= iq1 && j < S) ? x1 : -__builtin_inff());
-        }
-        sum0 += t0;
-        sum1 += t1;
-      }
+    for (int ks = 0; ks < C::kKSteps; ++ks) {
+      const u32x4_t ak = *reinterpret_cast<const u32x4_t*>(src + ks * C::kFragBytes);
+      t.s0 = mfma_32x32x16(ak, qf[0][ks], ks ? t.s0 : f32x16_t{});
+      t.s1 = mfma_32x32x16(ak, qf[1][ks], ks ? t.s1 : f32x16_t{});
     }
+  };
+  auto exp_full = [&](const LTile& t) __attribute__((always_inline)) {
+    float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      t0 += fast_exp2(__builtin_fmaf(t.s0[v], c, -u0));
+      t1 += fast_exp2(__builtin_fmaf(t.s1[v], c, -u1));
+    }
+    sum0 += t0;
+    sum1 += t1;
+  };
+  auto exp_masked = [&](const LTile& t, int kb) __attribute__((always_inline)) {
+    float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int j = kb * kBlk + mfma_row(v, lane);
+      const float x0 = __builtin_fmaf(t.s0[v], c, -u0);
+      const float x1 = __builtin_fmaf(t.s1[v], c, -u1);
+      t0 += fast_exp2((j <= iq0 && j < S) ? x0 : -__builtin_inff());
+      t1 += fast_exp2((j <= iq1 && j < S) ? x1 : -__builtin_inff());
+    }
+    sum0 += t0;
+    sum1 += t1;
+  };
+  // Shifts from the first key block (key 0 is valid for every row).
+  auto set_shift = [&](const LTile& t) __attribute__((always_inline)) {
+    float m0 = -__builtin_inff(), m1 = -__builtin_inff();
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int j = mfma_row(v, lane);
+      if (j <= iq0 && j < S) m0 = fmaxf(m0, t.s0[v]);
+      if (j <= iq1 && j < S) m1 = fmaxf(m1, t.s1[v]);
+    }
+    m0 = fmaxf(m0, __shfl_xor(m0, 32));
+    m1 = fmaxf(m1, __shfl_xor(m1, 32));
+    u0 = m0 * c;
+    u1 = m1 * c;
+  };
+  // Exponentials of block kb (in cur) and MFMAs of block kb + 1 (into nxt).
+  auto step = [&](LTile& cur, LTile& nxt, int kb, const unsigned char* nk, int nslot)
+                  __attribute__((always_inline)) {
+    const bool m_ok = kb + 1 < kb_end;
+    const bool full = kb < kb_full;
+    if (m_ok && full) {
+      mfma_block(nxt, nk, nslot);
+      exp_full(cur);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int m = 0; m < C::kMfmaPerBlock; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, C::kValuPerBlock / C::kMfmaPerBlock, 0);
+        if ((m & 1) == 1 && m < 2 * C::kKSteps - 2)
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    } else {
+      if (m_ok) mfma_block(nxt, nk, nslot);
+      if (full)
+        exp_full(cur);
+      else if (kb < kb_end)
+        exp_masked(cur, kb);
+    }
+  };
 
-    if (st + 1 < n_stages) store_stage(buf ^ 1);
+  LTile t0, t1;
+  auto stage = [&](auto bufc, int st) __attribute__((always_inline)) {
+    constexpr int kBuf = decltype(bufc)::value;
+    unsigned char* ck = kBuf ? k_lds1 : k_lds0;
+    unsigned char* nk = kBuf ? k_lds0 : k_lds1;
+    const bool more = st + 1 < n_stages;
+    if (more) issue_loads(st + 1, 0);
+    const int kb0 = st * C::kSlots;
+    step(t0, t1, kb0 + 0, ck, 1);
+    if (more) {
+      store_half(st + 1, 0, nk);
+      issue_loads(st + 1, 1);
+    }
+    step(t1, t0, kb0 + 1, ck, 2);
+    step(t0, t1, kb0 + 2, ck, 3);
+    if (more) store_half(st + 1, 1, nk);
     __syncthreads();
+    step(t1, t0, kb0 + 3, nk, 0);
+  };
+
+  issue_loads(0, 0);
+  store_half(0, 0, k_lds0);
+  issue_loads(0, 1);
+  store_half(0, 1, k_lds0);
+  __syncthreads();
+  if (0 < kb_end) {
+    mfma_block(t0, k_lds0, 0);
+    set_shift(t0);
+  }
+  for (int st = 0; st < n_stages; st += 2) {
+    stage(std::integral_constant<int, 0>{}, st);
+    if (st + 1 >= n_stages) break;
+    stage(std::integral_constant<int, 1>{}, st + 1);
   }
 
   // Combine the two half-columns (lanes l and l^32 hold the same query).
