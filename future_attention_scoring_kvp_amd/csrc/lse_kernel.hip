@@ -167,14 +167,18 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(LseArgs a) {
     sum1 += t1;
   };
   auto exp_masked = [&](const LTile& t, int kb) __attribute__((always_inline)) {
+    // key j = 32 kb + 8 (v / 4) + 4 h32 + v % 4 counts iff j <= min(i, S - 1),
+    // i.e. iff the constant 8 (v / 4) + v % 4 <= lim
+    const int lim0 = min(iq0, S - 1) - kb * kBlk - 4 * h32;
+    const int lim1 = min(iq1, S - 1) - kb * kBlk - 4 * h32;
     float t0 = 0.f, t1 = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int j = kb * kBlk + mfma_row(v, lane);
+      const int r = 8 * (v >> 2) + (v & 3);
       const float x0 = __builtin_fmaf(t.s0[v], c, -u0);
       const float x1 = __builtin_fmaf(t.s1[v], c, -u1);
-      t0 += fast_exp2((j <= iq0 && j < S) ? x0 : -__builtin_inff());
-      t1 += fast_exp2((j <= iq1 && j < S) ? x1 : -__builtin_inff());
+      t0 += fast_exp2(r <= lim0 ? x0 : -__builtin_inff());
+      t1 += fast_exp2(r <= lim1 ? x1 : -__builtin_inff());
     }
     sum0 += t0;
     sum1 += t1;

@@ -16,9 +16,9 @@
 //     heads of a block consecutively -- four pairs per LDS stage, double
 //     buffered; wave w stages pair w of every stage;
 //   * in LDS a pair is stored as the MFMA B operands themselves: per 16-wide
-//     slice of d, 1 KB holding lane l's 16 bytes at 16 l.  bf16 Q is copied
-//     there straight from HBM by buffer loads to LDS (no VGPR staging) and
-//     every operand read is one contiguous, bank-conflict-free ds_read_b128;
+//     slice of d, 1 KB holding lane l's 16 bytes at 16 l, copied from HBM
+//     through VGPRs in two halves, so every operand read is one contiguous,
+//     bank-conflict-free ds_read_b128;
 //   * per pair and wave: 16 MFMA 32x32x16 give a 64 x 32 logit tile; each
 //     lane applies fma + exp2 + add to its 32 values and keeps 32 per-key
 //     partial sums (its query column) in registers;
@@ -198,14 +198,16 @@ __global__ __launch_bounds__(256, 2) void mass_kernel(MassArgs a) {
       }
     };
     auto exp_masked = [&](const Tile& t, int p) __attribute__((always_inline)) {
-      const int i = (qb_hi - p / G) * kBlk + l32;
+      // query i counts for key j = key0 + 32 b + 8 (v / 4) + 4 h32 + v % 4 iff
+      // i >= j + w, i.e. iff the constant 8 (v / 4) + v % 4 <= lim - 32 b
+      const int lim = (qb_hi - p / G) * kBlk + l32 - key0 - w - 4 * h32;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int j = key0 + mfma_row(v, lane);
+        const int r = 8 * (v >> 2) + (v & 3);
         const float x0 = __builtin_fmaf(t.s0[v], c, -t.l2);
         const float x1 = __builtin_fmaf(t.s1[v], c, -t.l2);
-        acc0[v] += fast_exp2(i >= j + w ? x0 : -__builtin_inff());
-        acc1[v] += fast_exp2(i >= j + 32 + w ? x1 : -__builtin_inff());
+        acc0[v] += fast_exp2(r <= lim ? x0 : -__builtin_inff());
+        acc1[v] += fast_exp2(r + 32 <= lim ? x1 : -__builtin_inff());
       }
     };
     // Exponentials of pair p (in cur) and MFMAs of pair p + 1 (into nxt).
