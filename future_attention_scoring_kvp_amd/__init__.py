@@ -10,6 +10,11 @@ built, importing works but every call raises.
     lse  = lse_fwd(q, k)                          # [B, Hq, S]  fp32
     mass = future_mass(q, k, lse, window)         # [B, Hkv, S] fp32
     keep = select_topk(mass, window, n_sink, k)   # [B, Hkv, n_keep] int32
+
+KVpop's training target from the masses:
+
+    mh = future_mass_per_head(q, k, lse, window)  # [B, Hq, S] fp32
+    r  = target_scores(mh, Hkv, window, agg=AGG_MEAN_LOG, eps=1e-6)   # [B, Hkv, S]
 """
 from __future__ import annotations
 
@@ -20,8 +25,9 @@ from typing import Optional
 
 import torch
 
-__all__ = ["lse_fwd", "future_mass", "select_topk", "keep_count", "KvpError", "library_path",
-           "load_library"]
+__all__ = ["lse_fwd", "future_mass", "future_mass_per_head", "target_scores", "select_topk",
+           "keep_count", "KvpError", "library_path", "load_library", "AGG_LOG_MEAN",
+           "AGG_MEAN_LOG", "AGG_MAX_LOG"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvp.so")
@@ -29,6 +35,7 @@ _lock = threading.Lock()
 _lib = None
 
 KVP_BF16, KVP_F32 = 0, 1
+AGG_LOG_MEAN, AGG_MEAN_LOG, AGG_MAX_LOG = 0, 1, 2
 
 
 class KvpError(RuntimeError):
@@ -58,6 +65,12 @@ def load_library():
             lib.kvp_lse_fwd.argtypes = [vp, vp, ctypes.c_int, _Dims, f32, vp, vp]
             lib.kvp_future_mass.restype = ctypes.c_int
             lib.kvp_future_mass.argtypes = [vp, vp, vp, ctypes.c_int, _Dims, f32, i32, vp, vp]
+            lib.kvp_future_mass_per_head.restype = ctypes.c_int
+            lib.kvp_future_mass_per_head.argtypes = [vp, vp, vp, ctypes.c_int, _Dims, f32, i32,
+                                                     vp, vp]
+            lib.kvp_target_scores.restype = ctypes.c_int
+            lib.kvp_target_scores.argtypes = [vp, i32, _Dims, i32, i32, ctypes.c_int, f32, i32,
+                                              i32, vp, vp, vp]
             lib.kvp_keep_count.restype = i64
             lib.kvp_keep_count.argtypes = [i64, i64, i64, i64]
             lib.kvp_select_topk.restype = ctypes.c_int
@@ -146,6 +159,74 @@ def future_mass(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, window: int
     _check(lib.kvp_future_mass(q.data_ptr(), k.data_ptr(), lse.data_ptr(), _dtype_code(q), d,
                                float(scale), int(window), out.data_ptr(), _stream_ptr(stream)),
            "kvp_future_mass")
+    return out
+
+
+def future_mass_per_head(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, window: int,
+                         scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    """Future-attention mass per key for each query head, fp32 [B, Hq, S]."""
+    lib = load_library()
+    _require_device(q, k, lse)
+    d = _dims(q, k)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (d.batch, d.n_q_heads, d.seq_len):
+        raise KvpError("lse must be fp32 [B, Hq, S]")
+    if out is None:
+        out = torch.empty((d.batch, d.n_q_heads, d.seq_len), dtype=torch.float32, device=q.device)
+    _require_device(out)
+    if out.dtype != torch.float32 or tuple(out.shape) != (d.batch, d.n_q_heads, d.seq_len):
+        raise KvpError("mass out must be fp32 [B, Hq, S]")
+    _check(lib.kvp_future_mass_per_head(q.data_ptr(), k.data_ptr(), lse.data_ptr(),
+                                        _dtype_code(q), d, float(scale), int(window),
+                                        out.data_ptr(), _stream_ptr(stream)),
+           "kvp_future_mass_per_head")
+    return out
+
+
+def target_scores(mass: torch.Tensor, n_kv_heads: int, window: int, *, per_head: bool = True,
+                  group_size: Optional[int] = None,
+                  normalize: bool = True, agg: int = AGG_MEAN_LOG, eps: float = 1e-6,
+                  query: int = -1, decay_step: int = 1,
+                  log_gamma: Optional[torch.Tensor] = None,
+                  out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """KVpop target scores fp32 [B, Hkv, S] from masses: [B, Hq, S] per head
+    (``per_head``) or [B, Hkv, S] sums over groups of ``group_size`` query
+    heads.  ``query >= 0`` applies the temporal decay with ``log_gamma``
+    (fp32 [Hkv] on the GPU)."""
+    lib = load_library()
+    _require_device(mass)
+    if mass.dtype != torch.float32 or mass.dim() != 3:
+        raise KvpError("mass must be fp32 [B, H, S]")
+    B, H, S = mass.shape
+    Hkv = int(n_kv_heads)
+    if Hkv < 1:
+        raise KvpError("n_kv_heads must be >= 1")
+    if per_head:
+        if H % Hkv != 0:
+            raise KvpError("query heads must be a multiple of n_kv_heads")
+        Hq = H
+    else:
+        if H != Hkv or group_size is None or int(group_size) < 1:
+            raise KvpError("group-sum masses must be [B, n_kv_heads, S] with group_size >= 1")
+        Hq = Hkv * int(group_size)
+    lg_ptr = None
+    if query >= 0:
+        if log_gamma is None:
+            raise KvpError("decay needs log_gamma [Hkv]")
+        _require_device(log_gamma)
+        if log_gamma.dtype != torch.float32 or tuple(log_gamma.shape) != (Hkv,):
+            raise KvpError("log_gamma must be fp32 [Hkv]")
+        lg_ptr = log_gamma.data_ptr()
+    if out is None:
+        out = torch.empty((B, Hkv, S), dtype=torch.float32, device=mass.device)
+    _require_device(out)
+    if out.dtype != torch.float32 or tuple(out.shape) != (B, Hkv, S):
+        raise KvpError("score out must be fp32 [B, Hkv, S]")
+    d = _Dims(B, Hq, Hkv, S, 128)  # head_dim is not read
+    _check(lib.kvp_target_scores(mass.data_ptr(), 1 if per_head else 0, d, int(window),
+                                 1 if normalize else 0, int(agg), float(eps), int(query),
+                                 int(decay_step), lg_ptr, out.data_ptr(), _stream_ptr(stream)),
+           "kvp_target_scores")
     return out
 
 

@@ -9,11 +9,14 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 // Limits that keep every index the kernels form in 32-bit ints, and the bytes
 // of one head (S * d * 4 at most) within a 32-bit buffer range.
 constexpr int64_t kMaxSeq = int64_t(1) << 22;
 constexpr int64_t kMaxBlocks = (int64_t(1) << 31) - 1;
+// Element-wise kernels index with 64-bit flat indices but launch 256-thread
+// blocks in a 32-bit grid.
+constexpr int64_t kMaxElems = kMaxBlocks * 256;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -98,7 +101,55 @@ kvp_status kvp_future_mass(const void* q, const void* k, const float* lse, kvp_d
   // A window beyond the sequence leaves no future query for any key.
   const int w = window > sh.S ? sh.S : window;
   return from_hip(kvp::launch_mass(q, k, lse, dtype == KVP_BF16 ? 0 : 1, sh,
-                                   resolve_scale(scale, sh.D), w, mass, stream));
+                                   resolve_scale(scale, sh.D), w, 0, mass, stream));
+}
+
+kvp_status kvp_future_mass_per_head(const void* q, const void* k, const float* lse,
+                                    kvp_dtype dtype, kvp_dims dims, float scale, int32_t window,
+                                    float* mass, hipStream_t stream) {
+  kvp::Shape sh;
+  const kvp_status st = check_dims(dims, true, sh);
+  if (st != KVP_OK) return st;
+  if (!valid_dtype(dtype)) return KVP_ERR_UNSUPPORTED;
+  if (std::isnan(scale) || std::isinf(scale) || window < 0) return KVP_ERR_INVALID;
+  if (sh.B == 0 || sh.S == 0) return KVP_OK;
+  if (!q || !k || !lse || !mass || !aligned(q, 16) || !aligned(k, 16) || !aligned(lse, 4) ||
+      !aligned(mass, 4))
+    return KVP_ERR_INVALID;
+  const int w = window > sh.S ? sh.S : window;
+  return from_hip(kvp::launch_mass(q, k, lse, dtype == KVP_BF16 ? 0 : 1, sh,
+                                   resolve_scale(scale, sh.D), w, 1, mass, stream));
+}
+
+kvp_status kvp_target_scores(const float* mass, int32_t per_head, kvp_dims dims, int32_t window,
+                             int32_t normalize, kvp_agg agg, float eps, int32_t query,
+                             int32_t decay_step, const float* log_gamma, float* score,
+                             hipStream_t stream) {
+  if (dims.batch < 0 || dims.seq_len < 0 || dims.n_q_heads < 1 || dims.n_kv_heads < 1 ||
+      dims.n_q_heads % dims.n_kv_heads != 0)
+    return KVP_ERR_INVALID;
+  if (dims.seq_len > kMaxSeq) return KVP_ERR_UNSUPPORTED;
+  if (window < 0 || (per_head != 0 && per_head != 1) || (normalize != 0 && normalize != 1))
+    return KVP_ERR_INVALID;
+  if (agg != KVP_AGG_LOG_MEAN && agg != KVP_AGG_MEAN_LOG && agg != KVP_AGG_MAX_LOG)
+    return KVP_ERR_INVALID;
+  if (!per_head && agg != KVP_AGG_LOG_MEAN) return KVP_ERR_INVALID;  // needs per-head masses
+  if (!(eps >= 0.f) || std::isinf(eps)) return KVP_ERR_INVALID;
+  if (query >= 0 && decay_step < 1) return KVP_ERR_INVALID;
+  if ((int64_t)dims.batch * dims.n_q_heads * dims.seq_len > kMaxElems) return KVP_ERR_UNSUPPORTED;
+  if (dims.batch == 0 || dims.seq_len == 0) return KVP_OK;
+  if (!mass || !score || !aligned(mass, 4) || !aligned(score, 4)) return KVP_ERR_INVALID;
+  if (query >= 0 && (!log_gamma || !aligned(log_gamma, 4))) return KVP_ERR_INVALID;
+  kvp::Shape sh;
+  sh.B = dims.batch;
+  sh.Hq = dims.n_q_heads;
+  sh.Hkv = dims.n_kv_heads;
+  sh.S = dims.seq_len;
+  sh.D = dims.head_dim;
+  sh.G = dims.n_q_heads / dims.n_kv_heads;
+  const int w = window > sh.S ? sh.S : window;
+  return from_hip(kvp::launch_target(mass, per_head, sh, w, normalize, (int)agg, eps, query,
+                                     query >= 0 ? decay_step : 1, log_gamma, score, stream));
 }
 
 kvp_status kvp_select_topk(const float* mass, kvp_dims dims, int32_t window, int32_t n_sink,

@@ -15,8 +15,15 @@ struct Shape {
 // dtype: 0 = bf16, 1 = fp32 (rounded to bf16 on load).
 hipError_t launch_lse(const void* q, const void* k, int dtype, const Shape& sh, float scale,
                       float* lse, hipStream_t stream);
+// per_head = 0: mass [B, Hkv, S] summed over each group; 1: mass [B, Hq, S].
 hipError_t launch_mass(const void* q, const void* k, const float* lse, int dtype, const Shape& sh,
-                       float scale, int window, float* mass, hipStream_t stream);
+                       float scale, int window, int per_head, float* mass, hipStream_t stream);
+// Target scores [B, Hkv, S] from masses ([B, Hq, S] per head or [B, Hkv, S]
+// group sums); agg: 0 log of the mean, 1 mean of the logs, 2 max of the logs;
+// query < 0: no decay.
+hipError_t launch_target(const float* mass, int per_head, const Shape& sh, int window,
+                         int normalize, int agg, float eps, int query, int decay_step,
+                         const float* log_gamma, float* score, hipStream_t stream);
 hipError_t launch_select(const float* mass, int64_t rows, int S, int window, int n_sink,
                          int top_k, int64_t n_keep, int32_t* keep, hipStream_t stream);
 

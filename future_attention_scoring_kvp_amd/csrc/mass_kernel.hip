@@ -3,6 +3,7 @@
 // Computes, for every key j of every (batch, KV head),
 //   mass[j] = sum over the G query heads g of the group,
 //             sum over queries i >= j + window of exp2(c * <q_i, k_j> - lse2_i)
+// (or, in per-head mode, the same sum for each query head on its own)
 // with c = scale * log2(e) and lse2 = LSE * log2(e): the un-normalised future
 // mass of KVpop (§3.1 Eq. 2, App. B.1) recovered from the per-query LSE as in
 // its §3.2 Eq. 8, without any S x S map.
@@ -65,7 +66,9 @@ struct MassArgs {
   const float* lse;
   float* mass;
   int B, Hq, Hkv, S, G, window;
-  float c;  // scale * log2(e)
+  int per_head;  // 0: one unit per (batch, KV head), masses summed over its G
+                 // query heads; 1: one unit per (batch, query head)
+  float c;       // scale * log2(e)
 };
 
 struct Tile {
@@ -82,11 +85,17 @@ __global__ __launch_bounds__(256, 2) void mass_kernel(MassArgs a) {
   __shared__ float l_lds1[C::kSlots * kBlk];
   __shared__ float red_extra[C::kRedInStage ? 1 : C::kWaves * C::kRedWaveFloats];
 
-  const int S = a.S, G = a.G, w = a.window;
+  const int S = a.S, w = a.window;
+  // A unit is a (batch, KV head) whose G query heads are swept together, or
+  // in per-head mode a single (batch, query head) with the keys of its KV head.
+  const int n_heads_out = a.per_head ? a.Hq : a.Hkv;
+  const int G = a.per_head ? 1 : a.G;  // query heads swept per unit
   int unit, tile;
-  xcd_map(blockIdx.x, a.B * a.Hkv, unit, tile);
-  const int b = unit / a.Hkv;
-  const int h = unit - b * a.Hkv;
+  xcd_map(blockIdx.x, a.B * n_heads_out, unit, tile);
+  const int b = unit / n_heads_out;
+  const int ho = unit - b * n_heads_out;                  // output row within the batch
+  const int h = a.per_head ? ho / a.G : ho;               // KV head
+  const int g0 = a.per_head ? ho : ho * a.G;              // first query head swept
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -96,8 +105,8 @@ __global__ __launch_bounds__(256, 2) void mass_kernel(MassArgs a) {
   const int key0 = tile_key0 + wave * C::kKeysPerWave;
 
   const T* __restrict__ kbase = static_cast<const T*>(a.k) + (size_t)(b * a.Hkv + h) * S * D;
-  const T* __restrict__ qgroup = static_cast<const T*>(a.q) + (size_t)(b * a.Hq + h * G) * S * D;
-  const float* __restrict__ lgroup = a.lse + (size_t)(b * a.Hq + h * G) * S;
+  const T* __restrict__ qgroup = static_cast<const T*>(a.q) + (size_t)(b * a.Hq + g0) * S * D;
+  const float* __restrict__ lgroup = a.lse + (size_t)(b * a.Hq + g0) * S;
   const uint32_t head_bytes = (uint32_t)S * D * sizeof(T);
 
   // Stationary keys: A operands of the two 32-row blocks, all slices of d.
@@ -295,12 +304,12 @@ __global__ __launch_bounds__(256, 2) void mass_kernel(MassArgs a) {
 #pragma unroll
   for (int col = 0; col < 32; ++col) tot += red[lane * C::kRedStride + col];
   const int key = key0 + lane;
-  if (key < S) a.mass[(size_t)(b * a.Hkv + h) * S + key] = tot;
+  if (key < S) a.mass[(size_t)(b * n_heads_out + ho) * S + key] = tot;
 }
 
 template <int D, typename T>
 hipError_t launch_mass_t(const void* q, const void* k, const float* lse, const Shape& sh,
-                         float scale, int window, float* mass, hipStream_t stream) {
+                         float scale, int window, int per_head, float* mass, hipStream_t stream) {
   using C = MassCfg<D>;
   MassArgs a;
   a.q = q;
@@ -313,9 +322,10 @@ hipError_t launch_mass_t(const void* q, const void* k, const float* lse, const S
   a.S = sh.S;
   a.G = sh.G;
   a.window = window;
+  a.per_head = per_head;
   a.c = scale * kLog2e;
   const int64_t n_tiles = (sh.S + C::kKeysPerWG - 1) / C::kKeysPerWG;
-  const int64_t blocks = n_tiles * (int64_t)sh.B * sh.Hkv;
+  const int64_t blocks = n_tiles * (int64_t)sh.B * (per_head ? sh.Hq : sh.Hkv);
   hipLaunchKernelGGL((mass_kernel<D, T>), dim3((unsigned)blocks), dim3(C::kThreads), 0, stream, a);
   return hipGetLastError();
 }
@@ -323,12 +333,14 @@ hipError_t launch_mass_t(const void* q, const void* k, const float* lse, const S
 }  // namespace
 
 hipError_t launch_mass(const void* q, const void* k, const float* lse, int dtype, const Shape& sh,
-                       float scale, int window, float* mass, hipStream_t stream) {
+                       float scale, int window, int per_head, float* mass, hipStream_t stream) {
   if (sh.D == 128)
-    return dtype == 0 ? launch_mass_t<128, uint16_t>(q, k, lse, sh, scale, window, mass, stream)
-                      : launch_mass_t<128, float>(q, k, lse, sh, scale, window, mass, stream);
-  return dtype == 0 ? launch_mass_t<64, uint16_t>(q, k, lse, sh, scale, window, mass, stream)
-                    : launch_mass_t<64, float>(q, k, lse, sh, scale, window, mass, stream);
+    return dtype == 0
+               ? launch_mass_t<128, uint16_t>(q, k, lse, sh, scale, window, per_head, mass, stream)
+               : launch_mass_t<128, float>(q, k, lse, sh, scale, window, per_head, mass, stream);
+  return dtype == 0
+             ? launch_mass_t<64, uint16_t>(q, k, lse, sh, scale, window, per_head, mass, stream)
+             : launch_mass_t<64, float>(q, k, lse, sh, scale, window, per_head, mass, stream);
 }
 
 }  // namespace kvp

@@ -1,14 +1,15 @@
 // Per-KV-head keep-set for gfx950.
 //
 //   keep = ascending( sinks [0, min(s, S))  U  window [max(0, S - w), S)
-//                     U  top-k of mass over the eligible range [s, S - w) )
+//                     U  top-k of score over the eligible range [s, S - w) )
 // KVpop Fig. 1 / §3 Eq. 1 (budget s + w + k per KV head) and Eq. 4 (eligible
-// set at the last query).  Ranking: mass descending, equal masses by
-// ascending index.
+// set at the last query).  The scores are future masses or any fp32 score
+// (e.g. the log targets, which are negative).  Ranking: score descending,
+// equal scores by ascending index.
 //
 // One workgroup (256 threads) per (batch, KV head) row:
-//   1. radix select, most significant byte first, on the fp32 bit patterns
-//      (masses are >= 0, so unsigned order = numeric order): four passes of a
+//   1. radix select, most significant byte first, on an order-preserving
+//      32-bit key of each fp32 score (any sign; see score_key): four passes of a
 //      256-bin LDS histogram over the candidates that match the bytes fixed
 //      so far give the k-th largest value T exactly and the number r of
 //      copies of T that belong to the top-k (the r lowest-indexed ones);
@@ -32,7 +33,14 @@ struct SelArgs {
   int64_t n_keep;
 };
 
-__device__ __forceinline__ uint32_t mass_bits(float m) { return __builtin_bit_cast(uint32_t, m); }
+// Order-preserving key of a float: unsigned key order equals numeric order
+// for every non-NaN value (negative values have all bits flipped, positive
+// ones the sign bit set); -0 is first mapped to +0 so that the two zeros tie.
+__device__ __forceinline__ uint32_t score_key(float m) {
+  uint32_t u = __builtin_bit_cast(uint32_t, m);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
 
 // Exclusive prefix (over the workgroup, in thread order) of a 0/1 flag, and
 // the chunk total.  Uses wave ballots and a 4-entry LDS table.
@@ -81,7 +89,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelArgs a) {
       hist[tid] = 0;
       __syncthreads();
       for (int j = e_lo + tid; j < e_hi; j += kSelThreads) {
-        const uint32_t u = mass_bits(m[j]);
+        const uint32_t u = score_key(m[j]);
         if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
       }
       __syncthreads();
@@ -117,7 +125,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelArgs a) {
         if (take_all) {
           kept = true;
         } else {
-          const uint32_t u = mass_bits(m[j]);
+          const uint32_t u = score_key(m[j]);
           kept = u > T;
           is_tie = u == T;
         }

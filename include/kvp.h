@@ -11,6 +11,13 @@
  *   kvp_select_topk  per-KV-head keep-set: sinks, recent window and the top-k
  *                    older tokens by mass.
  *
+ * Two more turn the masses into KVpop's training target:
+ *
+ *   kvp_future_mass_per_head  the future mass of every key for each query head
+ *                             on its own (no group sum);
+ *   kvp_target_scores         count normalisation, log(eps + m), aggregation
+ *                             over the group and the temporal decay.
+ *
  * Sources, cited by page title and section/equation:
  *   [KVpop] "KVpop — Key-Value Cache Compression with Predictive Online
  *           Pruning" (arXiv 2607.05061);
@@ -103,6 +110,45 @@ kvp_status kvp_future_mass(const void* q, const void* k, const float* lse, kvp_d
                            kvp_dims dims, float scale, int32_t window, float* mass,
                            hipStream_t stream);
 
+/* Stage 2, per query head.
+ *   mass[b, g, j] = sum_{i = j + window}^{S-1} exp(scale * <q[b,g,i], k[b,g/G,j]> - lse[b,g,i])
+ * The same pass as kvp_future_mass without the sum over the group: the
+ * un-normalised per-head mass m^(h,g) of [KVpop] §3.1 Eq. 2 / App. B.1, the
+ * input of the per-head aggregation of Eq. 3.  Arguments as kvp_future_mass
+ * except mass: device fp32 [B, Hq, S], written entirely. */
+kvp_status kvp_future_mass_per_head(const void* q, const void* k, const float* lse,
+                                    kvp_dtype dtype, kvp_dims dims, float scale, int32_t window,
+                                    float* mass, hipStream_t stream);
+
+/* Aggregation of the per-head log masses over the query heads of a group
+ * ([KVpop] §3.1 Eq. 3 leaves Agg open; App. B.1 uses the log of the mean). */
+typedef enum {
+  KVP_AGG_LOG_MEAN = 0,  /* log(eps + (1/G) sum_g m_g)      App. B.1            */
+  KVP_AGG_MEAN_LOG = 1,  /* (1/G) sum_g log(eps + m_g)      Eq. 3, Agg = mean   */
+  KVP_AGG_MAX_LOG = 2    /* max_g log(eps + m_g)            Eq. 3, Agg = max    */
+} kvp_agg;
+
+/* KVpop target scores ([KVpop] §3.1 Eq. 2-3, App. B.1-B.3), one per key:
+ *   m_g[t]  = mass[b, g, t] / N_t (per_head = 1) or the group sum / G
+ *             (per_head = 0, only with KVP_AGG_LOG_MEAN), where
+ *             N_t = max(1, S - (t + window)) if normalize (Eq. 2 / B.2), else 1;
+ *   r[t]    = Agg_g log(eps + m_g[t])                    (Eq. 3 / B.1);
+ *   with query >= 0 the decayed score of App. B.3 at query position q:
+ *   r(q)[t] = r[t] + floor((q - t) / decay_step) * log_gamma[h]  for t <= q,
+ *             -inf for t > q (not yet generated).
+ *   mass      : device fp32 [B, Hq, S] (per_head = 1) or [B, Hkv, S] (0), as
+ *               written by kvp_future_mass_per_head / kvp_future_mass.
+ *   eps       : >= 0 (eps = 0 gives -inf for zero mass).
+ *   query     : < 0 for no decay; else decay_step >= 1 and log_gamma is a
+ *               device fp32 [Hkv] array of log(gamma_h) (gamma_h in (0, 1)).
+ *   score     : device fp32 [B, Hkv, S], written entirely.
+ *   dims      : head_dim is not read.
+ * Natural logs in fp32.  The scores can be passed to kvp_select_topk. */
+kvp_status kvp_target_scores(const float* mass, int32_t per_head, kvp_dims dims, int32_t window,
+                             int32_t normalize, kvp_agg agg, float eps, int32_t query,
+                             int32_t decay_step, const float* log_gamma, float* score,
+                             hipStream_t stream);
+
 /* Size of every KV head's keep-set ([KVpop] §3 Eq. 1, budget B = s + w + k,
  * clipped to the sequence):
  *   min(s, S) + |[max(s, S - w), S)| + min(k, max(0, S - w - s)).
@@ -116,11 +162,13 @@ int64_t kvp_keep_count(int64_t seq_len, int64_t window, int64_t n_sink, int64_t 
  * [KVpop] Fig. 1 (sinks and the protected window are always retained, the
  * remaining budget goes to the top-k long-range tokens), Eq. 1 (budget) and
  * Eq. 4 (eligible set at the last query: s <= t <= S-1-w); the StreamingLLM
- * sink rule of [Tut].  Order: mass descending, equal masses by ascending
- * index (lower index wins).  Masses must be >= 0 and not NaN (as written by
- * kvp_future_mass); selection compares their fp32 bit patterns exactly.
- *   mass : device fp32 [B, Hkv, S] (the batch dimension may also stack
- *          layers: any number of independent [Hkv, S] rows).
+ * sink rule of [Tut].  Order: score descending, equal scores by ascending
+ * index (lower index wins).  The scores are masses (kvp_future_mass) or any
+ * fp32 scores of either sign, e.g. kvp_target_scores; -0 equals +0, -inf is
+ * allowed, NaN gives an unspecified keep-set.  Selection compares exactly,
+ * through an order-preserving integer key of every fp32 value.
+ *   mass : device fp32 [B, Hkv, S] scores (the batch dimension may also
+ *          stack layers: any number of independent [Hkv, S] rows).
  *   keep : device int32 [B, Hkv, kvp_keep_count(S, window, n_sink, top_k)].
  *   dims : only batch, n_kv_heads and seq_len are read. */
 kvp_status kvp_select_topk(const float* mass, kvp_dims dims, int32_t window, int32_t n_sink,

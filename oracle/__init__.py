@@ -46,7 +46,7 @@ def _bind(lib):
     lib.oracle_round_bf16.argtypes = [vp, i64, vp]
     lib.oracle_future_mass.restype = cint
     lib.oracle_future_mass.argtypes = [vp, vp, cint, i64, i64, i64, i64, i64, dbl, i64,
-                                       i64, i64, i64, cint, vp, vp, vp, vp]
+                                       i64, i64, i64, cint, vp, vp, vp, vp, vp]
     lib.oracle_lse_rows.restype = cint
     lib.oracle_lse_rows.argtypes = [vp, vp, cint, i64, i64, i64, i64, i64, dbl, vp, i64, cint, vp]
     lib.oracle_keep_count.restype = i64
@@ -95,12 +95,13 @@ def round_bf16(x: np.ndarray, lib=None) -> np.ndarray:
 def future_mass(q: np.ndarray, k: np.ndarray, window: int, scale: float = 0.0, *,
                 b_only: int = -1, h_only: int = -1, row_lo: int = 0,
                 f32_exact: bool = False, nthreads: Optional[int] = None, lib=None,
-                want_rowsum: bool = False, want_winmass: bool = False) -> dict:
+                want_rowsum: bool = False, want_winmass: bool = False,
+                want_per_head: bool = False) -> dict:
     """Dense causal softmax + future mass.  q: [B,Hq,S,D], k: [B,Hkv,S,D], as
     bf16 bit patterns (uint16) or float32 (rounded to bf16 unless
     ``f32_exact``).  Returns dict of fp64 arrays: lse [B,Hq,S], mass
-    [B,Hkv,S] (+ rowsum, winmass).  Entries outside a b_only/h_only/row_lo
-    restriction are NaN."""
+    [B,Hkv,S] (+ rowsum, winmass, and the per-query-head masses mass_heads
+    [B,Hq,S]).  Entries outside a b_only/h_only/row_lo restriction are NaN."""
     lib = lib or load()
     q = np.ascontiguousarray(q)
     k = np.ascontiguousarray(k)
@@ -114,12 +115,14 @@ def future_mass(q: np.ndarray, k: np.ndarray, window: int, scale: float = 0.0, *
     mass = np.full((B, Hkv, S), np.nan)
     rowsum = np.full((B, Hq, S), np.nan) if want_rowsum else None
     winmass = np.full((B, Hq, S), np.nan) if want_winmass else None
+    mass_heads = np.full((B, Hq, S), np.nan) if want_per_head else None
     rc = lib.oracle_future_mass(
         q.ctypes.data, k.ctypes.data, _dtype_code(q, f32_exact), B, Hq, Hkv, S, D,
         float(scale), int(window), int(b_only), int(h_only), int(row_lo),
         nthreads or default_threads(), lse.ctypes.data, mass.ctypes.data,
         rowsum.ctypes.data if rowsum is not None else None,
-        winmass.ctypes.data if winmass is not None else None)
+        winmass.ctypes.data if winmass is not None else None,
+        mass_heads.ctypes.data if mass_heads is not None else None)
     if rc != 0:
         raise ValueError(f"oracle_future_mass rejected the arguments (rc={rc})")
     out = {"lse": lse, "mass": mass}
@@ -127,6 +130,8 @@ def future_mass(q: np.ndarray, k: np.ndarray, window: int, scale: float = 0.0, *
         out["rowsum"] = rowsum
     if winmass is not None:
         out["winmass"] = winmass
+    if mass_heads is not None:
+        out["mass_heads"] = mass_heads
     return out
 
 
@@ -164,3 +169,56 @@ def select(mass: np.ndarray, window: int, n_sink: int, top_k: int, lib=None) -> 
     if rc != 0:
         raise ValueError(f"oracle_select failed (rc={rc})")
     return keep
+
+
+AGG_LOG_MEAN, AGG_MEAN_LOG, AGG_MAX_LOG = 0, 1, 2
+
+
+def target_scores(mass: np.ndarray, window: int, n_kv_heads: int, *, per_head: bool = True,
+                  group_size: Optional[int] = None, normalize: bool = True,
+                  agg: int = AGG_MEAN_LOG, eps: float = 1e-6, query: int = -1,
+                  decay_step: int = 1, log_gamma: Optional[np.ndarray] = None) -> np.ndarray:
+    """KVpop target scores in fp64, [B, Hkv, S], following the page's steps:
+
+    * count normalisation m / N_t with N_t = max(1, S - (t + w))  (§3.1 Eq. 2,
+      App. B.2), or none (App. B.1);
+    * log(eps + m) aggregated over the query heads g of each KV head
+      (§3.1 Eq. 3): agg 0 = log of the group mean (App. B.1), 1 = mean of the
+      logs, 2 = max of the logs;
+    * with query >= 0 the temporal decay of App. B.3,
+      r(q) = r + floor((q - t) / n) * log(gamma_h) for t <= q, and -inf for
+      t > q (not generated yet).
+
+    mass: [B, Hq, S] per-head masses (per_head) or [B, Hkv, S] group sums of
+    group_size heads (only agg 0)."""
+    with np.errstate(divide="ignore"):  # log(0) = -inf is the defined value for eps = 0
+        return _target_scores(np.asarray(mass, dtype=np.float64), window, n_kv_heads, per_head,
+                              group_size, normalize, agg, eps, query, decay_step, log_gamma)
+
+
+def _target_scores(mass, window, n_kv_heads, per_head, group_size, normalize, agg, eps, query,
+                   decay_step, log_gamma):
+    B, H, S = mass.shape
+    t = np.arange(S)
+    n_t = np.maximum(1, S - (t + window)).astype(np.float64) if normalize else np.ones(S)
+    if per_head:
+        G = H // n_kv_heads
+        m = mass.reshape(B, n_kv_heads, G, S) / n_t
+        if agg == AGG_LOG_MEAN:
+            r = np.log(eps + m.mean(axis=2))
+        elif agg == AGG_MEAN_LOG:
+            r = np.log(eps + m).mean(axis=2)
+        elif agg == AGG_MAX_LOG:
+            r = np.log(eps + m).max(axis=2)
+        else:
+            raise ValueError("unknown aggregation")
+    else:
+        if agg != AGG_LOG_MEAN:
+            raise ValueError("group sums only support the log of the group mean")
+        r = np.log(eps + mass / (group_size * n_t))
+    if query >= 0:
+        lg = np.asarray(log_gamma, dtype=np.float64).reshape(1, n_kv_heads, 1)
+        steps = np.where(t <= query, (query - t) // decay_step, 0).astype(np.float64)
+        r = r + steps * lg
+        r = np.where(t <= query, r, -np.inf)
+    return r

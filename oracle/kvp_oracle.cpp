@@ -172,6 +172,9 @@ int oracle_round_bf16(const float* x, int64_t n, uint16_t* out) {
  *
  *   lse[b,g,i]     = ln sum_{j<=i} exp(l_g(i,j))                  ([B,Hq,S])
  *   mass[b,h,j]    = sum_{g: g/G = h} sum_{i >= j+window} p_g(i->j)  ([B,Hkv,S])
+ *   mass_heads[b,g,j] = sum_{i >= j+window} p_g(i->j), each query head on its
+ *                    own: the per-head mass m^(h,g) of [KVpop] §3.1 Eq. 2 in
+ *                    the un-normalised form of App. B.1     ([B,Hq,S]; optional)
  *   rowsum[b,g,i]  = sum_{j<=i} p_g(i->j)          (should be 1; optional)
  *   winmass[b,g,i] = sum_{i-window < j <= i} p_g(i->j)  (in-window mass; optional)
  *
@@ -182,7 +185,8 @@ int oracle_round_bf16(const float* x, int64_t n, uint16_t* out) {
 int oracle_future_mass(const void* q, const void* k, int dtype, int64_t B, int64_t Hq,
                        int64_t Hkv, int64_t S, int64_t D, double scale, int64_t window,
                        int64_t b_only, int64_t h_only, int64_t row_lo, int nthreads,
-                       double* lse, double* mass, double* rowsum, double* winmass) {
+                       double* lse, double* mass, double* rowsum, double* winmass,
+                       double* mass_heads) {
   if (!q || !k || B < 0 || Hq < 1 || Hkv < 1 || S < 0 || D < 1 || Hq % Hkv != 0 ||
       window < 0 || dtype < 0 || dtype > 2 || row_lo < 0)
     return 1;
@@ -237,6 +241,16 @@ int oracle_future_mass(const void* q, const void* k, int dtype, int64_t B, int64
           double acc = 0.0;
           for (int64_t it = 0; it < n_items; ++it) acc += colbuf[it][j];
           out[j] = acc;
+        }
+      }
+      if (mass_heads) {
+        for (int64_t gg = 0; gg < G; ++gg) {
+          double* out = mass_heads + (b * Hq + h * G + gg) * S;
+          for (int64_t j = 0; j < S; ++j) {
+            double acc = 0.0;
+            for (int64_t part = 0; part < kPartitions; ++part) acc += colbuf[gg * kPartitions + part][j];
+            out[j] = acc;
+          }
         }
       }
     }

@@ -33,7 +33,8 @@ def lib():
 def test_header_declares_the_three_stages():
     names = declared_functions()
     for n in ("kvp_lse_fwd", "kvp_future_mass", "kvp_select_topk", "kvp_keep_count",
-              "kvp_status_string", "kvp_abi_version"):
+              "kvp_status_string", "kvp_abi_version", "kvp_future_mass_per_head",
+              "kvp_target_scores"):
         assert n in names
 
 
@@ -43,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.kvp_abi_version() == 1
+    assert lib.kvp_abi_version() == 2
     for code in range(5):
         assert lib.kvp_status_string(code)
     assert lib.kvp_status_string(99) == b"unknown status"
@@ -123,3 +124,35 @@ def test_binding_rejects_cpu_tensors(lib):
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(kvp.KvpError):
         kvp.lse_fwd(q, q)
+
+
+def target_call(lib, mass=FAKE, per_head=1, d=None, w=4, norm=1, agg=1, eps=1e-6, q=-1, n=1,
+                lg=None, out=FAKE):
+    return lib.kvp_target_scores(mass, per_head, d or dims(), w, norm, agg, eps, q, n, lg, out,
+                                 None)
+
+
+def test_mass_per_head_validation(lib):
+    f = lib.kvp_future_mass_per_head
+    assert f(FAKE, FAKE, None, 0, dims(), 0.0, 4, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, 0, dims(), 0.0, -1, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, 0, dims(Hq=6, Hkv=4), 0.0, 4, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, 0, dims(D=96), 0.0, 4, FAKE, None) == UNSUPPORTED
+    assert f(None, None, None, 0, dims(S=0), 0.0, 4, None, None) == OK
+
+
+def test_target_scores_validation(lib):
+    assert target_call(lib, mass=None) == INVALID
+    assert target_call(lib, out=None) == INVALID
+    assert target_call(lib, w=-1) == INVALID
+    assert target_call(lib, per_head=2) == INVALID
+    assert target_call(lib, norm=3) == INVALID
+    assert target_call(lib, agg=7) == INVALID
+    assert target_call(lib, per_head=0, agg=1) == INVALID     # mean of logs needs per-head masses
+    assert target_call(lib, eps=-1.0) == INVALID
+    assert target_call(lib, eps=float("nan")) == INVALID
+    assert target_call(lib, q=10, n=0, lg=FAKE) == INVALID    # decay step must be >= 1
+    assert target_call(lib, q=10, n=4, lg=None) == INVALID    # decay needs log(gamma)
+    assert target_call(lib, d=dims(Hq=3, Hkv=2)) == INVALID
+    assert target_call(lib, d=dims(S=(1 << 22) + 1)) == UNSUPPORTED
+    assert target_call(lib, mass=None, out=None, d=dims(B=0)) == OK
