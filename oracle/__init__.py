@@ -53,6 +53,9 @@ def _bind(lib):
     lib.oracle_keep_count.argtypes = [i64, i64, i64, i64]
     lib.oracle_select.restype = cint
     lib.oracle_select.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp]
+    if hasattr(lib, "oracle_running_cutoff"):
+        lib.oracle_running_cutoff.restype = cint
+        lib.oracle_running_cutoff.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp, vp]
     return lib
 
 
@@ -169,6 +172,24 @@ def select(mass: np.ndarray, window: int, n_sink: int, top_k: int, lib=None) -> 
     if rc != 0:
         raise ValueError(f"oracle_select failed (rc={rc})")
     return keep
+
+
+def running_cutoff(score: np.ndarray, window: int, n_sink: int, top_k: int, lib=None):
+    """KVpop §3.2 running top-k: (rank [B,Hkv,S], cutoff [B,Hkv,S]) int32.
+    rank: position of each token t >= s in the order (priority descending,
+    index ascending), -1 for sinks; cutoff[q]: rank of the k-th best eligible
+    token at query q (Fenwick tree + binary lifting), S when fewer than k are
+    eligible, -1 when k = 0."""
+    lib = lib or load()
+    score = np.ascontiguousarray(score, dtype=np.float64)
+    B, H, S = score.shape
+    rank = np.empty((B, H, S), dtype=np.int32)
+    cutoff = np.empty((B, H, S), dtype=np.int32)
+    rc = lib.oracle_running_cutoff(score.ctypes.data, B, H, S, window, n_sink, top_k,
+                                   rank.ctypes.data, cutoff.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_running_cutoff failed (rc={rc})")
+    return rank, cutoff
 
 
 AGG_LOG_MEAN, AGG_MEAN_LOG, AGG_MAX_LOG = 0, 1, 2

@@ -341,4 +341,68 @@ int oracle_select(const double* mass, int64_t B, int64_t Hkv, int64_t S, int64_t
   return 0;
 }
 
+/* Running top-k cutoff of [KVpop] §3.2 ("Running top-k sparse attention"),
+ * per (b, KV head) row of static priorities score[b,h,:]:
+ *   1. sort the tokens t in [s, S) once by priority (descending; equal
+ *      priorities by ascending index) and give each its rank (0 = best);
+ *      tokens t < s (sinks) get rank -1;
+ *   2. for q = 0 .. S-1 the token t = q - w becomes eligible (Eq. 4,
+ *      E(q) = {s <= t <= q - w}); its rank is inserted into a Fenwick tree
+ *      over ranks, and the rank of the k-th best eligible token is found by
+ *      binary lifting: cutoff[q].  With fewer than k eligible tokens every
+ *      eligible token is retained and cutoff[q] = S; with k = 0 none is and
+ *      cutoff[q] = -1.
+ * At query q an eligible token t is retained iff rank[t] <= cutoff[q].
+ * Returns 0, or 1 on invalid arguments. */
+int oracle_running_cutoff(const double* score, int64_t B, int64_t Hkv, int64_t S, int64_t window,
+                          int64_t n_sink, int64_t top_k, int32_t* rank, int32_t* cutoff) {
+  if (B < 0 || Hkv < 1 || S < 0 || window < 0 || n_sink < 0 || top_k < 0) return 1;
+  if (S > 0 && B > 0 && (!score || !rank || !cutoff)) return 1;
+  const int64_t s = std::min(n_sink, S);
+  const int64_t n = S - s;  // rankable tokens
+  for (int64_t bh = 0; bh < B * Hkv; ++bh) {
+    const double* m = score + bh * S;
+    int32_t* rk = rank + bh * S;
+    int32_t* cut = cutoff + bh * S;
+    std::vector<int64_t> order;
+    for (int64_t t = s; t < S; ++t) order.push_back(t);
+    std::sort(order.begin(), order.end(), [&](int64_t a, int64_t b) {
+      if (m[a] != m[b]) return m[a] > m[b];
+      return a < b;
+    });
+    for (int64_t t = 0; t < s; ++t) rk[t] = -1;
+    for (int64_t r = 0; r < n; ++r) rk[order[r]] = static_cast<int32_t>(r);
+    // Fenwick tree over ranks 1..n (rank r stored at index r + 1)
+    std::vector<int64_t> tree(static_cast<size_t>(n + 1), 0);
+    int64_t top = 1;
+    while (top * 2 <= n) top *= 2;
+    int64_t eligible = 0;
+    for (int64_t q = 0; q < S; ++q) {
+      const int64_t t = q - window;
+      if (t >= s) {
+        for (int64_t i = rk[t] + 1; i <= n; i += i & -i) tree[i] += 1;
+        ++eligible;
+      }
+      if (top_k == 0) {  // no long-range token is retained
+        cut[q] = -1;
+        continue;
+      }
+      if (eligible < top_k) {  // every eligible token is retained
+        cut[q] = static_cast<int32_t>(S);
+        continue;
+      }
+      // binary lifting: largest position p with prefix(p) < k; rank p is the k-th
+      int64_t pos = 0, acc = 0;
+      for (int64_t step = top; step > 0; step /= 2) {
+        if (pos + step <= n && acc + tree[pos + step] < top_k) {
+          pos += step;
+          acc += tree[pos];
+        }
+      }
+      cut[q] = static_cast<int32_t>(pos);  // the k-th best eligible token has rank pos
+    }
+  }
+  return 0;
+}
+
 }  // extern "C"
