@@ -15,6 +15,10 @@ KVpop's training target from the masses:
 
     mh = future_mass_per_head(q, k, lse, window)  # [B, Hq, S] fp32
     r  = target_scores(mh, Hkv, window, agg=AGG_MEAN_LOG, eps=1e-6)   # [B, Hkv, S]
+
+The running top-k mask of every query position:
+
+    rank, cutoff = running_cutoff(r, window, n_sink, k)   # int32 [B, Hkv, S] each
 """
 from __future__ import annotations
 
@@ -26,7 +30,7 @@ from typing import Optional
 import torch
 
 __all__ = ["lse_fwd", "future_mass", "future_mass_per_head", "target_scores", "select_topk",
-           "keep_count", "KvpError", "library_path", "load_library", "AGG_LOG_MEAN",
+           "keep_count", "running_cutoff", "KvpError", "library_path", "load_library", "AGG_LOG_MEAN",
            "AGG_MEAN_LOG", "AGG_MAX_LOG"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -75,6 +79,11 @@ def load_library():
             lib.kvp_keep_count.argtypes = [i64, i64, i64, i64]
             lib.kvp_select_topk.restype = ctypes.c_int
             lib.kvp_select_topk.argtypes = [vp, _Dims, i32, i32, i32, vp, vp]
+            lib.kvp_running_cutoff_workspace_bytes.restype = ctypes.c_size_t
+            lib.kvp_running_cutoff_workspace_bytes.argtypes = [_Dims, i32]
+            lib.kvp_running_cutoff.restype = ctypes.c_int
+            lib.kvp_running_cutoff.argtypes = [vp, _Dims, i32, i32, i32, vp, vp, vp,
+                                               ctypes.c_size_t, vp]
             lib.kvp_status_string.restype = ctypes.c_char_p
             lib.kvp_status_string.argtypes = [ctypes.c_int]
             lib.kvp_abi_version.restype = i32
@@ -253,3 +262,32 @@ def select_topk(mass: torch.Tensor, window: int, n_sink: int, top_k: int,
     _check(lib.kvp_select_topk(mass.data_ptr(), d, int(window), int(n_sink), int(top_k),
                                out.data_ptr(), _stream_ptr(stream)), "kvp_select_topk")
     return out
+
+
+def running_cutoff(score: torch.Tensor, window: int, n_sink: int, top_k: int,
+                   workspace: Optional[torch.Tensor] = None, stream=None):
+    """Static ranks and per-query cutoff ranks of the running top-k, each
+    int32 with the shape of ``score`` ([..., S], leading dims flattened into
+    rows).  Token t >= n_sink is kept at query q iff t <= q - window and
+    rank[t] <= cutoff[q].  ``workspace`` (a uint8 GPU tensor) is allocated
+    when not given."""
+    lib = load_library()
+    _require_device(score)
+    if score.dtype != torch.float32 or score.dim() < 1:
+        raise KvpError("score must be fp32 [..., S]")
+    if window < 0 or n_sink < 0 or top_k < 0:
+        raise KvpError("window, n_sink and top_k must be >= 0")
+    S = score.shape[-1]
+    rows = score.numel() // S if S else 0
+    d = _Dims(rows, 1, 1, S, 128)
+    need = int(lib.kvp_running_cutoff_workspace_bytes(d, int(n_sink)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=score.device)
+    _require_device(workspace)
+    rank = torch.empty(score.shape, dtype=torch.int32, device=score.device)
+    cutoff = torch.empty(score.shape, dtype=torch.int32, device=score.device)
+    _check(lib.kvp_running_cutoff(score.data_ptr(), d, int(window), int(n_sink), int(top_k),
+                                  rank.data_ptr(), cutoff.data_ptr(), workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(),
+                                  _stream_ptr(stream)), "kvp_running_cutoff")
+    return rank, cutoff

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 2;
+constexpr int32_t kAbiVersion = 3;
 // Limits that keep every index the kernels form in 32-bit ints, and the bytes
 // of one head (S * d * 4 at most) within a 32-bit buffer range.
 constexpr int64_t kMaxSeq = int64_t(1) << 22;
@@ -166,6 +166,35 @@ kvp_status kvp_select_topk(const float* mass, kvp_dims dims, int32_t window, int
   const int w = window > S ? S : window;
   const int s = n_sink > S ? S : n_sink;
   return from_hip(kvp::launch_select(mass, rows, S, w, s, top_k, n_keep, keep, stream));
+}
+
+size_t kvp_running_cutoff_workspace_bytes(kvp_dims dims, int32_t n_sink) {
+  if (dims.batch < 0 || dims.seq_len < 0 || dims.n_kv_heads < 1 || n_sink < 0) return 0;
+  const int64_t rows = int64_t(dims.batch) * dims.n_kv_heads;
+  const int S = dims.seq_len;
+  return kvp::cutoff_workspace_bytes(rows, S, n_sink > S ? S : n_sink);
+}
+
+kvp_status kvp_running_cutoff(const float* score, kvp_dims dims, int32_t window, int32_t n_sink,
+                              int32_t top_k, int32_t* rank, int32_t* cutoff, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  if (dims.batch < 0 || dims.seq_len < 0 || dims.n_kv_heads < 1) return KVP_ERR_INVALID;
+  if (window < 0 || n_sink < 0 || top_k < 0) return KVP_ERR_INVALID;
+  if (dims.seq_len > kMaxSeq) return KVP_ERR_UNSUPPORTED;
+  const int64_t rows = int64_t(dims.batch) * dims.n_kv_heads;
+  if (rows > kMaxBlocks) return KVP_ERR_UNSUPPORTED;
+  if (rows == 0 || dims.seq_len == 0) return KVP_OK;
+  if (!score || !rank || !cutoff || !aligned(score, 4) || !aligned(rank, 4) ||
+      !aligned(cutoff, 4))
+    return KVP_ERR_INVALID;
+  const int S = dims.seq_len;
+  const int w = window > S ? S : window;
+  const int s = n_sink > S ? S : n_sink;
+  const size_t need = kvp::cutoff_workspace_bytes(rows, S, s);
+  if (workspace_bytes < need) return KVP_ERR_WORKSPACE;
+  if (need > 0 && (!workspace || !aligned(workspace, 4))) return KVP_ERR_INVALID;
+  return from_hip(kvp::launch_cutoff(score, rows, S, w, s, top_k, rank, cutoff, workspace,
+                                     stream));
 }
 
 }  // extern "C"

@@ -27,4 +27,11 @@ hipError_t launch_target(const float* mass, int per_head, const Shape& sh, int w
 hipError_t launch_select(const float* mass, int64_t rows, int S, int window, int n_sink,
                          int top_k, int64_t n_keep, int32_t* keep, hipStream_t stream);
 
+// Running top-k cutoff: rank [rows, S] and cutoff [rows, S] (int32) from
+// scores [rows, S]; workspace of cutoff_workspace_bytes(rows, S, n_sink).
+size_t cutoff_workspace_bytes(int64_t rows, int S, int n_sink);
+hipError_t launch_cutoff(const float* score, int64_t rows, int S, int window, int n_sink,
+                         int top_k, int32_t* rank, int32_t* cutoff, void* workspace,
+                         hipStream_t stream);
+
 }  // namespace kvp

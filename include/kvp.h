@@ -18,6 +18,12 @@
  *   kvp_target_scores         count normalisation, log(eps + m), aggregation
  *                             over the group and the temporal decay.
  *
+ * And one gives the keep-set of every query position rather than only the
+ * last one:
+ *
+ *   kvp_running_cutoff        static ranks and the per-query cutoff rank of
+ *                             the running top-k (the sparse mask predicate).
+ *
  * Sources, cited by page title and section/equation:
  *   [KVpop] "KVpop — Key-Value Cache Compression with Predictive Online
  *           Pruning" (arXiv 2607.05061);
@@ -173,6 +179,41 @@ int64_t kvp_keep_count(int64_t seq_len, int64_t window, int64_t n_sink, int64_t 
  *   dims : only batch, n_kv_heads and seq_len are read. */
 kvp_status kvp_select_topk(const float* mass, kvp_dims dims, int32_t window, int32_t n_sink,
                            int32_t top_k, int32_t* keep, hipStream_t stream);
+
+/* Bytes of device workspace kvp_running_cutoff needs for `dims` (batch,
+ * n_kv_heads and seq_len are read) and `n_sink`: 20 * B * Hkv * (S - min(s, S)).
+ * Pure host function; 0 for invalid arguments. */
+size_t kvp_running_cutoff_workspace_bytes(kvp_dims dims, int32_t n_sink);
+
+/* Running top-k cutoff ([KVpop] §3.2 "Efficient Target Implementation", the
+ * paragraphs on running top-k sparse attention and on its kernel; Appendix I).
+ * Per (b, h) row of static priorities score[b, h, 0..S):
+ *   rank[b, h, t]   = position of t in the order of { s <= t' < S } by
+ *                     score descending, equal scores by ascending index
+ *                     (0 = best); -1 for the sinks t < s;
+ *   cutoff[b, h, q] = rank of the k-th best token of the eligible set
+ *                     E(q) = { s <= t <= q - window } (Eq. 4), or
+ *                     S  while |E(q)| < k (every eligible token is kept),
+ *                     -1 if top_k = 0 (none is).
+ * At query q the sparse attention mask keeps the sinks, the window
+ * (q - window < t <= q) and the eligible tokens t with
+ * rank[b, h, t] <= cutoff[b, h, q]; at q = S - 1 this is exactly the
+ * keep-set of kvp_select_topk.  Scores, their comparison and the signed-zero
+ * / -inf / NaN rules are those of kvp_select_topk.
+ *   score     : device fp32 [B, Hkv, S] (batch may stack layers).
+ *   rank      : device int32 [B, Hkv, S], written entirely.
+ *   cutoff    : device int32 [B, Hkv, S], written entirely.
+ *   workspace : device scratch of at least
+ *               kvp_running_cutoff_workspace_bytes(dims, n_sink) bytes, 4-byte
+ *               aligned, owned by the caller (NULL allowed when that is 0);
+ *               its contents on entry and exit are unspecified.
+ *               KVP_ERR_WORKSPACE if workspace_bytes is smaller.
+ *   dims      : only batch, n_kv_heads and seq_len are read.
+ * Results are exact (integer ranks); two kernels: a per-row stable radix
+ * sort, then a per-row sweep over q whose cutoff only moves down. */
+kvp_status kvp_running_cutoff(const float* score, kvp_dims dims, int32_t window, int32_t n_sink,
+                              int32_t top_k, int32_t* rank, int32_t* cutoff, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
 
 /* Static string for a status code. */
 const char* kvp_status_string(kvp_status status);

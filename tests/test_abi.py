@@ -12,7 +12,7 @@ import future_attention_scoring_kvp_amd as kvp
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvp.h")
 
-OK, INVALID, UNSUPPORTED = 0, 1, 2
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
 FAKE = 0x100000  # never dereferenced: every call below fails validation or is empty
 
 
@@ -34,7 +34,7 @@ def test_header_declares_the_three_stages():
     names = declared_functions()
     for n in ("kvp_lse_fwd", "kvp_future_mass", "kvp_select_topk", "kvp_keep_count",
               "kvp_status_string", "kvp_abi_version", "kvp_future_mass_per_head",
-              "kvp_target_scores"):
+              "kvp_target_scores", "kvp_running_cutoff", "kvp_running_cutoff_workspace_bytes"):
         assert n in names
 
 
@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.kvp_abi_version() == 2
+    assert lib.kvp_abi_version() == 3
     for code in range(5):
         assert lib.kvp_status_string(code)
     assert lib.kvp_status_string(99) == b"unknown status"
@@ -156,3 +156,31 @@ def test_target_scores_validation(lib):
     assert target_call(lib, d=dims(Hq=3, Hkv=2)) == INVALID
     assert target_call(lib, d=dims(S=(1 << 22) + 1)) == UNSUPPORTED
     assert target_call(lib, mass=None, out=None, d=dims(B=0)) == OK
+
+
+def cutoff_call(lib, score=FAKE, d=None, w=4, s=4, k=8, rank=FAKE, cut=FAKE, ws=FAKE,
+                ws_bytes=1 << 30):
+    return lib.kvp_running_cutoff(score, d or dims(), w, s, k, rank, cut, ws, ws_bytes, None)
+
+
+def test_running_cutoff_workspace_and_validation(lib):
+    size = lib.kvp_running_cutoff_workspace_bytes
+    # pos + two (key, index) ping-pong buffers per rankable token
+    assert size(dims(B=2, Hkv=3, S=100), 4) == 2 * 3 * 96 * 20
+    assert size(dims(S=100), 200) == 0           # every token is a sink
+    assert size(dims(S=0), 0) == 0
+    assert size(dims(B=-1), 0) == 0
+    assert cutoff_call(lib, score=None) == INVALID
+    assert cutoff_call(lib, rank=None) == INVALID
+    assert cutoff_call(lib, cut=None) == INVALID
+    assert cutoff_call(lib, score=FAKE + 2) == INVALID
+    assert cutoff_call(lib, w=-1) == INVALID
+    assert cutoff_call(lib, s=-1) == INVALID
+    assert cutoff_call(lib, k=-1) == INVALID
+    assert cutoff_call(lib, d=dims(Hkv=0)) == INVALID
+    assert cutoff_call(lib, ws=None) == INVALID
+    need = size(dims(), 4)
+    assert cutoff_call(lib, ws_bytes=need - 1) == WORKSPACE
+    assert cutoff_call(lib, d=dims(S=(1 << 22) + 1)) == UNSUPPORTED
+    assert cutoff_call(lib, score=None, rank=None, cut=None, ws=None, d=dims(B=0)) == OK
+    assert cutoff_call(lib, score=None, rank=None, cut=None, ws=None, d=dims(S=0)) == OK
