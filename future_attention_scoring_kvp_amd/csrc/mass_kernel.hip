@@ -9,13 +9,16 @@
 // its §3.2 Eq. 8, without any S x S map.
 //
 // Work decomposition (keys stationary, queries streamed):
-//   * one workgroup = 4 waves = 256 consecutive keys of one (batch, KV head);
+//   * one workgroup = 8 waves = 512 consecutive keys of one (batch, KV head),
+//     one workgroup per CU (two waves of the same workgroup per SIMD, so the
+//     co-resident waves advance together and a tile's time follows its work);
 //     each wave keeps its 64 keys (two 32-row MFMA blocks, all of d) as bf16
 //     A operands in registers for the whole sweep;
 //   * the workgroup sweeps the future (query block, head) pairs of its group
 //     -- query blocks of 32 from the end of the sequence backwards, the G
-//     heads of a block consecutively -- four pairs per LDS stage, double
-//     buffered; wave w stages pair w of every stage;
+//     heads of a block consecutively -- eight pairs per LDS stage, double
+//     buffered; wave w stages pair w of every stage, and every staged pair
+//     feeds all 512 keys;
 //   * in LDS a pair is stored as the MFMA B operands themselves: per 16-wide
 //     slice of d, 1 KB holding lane l's 16 bytes at 16 l, copied from HBM
 //     through VGPRs in two halves, so every operand read is one contiguous,
@@ -42,7 +45,7 @@ namespace {
 
 template <int D>
 struct MassCfg {
-  static constexpr int kWaves = 4;
+  static constexpr int kWaves = 8;
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kKeysPerWave = 64;
   static constexpr int kKeysPerWG = kWaves * kKeysPerWave;
@@ -55,9 +58,10 @@ struct MassCfg {
   static constexpr int kValuPerPair = 3 * 32;           // fma + exp + add per value
   static constexpr int kRedStride = 33;                 // column partials per key (+1 pad)
   static constexpr int kRedWaveFloats = kKeysPerWave * kRedStride;
-  // the final reduction reuses the stage buffers (two waves per buffer) when
-  // they are large enough
-  static constexpr bool kRedInStage = 2 * kRedWaveFloats * 4 <= kStageBytes;
+  // the final reduction reuses the two stage buffers when they hold every
+  // wave's partials
+  static constexpr int kRedWavesPerBuf = kStageBytes / (kRedWaveFloats * 4);
+  static constexpr bool kRedInStage = 2 * kRedWavesPerBuf >= kWaves;
 };
 
 struct MassArgs {
@@ -77,7 +81,7 @@ struct Tile {
 };
 
 template <int D, typename T>
-__global__ __launch_bounds__(256, 2) void mass_kernel(MassArgs a) {
+__global__ __launch_bounds__(MassCfg<D>::kThreads, 1) void mass_kernel(MassArgs a) {
   using C = MassCfg<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char q_lds0[C::kStageBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char q_lds1[C::kStageBytes];
@@ -247,6 +251,15 @@ __global__ __launch_bounds__(256, 2) void mass_kernel(MassArgs a) {
     };
 
     Tile t0, t1;
+    // One stage: the exponentials of its kSlots pairs; the MFMAs of each next
+    // pair are issued one step ahead, the last step's from the other buffer
+    // once the barrier has published it.  The copies for the next stage are
+    // issued at the start and stored in two halves further on, so each half
+    // has a few steps to arrive.
+    static_assert(C::kSlots % 2 == 0 && C::kSlots >= 4, "tile ping-pong needs an even stage");
+    constexpr int kStoreA = C::kSlots / 4;      // store half 0 after this step
+    constexpr int kStoreB = C::kSlots / 2 + 1 < C::kSlots - 2 ? C::kSlots / 2 + 1
+                                                              : C::kSlots - 2;  // store half 1 after this step
     auto stage = [&](auto bufc, int st) __attribute__((always_inline)) {
       constexpr int kBuf = decltype(bufc)::value;
       unsigned char* cq = kBuf ? q_lds1 : q_lds0;
@@ -256,19 +269,23 @@ __global__ __launch_bounds__(256, 2) void mass_kernel(MassArgs a) {
       const bool more = st + 1 < n_stages;
       if (more) issue_loads(st + 1, 0);
       const int p0 = st * C::kSlots;
-      step(t0, t1, p0 + 0, cq, cl, 1);
-      if (more) {
-        store_half(st + 1, 0, nq);
-        issue_loads(st + 1, 1);
-      }
-      step(t1, t0, p0 + 1, cq, cl, 2);
-      step(t0, t1, p0 + 2, cq, cl, 3);
-      if (more) {
-        store_half(st + 1, 1, nq);
-        finish_loads(st + 1, nl);
+#pragma unroll
+      for (int j = 0; j < C::kSlots - 1; ++j) {
+        if (j & 1)
+          step(t1, t0, p0 + j, cq, cl, j + 1);
+        else
+          step(t0, t1, p0 + j, cq, cl, j + 1);
+        if (more && j == kStoreA) {
+          store_half(st + 1, 0, nq);
+          issue_loads(st + 1, 1);
+        }
+        if (more && j == kStoreB) {
+          store_half(st + 1, 1, nq);
+          finish_loads(st + 1, nl);
+        }
       }
       __syncthreads();
-      step(t1, t0, p0 + 3, nq, nl, 0);
+      step(t1, t0, p0 + C::kSlots - 1, nq, nl, 0);
     };
 
     issue_loads(0, 0);
@@ -289,9 +306,11 @@ __global__ __launch_bounds__(256, 2) void mass_kernel(MassArgs a) {
   // keys per block; add the 32 columns of every key in LDS in a fixed order.
   __syncthreads();
   float* red;
-  if constexpr (C::kRedInStage)
-    red = reinterpret_cast<float*>(wave < 2 ? q_lds0 : q_lds1) + (wave & 1) * C::kRedWaveFloats;
-  else
+  if constexpr (C::kRedInStage) {
+    constexpr int kPer = C::kRedWavesPerBuf;
+    red = reinterpret_cast<float*>(wave < kPer ? q_lds0 : q_lds1) +
+          (wave < kPer ? wave : wave - kPer) * C::kRedWaveFloats;
+  } else
     red = red_extra + wave * C::kRedWaveFloats;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
