@@ -23,6 +23,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+constexpr int kNumCUs = 256;     // MI355X: 8 XCDs x 32 compute units
 constexpr int kBlk = 32;          // MFMA tile edge (rows = keys, cols = queries)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;

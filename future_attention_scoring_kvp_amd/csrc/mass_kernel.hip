@@ -11,14 +11,16 @@
 // Work decomposition (keys stationary, queries streamed):
 //   * one workgroup = 8 waves = 512 consecutive keys of one (batch, KV head),
 //     one workgroup per CU (two waves of the same workgroup per SIMD, so the
-//     co-resident waves advance together and a tile's time follows its work);
+//     co-resident waves advance together and a tile's time follows its work;
+//     two workgroups on one CU issue at very different rates, oldest first);
+//     grids too small for two workgroups per CU use 4 waves = 256 keys;
 //     each wave keeps its 64 keys (two 32-row MFMA blocks, all of d) as bf16
 //     A operands in registers for the whole sweep;
 //   * the workgroup sweeps the future (query block, head) pairs of its group
 //     -- query blocks of 32 from the end of the sequence backwards, the G
-//     heads of a block consecutively -- eight pairs per LDS stage, double
-//     buffered; wave w stages pair w of every stage, and every staged pair
-//     feeds all 512 keys;
+//     heads of a block consecutively -- one pair per wave per LDS stage,
+//     double buffered; wave w stages pair w of every stage, and every staged
+//     pair feeds all keys of the workgroup;
 //   * in LDS a pair is stored as the MFMA B operands themselves: per 16-wide
 //     slice of d, 1 KB holding lane l's 16 bytes at 16 l, copied from HBM
 //     through VGPRs in two halves, so every operand read is one contiguous,
@@ -43,9 +45,9 @@
 namespace kvp {
 namespace {
 
-template <int D>
+template <int D, int W>
 struct MassCfg {
-  static constexpr int kWaves = 8;
+  static constexpr int kWaves = W;
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kKeysPerWave = 64;
   static constexpr int kKeysPerWG = kWaves * kKeysPerWave;
@@ -80,9 +82,9 @@ struct Tile {
   float l2;         // lse2 of this lane's query column
 };
 
-template <int D, typename T>
-__global__ __launch_bounds__(MassCfg<D>::kThreads, 1) void mass_kernel(MassArgs a) {
-  using C = MassCfg<D>;
+template <int D, typename T, int W>
+__global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
+  using C = MassCfg<D, W>;
   __shared__ __attribute__((aligned(1024))) unsigned char q_lds0[C::kStageBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char q_lds1[C::kStageBytes];
   __shared__ float l_lds0[C::kSlots * kBlk];
@@ -257,9 +259,10 @@ __global__ __launch_bounds__(MassCfg<D>::kThreads, 1) void mass_kernel(MassArgs 
     // issued at the start and stored in two halves further on, so each half
     // has a few steps to arrive.
     static_assert(C::kSlots % 2 == 0 && C::kSlots >= 4, "tile ping-pong needs an even stage");
-    constexpr int kStoreA = C::kSlots / 4;      // store half 0 after this step
-    constexpr int kStoreB = C::kSlots / 2 + 1 < C::kSlots - 2 ? C::kSlots / 2 + 1
-                                                              : C::kSlots - 2;  // store half 1 after this step
+    constexpr int kStoreA = C::kSlots == 8 ? 1 : 0;  // store half 0 after this step
+    constexpr int kStoreB = C::kSlots == 8 ? 3 : 2;  // store half 1 after this step
+    static_assert(kStoreA < kStoreB && kStoreB <= C::kSlots - 2,
+                  "both halves must be stored before the stage's last step");
     auto stage = [&](auto bufc, int st) __attribute__((always_inline)) {
       constexpr int kBuf = decltype(bufc)::value;
       unsigned char* cq = kBuf ? q_lds1 : q_lds0;
@@ -326,10 +329,10 @@ __global__ __launch_bounds__(MassCfg<D>::kThreads, 1) void mass_kernel(MassArgs 
   if (key < S) a.mass[(size_t)(b * n_heads_out + ho) * S + key] = tot;
 }
 
-template <int D, typename T>
-hipError_t launch_mass_t(const void* q, const void* k, const float* lse, const Shape& sh,
+template <int D, typename T, int W>
+hipError_t launch_mass_w(const void* q, const void* k, const float* lse, const Shape& sh,
                          float scale, int window, int per_head, float* mass, hipStream_t stream) {
-  using C = MassCfg<D>;
+  using C = MassCfg<D, W>;
   MassArgs a;
   a.q = q;
   a.k = k;
@@ -345,8 +348,22 @@ hipError_t launch_mass_t(const void* q, const void* k, const float* lse, const S
   a.c = scale * kLog2e;
   const int64_t n_tiles = (sh.S + C::kKeysPerWG - 1) / C::kKeysPerWG;
   const int64_t blocks = n_tiles * (int64_t)sh.B * (per_head ? sh.Hq : sh.Hkv);
-  hipLaunchKernelGGL((mass_kernel<D, T>), dim3((unsigned)blocks), dim3(C::kThreads), 0, stream, a);
+  hipLaunchKernelGGL((mass_kernel<D, T, W>), dim3((unsigned)blocks), dim3(C::kThreads), 0, stream,
+                     a);
   return hipGetLastError();
+}
+
+// 512-key workgroups (one per CU) when the grid has at least two per CU;
+// otherwise 256-key workgroups (two per CU), which double the workgroup count
+// of short sequences.
+template <int D, typename T>
+hipError_t launch_mass_t(const void* q, const void* k, const float* lse, const Shape& sh,
+                         float scale, int window, int per_head, float* mass, hipStream_t stream) {
+  const int64_t units = (int64_t)sh.B * (per_head ? sh.Hq : sh.Hkv);
+  const int64_t blocks8 = units * ((sh.S + MassCfg<D, 8>::kKeysPerWG - 1) / MassCfg<D, 8>::kKeysPerWG);
+  if (blocks8 >= 2 * kNumCUs)
+    return launch_mass_w<D, T, 8>(q, k, lse, sh, scale, window, per_head, mass, stream);
+  return launch_mass_w<D, T, 4>(q, k, lse, sh, scale, window, per_head, mass, stream);
 }
 
 }  // namespace
