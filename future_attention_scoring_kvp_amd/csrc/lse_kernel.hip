@@ -5,12 +5,15 @@
 // per-query log-normaliser that KVpop §3.2 (Eq. 8) reuses for the future mass.
 //
 // Work decomposition (queries stationary, keys streamed):
-//   * one workgroup = 4 waves; each wave owns 64 consecutive query positions
-//     of one query head (two 32-column MFMA blocks kept as bf16 B operands in
-//     registers); the 4 waves cover (position block, head) pairs of one GQA
-//     group, heads fastest, so the group's shared keys are staged once;
-//   * keys are streamed in blocks of 32 from position 0 upwards, four blocks
-//     per LDS stage, double buffered; wave w stages block w of every stage.
+//   * one workgroup = 8 waves (one per CU; 4 waves, two per CU, for grids
+//     too small to give every CU two); each wave owns 64 consecutive query
+//     positions of one query head (two 32-column MFMA blocks kept as bf16 B
+//     operands in registers); the waves cover (position block, head) pairs
+//     of one GQA group, heads fastest, so the group's shared keys are staged
+//     once for all of them;
+//   * keys are streamed in blocks of 32 from position 0 upwards, one block
+//     per wave per LDS stage, double buffered; wave w stages block w of
+//     every stage.
 //     In LDS a key block is stored as the MFMA A operands themselves (per
 //     16-wide slice of d, 1 KB with lane l's 16 bytes at 16 l), copied from
 //     HBM through VGPRs in two halves, so every operand read is one
@@ -35,9 +38,9 @@
 namespace kvp {
 namespace {
 
-template <int D>
+template <int D, int W>
 struct LseCfg {
-  static constexpr int kWaves = 4;
+  static constexpr int kWaves = W;
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kQueriesPerWave = 64;
   static constexpr int kKSteps = D / 16;          // 16-wide slices of d
@@ -62,9 +65,9 @@ struct LTile {
   f32x16_t s0, s1;  // logits: 32 keys (rows) x query half 0 / 1 (columns)
 };
 
-template <int D, typename T>
-__global__ __launch_bounds__(256, 2) void lse_kernel(LseArgs a) {
-  using C = LseCfg<D>;
+template <int D, typename T, int W>
+__global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
+  using C = LseCfg<D, W>;
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[C::kStageBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[C::kStageBytes];
 
@@ -223,6 +226,14 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(LseArgs a) {
   };
 
   LTile t0, t1;
+  // One stage: the exponentials of its kSlots key blocks, the MFMAs of each
+  // next block one step ahead (the last step's from the other buffer, after
+  // the barrier); the next stage's copies are stored in two halves.
+  static_assert(C::kSlots % 2 == 0 && C::kSlots >= 4, "tile ping-pong needs an even stage");
+  constexpr int kStoreA = C::kSlots == 8 ? 1 : 0;  // store half 0 after this step
+  constexpr int kStoreB = C::kSlots == 8 ? 3 : 2;  // store half 1 after this step
+  static_assert(kStoreA < kStoreB && kStoreB <= C::kSlots - 2,
+                "both halves must be stored before the stage's last step");
   auto stage = [&](auto bufc, int st) __attribute__((always_inline)) {
     constexpr int kBuf = decltype(bufc)::value;
     unsigned char* ck = kBuf ? k_lds1 : k_lds0;
@@ -230,16 +241,20 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(LseArgs a) {
     const bool more = st + 1 < n_stages;
     if (more) issue_loads(st + 1, 0);
     const int kb0 = st * C::kSlots;
-    step(t0, t1, kb0 + 0, ck, 1);
-    if (more) {
-      store_half(st + 1, 0, nk);
-      issue_loads(st + 1, 1);
+#pragma unroll
+    for (int j = 0; j < C::kSlots - 1; ++j) {
+      if (j & 1)
+        step(t1, t0, kb0 + j, ck, j + 1);
+      else
+        step(t0, t1, kb0 + j, ck, j + 1);
+      if (more && j == kStoreA) {
+        store_half(st + 1, 0, nk);
+        issue_loads(st + 1, 1);
+      }
+      if (more && j == kStoreB) store_half(st + 1, 1, nk);
     }
-    step(t1, t0, kb0 + 1, ck, 2);
-    step(t0, t1, kb0 + 2, ck, 3);
-    if (more) store_half(st + 1, 1, nk);
     __syncthreads();
-    step(t1, t0, kb0 + 3, nk, 0);
+    step(t1, t0, kb0 + C::kSlots - 1, nk, 0);
   };
 
   issue_loads(0, 0);
@@ -324,10 +339,10 @@ __global__ __launch_bounds__(256) void lse_fix_kernel(LseArgs a, float scale) {
   }
 }
 
-template <int D, typename T>
-hipError_t launch_lse_t(const void* q, const void* k, const Shape& sh, float scale, float* lse,
+template <int D, typename T, int W>
+hipError_t launch_lse_w(const void* q, const void* k, const Shape& sh, float scale, float* lse,
                         hipStream_t stream) {
-  using C = LseCfg<D>;
+  using C = LseCfg<D, W>;
   LseArgs a;
   a.q = q;
   a.k = k;
@@ -341,7 +356,8 @@ hipError_t launch_lse_t(const void* q, const void* k, const Shape& sh, float sca
   const int64_t n_pb = (sh.S + C::kQueriesPerWave - 1) / C::kQueriesPerWave;
   a.n_wg = (int)((n_pb * sh.G + C::kWaves - 1) / C::kWaves);
   const int64_t blocks = (int64_t)a.n_wg * sh.B * sh.Hkv;
-  hipLaunchKernelGGL((lse_kernel<D, T>), dim3((unsigned)blocks), dim3(C::kThreads), 0, stream, a);
+  hipLaunchKernelGGL((lse_kernel<D, T, W>), dim3((unsigned)blocks), dim3(C::kThreads), 0, stream,
+                     a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t rows = (int64_t)sh.B * sh.Hq * sh.S;
@@ -349,6 +365,17 @@ hipError_t launch_lse_t(const void* q, const void* k, const Shape& sh, float sca
   hipLaunchKernelGGL((lse_fix_kernel<D, T>), dim3((unsigned)fix_blocks), dim3(256), 0, stream, a,
                      scale);
   return hipGetLastError();
+}
+
+// 8-wave workgroups (one per CU) when the grid holds at least two per CU,
+// else 4-wave workgroups (two per CU).
+template <int D, typename T>
+hipError_t launch_lse_t(const void* q, const void* k, const Shape& sh, float scale, float* lse,
+                        hipStream_t stream) {
+  const int64_t n_pb = (sh.S + LseCfg<D, 8>::kQueriesPerWave - 1) / LseCfg<D, 8>::kQueriesPerWave;
+  const int64_t blocks8 = (n_pb * sh.G + 7) / 8 * sh.B * sh.Hkv;
+  if (blocks8 >= 2 * kNumCUs) return launch_lse_w<D, T, 8>(q, k, sh, scale, lse, stream);
+  return launch_lse_w<D, T, 4>(q, k, sh, scale, lse, stream);
 }
 
 }  // namespace
