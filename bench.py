@@ -16,6 +16,11 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
                launch over its average launch time, measured with HIP events
                on the stream it runs on, against the bf16 dense MFMA peak
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
+  next_rows    after the timed steps: the per-head mass pass, the KVpop target
+               epilogue and the running top-k cutoff on the same layers
+  roofline.traffic is the HBM bytes per mass-kernel launch from the committed
+  counter summary (profiles/), reported only while the kernel sources still
+  hash to the value recorded there
 
     python bench.py [--steps K] [--warmup W] [--workload N] [--no-cpu-baseline]
     python bench.py --copy-probe BYTES   # plain copy kernel, for counter scaling
@@ -23,8 +28,10 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -46,6 +53,37 @@ def mass_pairs(B: int, Hq: int, S: int, w: int) -> int:
     head, query i, key j) with j + w <= i."""
     n = max(S - w, 0)
     return B * Hq * n * (n + 1) // 2
+
+
+MASS_SOURCES = ("future_attention_scoring_kvp_amd/csrc/mass_kernel.hip",
+                "future_attention_scoring_kvp_amd/csrc/kvp_device.h")
+TRAFFIC_SUMMARY = "profiles/mass_kernel_qwen3_4b_32k_pmc.md"
+
+
+def mass_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for rel in MASS_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload_name: str):
+    """HBM bytes per mass-kernel launch recorded in the counter summary, or
+    None if there is none for this workload or the kernel has changed since."""
+    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    fields = dict(re.findall(r"^([a-z_0-9]+):\s*(\S+)\s*$", text, flags=re.M))
+    if fields.get("workload") != workload_name:
+        return None
+    if fields.get("kernel_sources_sha256") != mass_sources_sha256():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def copy_probe(nbytes: int, reps: int) -> None:
@@ -80,6 +118,58 @@ def cpu_baseline(wl, li0, n_heads: int) -> dict:
                        f"all {S} query rows: {pairs} future-mass pairs, LSE included")}
 
 
+def next_rows(kvp, torch, wl, L, q_all, k_all, lse_all, stream) -> dict:
+    """Per-launch times of the entry points beyond the three-stage path, on
+    the same resident layers (not part of the timed steps): the per-query-head
+    mass pass (every layer), the target epilogue over all layers' per-head
+    masses in one launch, and the running top-k cutoff over all (layer, KV
+    head) rows of those scores in one launch."""
+    B, Hq, Hkv, S, D = wl.B, wl.Hq, wl.Hkv, wl.S, wl.D
+    w, s, k = wl.window, wl.n_sink, wl.top_k
+    dev = q_all.device
+    mh_all = torch.empty((L * B, Hq, S), dtype=torch.float32, device=dev)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def per_head_all():
+        for l in range(L):
+            kvp.future_mass_per_head(q_all[l], k_all[l], lse_all[l], w,
+                                     out=mh_all[l * B:(l + 1) * B])
+
+    ph_ms = timed(per_head_all, 1) / L
+    pairs = mass_pairs(B, Hq, S, w)
+    score = torch.empty((L * B, Hkv, S), dtype=torch.float32, device=dev)
+    tgt_ms = timed(lambda: kvp.target_scores(mh_all, Hkv, w, agg=kvp.AGG_MEAN_LOG, eps=1e-6,
+                                             out=score), 10)
+    tgt_bytes = 4 * L * B * (Hq + Hkv) * S
+    rows = L * B * Hkv
+    ws = torch.empty(max(1, 20 * rows * (S - min(s, S))), dtype=torch.uint8, device=dev)
+    cut_ms = timed(lambda: kvp.running_cutoff(score, w, s, k, workspace=ws), 3)
+    log(f"bench: per-head mass {ph_ms:.3f} ms/layer, target {tgt_ms:.4f} ms, "
+        f"running cutoff {cut_ms:.3f} ms ({rows} rows)")
+    return {
+        "mass_per_head": {"ms_per_layer": round(ph_ms, 4),
+                          "gpairs_per_s": round(pairs / (ph_ms * 1e-3) / 1e9, 3),
+                          "frac_bf16_peak": round(pairs * 2 * D / (ph_ms * 1e-3) / 1e12
+                                                  / PEAK_BF16_TFLOPS, 4)},
+        "target_scores": {"ms_all_layers": round(tgt_ms, 4), "bytes": tgt_bytes,
+                          "gbs": round(tgt_bytes / (tgt_ms * 1e-3) / 1e9, 1),
+                          "frac_hbm": round(tgt_bytes / (tgt_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                          "agg": "mean of logs, count-normalised, eps 1e-6"},
+        "running_cutoff": {"ms_all_layers": round(cut_ms, 4), "rows": rows, "keys_per_row": S,
+                           "mkeys_per_s": round(rows * S / (cut_ms * 1e-3) / 1e6, 1)},
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -90,6 +180,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=2,
                     help="whole KV heads of layer 0 in the oracle sample")
+    ap.add_argument("--no-extras", action="store_true", help="skip the next_rows timings")
+    ap.add_argument("--sha", action="store_true", help="print the mass kernel sources' sha256")
     ap.add_argument("--copy-probe", type=int, default=0)
     ap.add_argument("--copy-reps", type=int, default=5)
     args = ap.parse_args()
@@ -100,6 +192,9 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
+    if args.sha:
+        print(mass_sources_sha256())
+        return 0
     import torch
     if args.copy_probe:
         copy_probe(args.copy_probe, args.copy_reps)
@@ -216,8 +311,11 @@ def main() -> int:
         "select_gbs": round(sel_bytes / (sel_launch_ms * 1e-3) / 1e9, 2),
         "roofline": {"kernel": "mass_kernel", "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic(wl.name)},
     }
+    if not args.no_extras:
+        out["next_rows"] = next_rows(kvp, torch, wl, L, q_all, k_all, lse_all, stream)
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(wl, li0, args.cpu_heads)
