@@ -8,7 +8,11 @@ Every function cites what it follows in the C++ source header:
   * logits / LSE: causal scaled softmax (LKV, §3 Preliminaries, Eq. 1) and the
     per-query log-normaliser reused by KVpop §3.2 (Eq. 8);
   * mass: KVpop §3.1 Eq. 2 un-normalised (App. B.1), summed over the group;
-  * keep-set: KVpop §3 Eq. 1 budget, Eq. 4 eligible set, Fig. 1.
+  * keep-set: KVpop §3 Eq. 1 budget, Eq. 4 eligible set, Fig. 1;
+  * target scores: KVpop §3.1 Eq. 2-3, App. B.1-B.3; running cutoff: KVpop
+    §3.2 (running top-k and its kernel);
+  * block / future scores: ForesightKV §3.2 "Golden Eviction" with the
+    appendix's block-level surrogate.
 """
 from __future__ import annotations
 
@@ -53,6 +57,10 @@ def _bind(lib):
     lib.oracle_keep_count.argtypes = [i64, i64, i64, i64]
     lib.oracle_select.restype = cint
     lib.oracle_select.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp]
+    if hasattr(lib, "oracle_block_scores"):
+        lib.oracle_block_scores.restype = cint
+        lib.oracle_block_scores.argtypes = [vp, vp, cint, i64, i64, i64, i64, i64, dbl, i64, i64,
+                                            i64, cint, cint, vp, vp]
     if hasattr(lib, "oracle_running_cutoff"):
         lib.oracle_running_cutoff.restype = cint
         lib.oracle_running_cutoff.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp, vp]
@@ -136,6 +144,38 @@ def future_mass(q: np.ndarray, k: np.ndarray, window: int, scale: float = 0.0, *
     if mass_heads is not None:
         out["mass_heads"] = mass_heads
     return out
+
+
+def block_count(S: int, block_start: int, block_len: int) -> int:
+    """Number of query blocks [block_start + t L, block_start + (t+1) L) ∩ [0, S)."""
+    return (S - block_start + block_len - 1) // block_len if S > block_start else 0
+
+
+def block_scores(q: np.ndarray, k: np.ndarray, window: int, block_start: int, block_len: int,
+                 scale: float = 0.0, *, per_head: bool = False, f32_exact: bool = False,
+                 nthreads: Optional[int] = None, lib=None) -> dict:
+    """ForesightKV Golden-Eviction scores in fp64 (§3.2 "Golden Eviction" and
+    the appendix's block surrogate): ``block`` [B, U, n_blocks, S], the mean
+    attention of every key over the rows of each query block and the query
+    heads of each unit (KV head, or query head with ``per_head``), and
+    ``future`` [B, U, n_blocks, S], its maximum over the blocks from t on."""
+    lib = lib or load()
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    U = Hq if per_head else Hkv
+    nb = block_count(S, block_start, block_len)
+    block = np.full((B, U, nb, S), np.nan)
+    future = np.full((B, U, nb, S), np.nan)
+    rc = lib.oracle_block_scores(q.ctypes.data, k.ctypes.data, _dtype_code(q, f32_exact), B, Hq,
+                                 Hkv, S, D, float(scale), int(window), int(block_start),
+                                 int(block_len), 1 if per_head else 0,
+                                 nthreads or default_threads(), block.ctypes.data,
+                                 future.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_block_scores rejected the arguments (rc={rc})")
+    return {"block": block, "future": future}
 
 
 def lse_rows(q: np.ndarray, k: np.ndarray, rows: np.ndarray, scale: float = 0.0, *,

@@ -405,4 +405,81 @@ int oracle_running_cutoff(const double* score, int64_t B, int64_t Hkv, int64_t S
   return 0;
 }
 
+/* ForesightKV Golden-Eviction block scores and future scores ("ForesightKV:
+ * Optimizing KV Cache Eviction for Reasoning Models by Learning Long-Term
+ * Contribution", §3.2 "Golden Eviction" and the appendix's block-level
+ * surrogate; the introduction states the future score as the maximum of the
+ * block scores of future steps).
+ *
+ * Query blocks: block t holds the query rows [block_start + t*block_len,
+ * block_start + (t+1)*block_len) clipped to S; rows below block_start belong
+ * to no block.  n_blocks = ceil((S - block_start) / block_len) (0 if
+ * S <= block_start).
+ *   block[b,u,t,j]  = mean over the query heads g of unit u and the rows i of
+ *                     block t of p_g(i->j), counting only i >= j + window;
+ *                     unit u is a KV head (its G query heads; per_head = 0)
+ *                     or a single query head (per_head = 1)
+ *   future[b,u,t,j] = max over t' >= t of block[b,u,t',j]
+ * Either output may be NULL.  Returns 0, or 1 on invalid arguments. */
+int oracle_block_scores(const void* q, const void* k, int dtype, int64_t B, int64_t Hq,
+                        int64_t Hkv, int64_t S, int64_t D, double scale, int64_t window,
+                        int64_t block_start, int64_t block_len, int per_head, int nthreads,
+                        double* block, double* future) {
+  if (!q || !k || B < 0 || Hq < 1 || Hkv < 1 || S < 0 || D < 1 || Hq % Hkv != 0 ||
+      window < 0 || dtype < 0 || dtype > 2 || block_start < 0 || block_len < 1 ||
+      (per_head != 0 && per_head != 1))
+    return 1;
+  if (!(scale > 0.0)) scale = 1.0 / std::sqrt(static_cast<double>(D));
+  const int64_t G = Hq / Hkv;
+  const int64_t n_blocks = S > block_start ? (S - block_start + block_len - 1) / block_len : 0;
+  const int64_t n_units = per_head ? Hq : Hkv;
+  const int64_t heads_per_unit = per_head ? 1 : G;
+
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t h = 0; h < Hkv; ++h) {
+      std::vector<double> kh, kt;
+      widen_head(k, dtype, (b * Hkv + h) * S * D, S, D, kh);
+      transpose_head(kh, S, D, kt);
+      // column sums of every (query head of the group, block): one item each
+      const int64_t n_items = G * n_blocks;
+      std::vector<std::vector<double>> colsum(static_cast<size_t>(n_items));
+      parallel_items(n_items, nthreads, [&](int64_t item) {
+        const int64_t gg = item / n_blocks;
+        const int64_t t = item % n_blocks;
+        const int64_t g = h * G + gg;
+        std::vector<double> qg;
+        widen_head(q, dtype, (b * Hq + g) * S * D, S, D, qg);
+        std::vector<double>& col = colsum[item];
+        col.assign(static_cast<size_t>(S), 0.0);
+        std::vector<double> p(static_cast<size_t>(S));
+        const int64_t i0 = block_start + t * block_len;
+        const int64_t i1 = std::min(S, i0 + block_len);
+        for (int64_t i = i0; i < i1; ++i) {
+          softmax_row(qg.data() + i * D, kt.data(), S, D, i, scale, p);
+          for (int64_t j = 0; j + window <= i; ++j) col[j] += p[j];
+        }
+      });
+      for (int64_t gg0 = 0; gg0 < G; gg0 += heads_per_unit) {
+        const int64_t u = per_head ? h * G + gg0 : h;
+        for (int64_t t = n_blocks - 1; t >= 0; --t) {
+          const int64_t i0 = block_start + t * block_len;
+          const double rows = static_cast<double>(std::min(S, i0 + block_len) - i0);
+          const int64_t o = ((b * n_units + u) * n_blocks + t) * S;
+          for (int64_t j = 0; j < S; ++j) {
+            double acc = 0.0;
+            for (int64_t gg = gg0; gg < gg0 + heads_per_unit; ++gg) acc += colsum[gg * n_blocks + t][j];
+            const double mean = acc / (rows * static_cast<double>(heads_per_unit));
+            if (block) block[o + j] = mean;
+            if (future) {
+              const double later = t + 1 < n_blocks ? future[o + S + j] : -INFINITY;
+              future[o + j] = std::max(mean, later);
+            }
+          }
+        }
+      }
+    }
+  }
+  return 0;
+}
+
 }  // extern "C"
