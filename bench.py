@@ -17,7 +17,8 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
                on the stream it runs on, against the bf16 dense MFMA peak
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
   next_rows    after the timed steps: the per-head mass pass, the KVpop target
-               epilogue and the running top-k cutoff on the same layers
+               epilogue, the running top-k cutoff and the Golden-Eviction
+               block / future scores on the same layers
   roofline.traffic is the HBM bytes per mass-kernel launch from the committed
   counter summary (profiles/), reported only while the kernel sources still
   hash to the value recorded there
@@ -122,8 +123,9 @@ def next_rows(kvp, torch, wl, L, q_all, k_all, lse_all, stream) -> dict:
     """Per-launch times of the entry points beyond the three-stage path, on
     the same resident layers (not part of the timed steps): the per-query-head
     mass pass (every layer), the target epilogue over all layers' per-head
-    masses in one launch, and the running top-k cutoff over all (layer, KV
-    head) rows of those scores in one launch."""
+    masses in one launch, the running top-k cutoff over all (layer, KV head)
+    rows of those scores in one launch, and the Golden-Eviction block and
+    future scores (every layer)."""
     B, Hq, Hkv, S, D = wl.B, wl.Hq, wl.Hkv, wl.S, wl.D
     w, s, k = wl.window, wl.n_sink, wl.top_k
     dev = q_all.device
@@ -151,11 +153,23 @@ def next_rows(kvp, torch, wl, L, q_all, k_all, lse_all, stream) -> dict:
     tgt_ms = timed(lambda: kvp.target_scores(mh_all, Hkv, w, agg=kvp.AGG_MEAN_LOG, eps=1e-6,
                                              out=score), 10)
     tgt_bytes = 4 * L * B * (Hq + Hkv) * S
+    # Golden-Eviction block / future scores with ForesightKV's training budget
+    # and eviction length (first 1024 rows, blocks of 256), window 0
+    b_start, b_len = 1024, 256
+    nb = kvp.block_count(S, b_start, b_len)
+    blk_buf = fut_buf = None
+    blk_ms = 0.0
+    if nb > 0:
+        def blocks_all():
+            for l in range(L):
+                kvp.block_future_scores(q_all[l], k_all[l], lse_all[l], b_start, b_len)
+        blk_ms = timed(blocks_all, 1) / L
+    blk_pairs = B * Hq * (S * (S + 1) // 2 - b_start * (b_start + 1) // 2) if nb > 0 else 0
     rows = L * B * Hkv
     ws = torch.empty(max(1, 20 * rows * (S - min(s, S))), dtype=torch.uint8, device=dev)
     cut_ms = timed(lambda: kvp.running_cutoff(score, w, s, k, workspace=ws), 3)
     log(f"bench: per-head mass {ph_ms:.3f} ms/layer, target {tgt_ms:.4f} ms, "
-        f"running cutoff {cut_ms:.3f} ms ({rows} rows)")
+        f"running cutoff {cut_ms:.3f} ms ({rows} rows), block scores {blk_ms:.3f} ms/layer")
     return {
         "mass_per_head": {"ms_per_layer": round(ph_ms, 4),
                           "gpairs_per_s": round(pairs / (ph_ms * 1e-3) / 1e9, 3),
@@ -167,6 +181,13 @@ def next_rows(kvp, torch, wl, L, q_all, k_all, lse_all, stream) -> dict:
                           "agg": "mean of logs, count-normalised, eps 1e-6"},
         "running_cutoff": {"ms_all_layers": round(cut_ms, 4), "rows": rows, "keys_per_row": S,
                            "mkeys_per_s": round(rows * S / (cut_ms * 1e-3) / 1e6, 1)},
+        "block_future_scores": {"ms_per_layer": round(blk_ms, 4), "block_start": b_start,
+                                "block_len": b_len, "blocks": nb,
+                                "gpairs_per_s": round(blk_pairs / (blk_ms * 1e-3) / 1e9, 3)
+                                if blk_ms > 0 else None,
+                                "frac_bf16_peak": round(blk_pairs * 2 * D / (blk_ms * 1e-3) / 1e12
+                                                        / PEAK_BF16_TFLOPS, 4)
+                                if blk_ms > 0 else None},
     }
 
 

@@ -19,6 +19,10 @@ KVpop's training target from the masses:
 The running top-k mask of every query position:
 
     rank, cutoff = running_cutoff(r, window, n_sink, k)   # int32 [B, Hkv, S] each
+
+ForesightKV's Golden-Eviction scores (query blocks of L rows after the first B):
+
+    blk, fut = block_future_scores(q, k, lse, B, L)     # fp32 [B, Hkv, n_blocks, S] each
 """
 from __future__ import annotations
 
@@ -30,7 +34,7 @@ from typing import Optional
 import torch
 
 __all__ = ["lse_fwd", "future_mass", "future_mass_per_head", "target_scores", "select_topk",
-           "keep_count", "running_cutoff", "KvpError", "library_path", "load_library", "AGG_LOG_MEAN",
+           "keep_count", "running_cutoff", "block_count", "block_future_scores", "KvpError", "library_path", "load_library", "AGG_LOG_MEAN",
            "AGG_MEAN_LOG", "AGG_MAX_LOG"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -79,6 +83,11 @@ def load_library():
             lib.kvp_keep_count.argtypes = [i64, i64, i64, i64]
             lib.kvp_select_topk.restype = ctypes.c_int
             lib.kvp_select_topk.argtypes = [vp, _Dims, i32, i32, i32, vp, vp]
+            lib.kvp_block_count.restype = i64
+            lib.kvp_block_count.argtypes = [i64, i64, i64]
+            lib.kvp_block_future_scores.restype = ctypes.c_int
+            lib.kvp_block_future_scores.argtypes = [vp, vp, vp, ctypes.c_int, _Dims, f32, i32, i32,
+                                                    i32, i32, vp, vp, vp]
             lib.kvp_running_cutoff_workspace_bytes.restype = ctypes.c_size_t
             lib.kvp_running_cutoff_workspace_bytes.argtypes = [_Dims, i32]
             lib.kvp_running_cutoff.restype = ctypes.c_int
@@ -291,3 +300,34 @@ def running_cutoff(score: torch.Tensor, window: int, n_sink: int, top_k: int,
                                   workspace.numel() * workspace.element_size(),
                                   _stream_ptr(stream)), "kvp_running_cutoff")
     return rank, cutoff
+
+
+def block_count(seq_len: int, block_start: int, block_len: int) -> int:
+    return int(load_library().kvp_block_count(seq_len, block_start, block_len))
+
+
+def block_future_scores(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, block_start: int,
+                        block_len: int, window: int = 0, *, per_head: bool = False,
+                        want_block: bool = True, scale: float = 0.0, stream=None):
+    """Golden-Eviction block scores and future scores, fp32 [B, U, n_blocks, S]
+    each (U = Hkv, or Hq with ``per_head``); ``block`` is None when
+    ``want_block`` is false."""
+    lib = load_library()
+    _require_device(q, k, lse)
+    d = _dims(q, k)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (d.batch, d.n_q_heads, d.seq_len):
+        raise KvpError("lse must be fp32 [B, Hq, S]")
+    nb = block_count(d.seq_len, block_start, block_len)
+    if nb < 0:
+        raise KvpError("block_start must be >= 0 and block_len >= 1")
+    U = d.n_q_heads if per_head else d.n_kv_heads
+    shape = (d.batch, U, nb, d.seq_len)
+    fut = torch.empty(shape, dtype=torch.float32, device=q.device)
+    blk = torch.empty(shape, dtype=torch.float32, device=q.device) if want_block else None
+    _check(lib.kvp_block_future_scores(q.data_ptr(), k.data_ptr(), lse.data_ptr(),
+                                       _dtype_code(q), d, float(scale), int(window),
+                                       1 if per_head else 0, int(block_start), int(block_len),
+                                       blk.data_ptr() if blk is not None else None,
+                                       fut.data_ptr(), _stream_ptr(stream)),
+           "kvp_block_future_scores")
+    return blk, fut

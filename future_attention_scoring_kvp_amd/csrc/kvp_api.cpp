@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 3;
+constexpr int32_t kAbiVersion = 4;
 // Limits that keep every index the kernels form in 32-bit ints, and the bytes
 // of one head (S * d * 4 at most) within a 32-bit buffer range.
 constexpr int64_t kMaxSeq = int64_t(1) << 22;
@@ -166,6 +166,34 @@ kvp_status kvp_select_topk(const float* mass, kvp_dims dims, int32_t window, int
   const int w = window > S ? S : window;
   const int s = n_sink > S ? S : n_sink;
   return from_hip(kvp::launch_select(mass, rows, S, w, s, top_k, n_keep, keep, stream));
+}
+
+int64_t kvp_block_count(int64_t seq_len, int64_t block_start, int64_t block_len) {
+  if (seq_len < 0 || block_start < 0 || block_len < 1) return -1;
+  return seq_len > block_start ? (seq_len - block_start + block_len - 1) / block_len : 0;
+}
+
+kvp_status kvp_block_future_scores(const void* q, const void* k, const float* lse,
+                                   kvp_dtype dtype, kvp_dims dims, float scale, int32_t window,
+                                   int32_t per_head, int32_t block_start, int32_t block_len,
+                                   float* block_scores, float* future_scores, hipStream_t stream) {
+  kvp::Shape sh;
+  const kvp_status st = check_dims(dims, true, sh);
+  if (st != KVP_OK) return st;
+  if (!valid_dtype(dtype)) return KVP_ERR_UNSUPPORTED;
+  if (std::isnan(scale) || std::isinf(scale) || window < 0) return KVP_ERR_INVALID;
+  if ((per_head != 0 && per_head != 1) || block_start < 0 || block_len < 1) return KVP_ERR_INVALID;
+  if (block_start % 32 != 0 || block_len % 32 != 0) return KVP_ERR_UNSUPPORTED;
+  const int64_t n_blocks = kvp_block_count(sh.S, block_start, block_len);
+  if (sh.B == 0 || n_blocks == 0) return KVP_OK;
+  if (!q || !k || !lse || !future_scores || !aligned(q, 16) || !aligned(k, 16) ||
+      !aligned(lse, 4) || !aligned(future_scores, 4) || (block_scores && !aligned(block_scores, 4)))
+    return KVP_ERR_INVALID;
+  const int w = window > sh.S ? sh.S : window;
+  const kvp::SegOut seg{block_start, block_len, static_cast<int>(n_blocks), block_scores,
+                        future_scores};
+  return from_hip(kvp::launch_block_scores(q, k, lse, dtype == KVP_BF16 ? 0 : 1, sh,
+                                           resolve_scale(scale, sh.D), w, per_head, seg, stream));
 }
 
 size_t kvp_running_cutoff_workspace_bytes(kvp_dims dims, int32_t n_sink) {

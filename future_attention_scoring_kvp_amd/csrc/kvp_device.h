@@ -65,6 +65,13 @@ __device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, void* ld
 // Eight elements at element offset `elem` of a buffer, as eight bf16 values
 // (16 bytes): bf16 is passed through, fp32 is rounded to nearest even.
 // Out-of-range reads give zeros.
+// One fp32 store through a buffer resource; offsets at or past the range of
+// the resource are dropped by the hardware bounds check.
+__device__ __forceinline__ void buf_store_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_offset,
+                                              float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_offset, 0, 0);
+}
+
 __device__ __forceinline__ u32x4_t buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t elem,
                                              const uint16_t*) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, elem * 2, 0, 0));

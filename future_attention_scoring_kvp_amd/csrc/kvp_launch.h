@@ -18,6 +18,18 @@ hipError_t launch_lse(const void* q, const void* k, int dtype, const Shape& sh, 
 // per_head = 0: mass [B, Hkv, S] summed over each group; 1: mass [B, Hq, S].
 hipError_t launch_mass(const void* q, const void* k, const float* lse, int dtype, const Shape& sh,
                        float scale, int window, int per_head, float* mass, hipStream_t stream);
+// Query-block mode of the mass pass (Golden-Eviction scores): blocks
+// [start + t len, start + (t+1) len) clipped to S, start and len multiples of
+// 32, n blocks; block (may be null) and future are [B, U, n, S] with U = Hkv
+// (group mean) or Hq (per_head).
+struct SegOut {
+  int start, len, n;
+  float* block;
+  float* future;
+};
+hipError_t launch_block_scores(const void* q, const void* k, const float* lse, int dtype,
+                               const Shape& sh, float scale, int window, int per_head,
+                               const SegOut& seg, hipStream_t stream);
 // Target scores [B, Hkv, S] from masses ([B, Hq, S] per head or [B, Hkv, S]
 // group sums); agg: 0 log of the mean, 1 mean of the logs, 2 max of the logs;
 // query < 0: no decay.

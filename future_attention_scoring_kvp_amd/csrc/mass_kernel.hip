@@ -75,6 +75,12 @@ struct MassArgs {
   int per_head;  // 0: one unit per (batch, KV head), masses summed over its G
                  // query heads; 1: one unit per (batch, query head)
   float c;       // scale * log2(e)
+  // query-block mode: blocks [seg_start + t seg_len, ...) clipped to S, both
+  // multiples of 32; per block the mean over its rows and the unit's heads
+  // (seg_block, may be null) and its suffix maximum (seg_future)
+  int seg_start, seg_len, n_seg;
+  float* seg_block;
+  float* seg_future;
 };
 
 struct Tile {
@@ -82,7 +88,26 @@ struct Tile {
   float l2;         // lse2 of this lane's query column
 };
 
-template <int D, typename T, int W>
+// Sum of a 16-value register row over the 32 lanes of a wave half (lanes
+// l and l ^ 16, ^ 8, ... with equal bit 5) by halving exchanges: afterwards
+// lane l holds the total of value v = (l & 31) >> 1 (lanes 2m and 2m+1 hold
+// the same total).  The inputs are consumed.
+__device__ __forceinline__ float reduce_columns(f32x16_t& x, int l32) {
+#pragma unroll
+  for (int half = 8, bit = 4; half >= 1; half >>= 1, --bit) {
+    const bool upper = (l32 >> bit) & 1;
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      const float lo = x[i], hi = x[i + half];
+      const float send = upper ? lo : hi;
+      const float keep = upper ? hi : lo;
+      x[i] = keep + __shfl_xor(send, 1 << bit);
+    }
+  }
+  return x[0] + __shfl_xor(x[0], 1);
+}
+
+template <int D, typename T, int W, bool kSeg>
 __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
   using C = MassCfg<D, W>;
   __shared__ __attribute__((aligned(1024))) unsigned char q_lds0[C::kStageBytes];
@@ -132,12 +157,61 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
 
   f32x16_t acc0 = {}, acc1 = {};
   const float c = a.c;
-  const int q_first = tile_key0 + w;  // first query any key of the tile can see
+  // first query any key of the tile can see (in query-block mode, and that
+  // belongs to a block)
+  const int q_first = kSeg ? max(tile_key0 + w, a.seg_start) : tile_key0 + w;
+
+  // query-block mode: per-key running maxima of the blocks flushed so far
+  // (block scores are >= 0), the lowest block flushed, and the key rows this
+  // lane writes after a column reduction
+  float fmax0 = 0.f, fmax1 = 0.f;
+  int seg_low = a.n_seg;
+  const int red_row = 8 * ((l32 >> 1) >> 2) + 4 * h32 + ((l32 >> 1) & 3);
+  const size_t seg_row0 = (size_t)(b * n_heads_out + ho) * a.n_seg;
+  // stores through buffer resources over one output row: the row base stays
+  // scalar, keys >= S fall outside the resource and are dropped
+  auto write_seg = [&](int t, float v0, float v1) __attribute__((always_inline)) {
+    if (l32 & 1) return;
+    const size_t o = (seg_row0 + t) * S;
+    const uint32_t off0 = (uint32_t)(key0 + red_row) * 4u;
+    const uint32_t row_bytes = (uint32_t)S * 4u;
+    if (a.seg_block) {
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.seg_block + o, row_bytes);
+      buf_store_f32(rb, off0, v0);
+      buf_store_f32(rb, off0 + 128u, v1);
+    }
+    const __amdgpu_buffer_rsrc_t rf = make_rsrc(a.seg_future + o, row_bytes);
+    buf_store_f32(rf, off0, fmax0);
+    buf_store_f32(rf, off0 + 128u, fmax1);
+  };
+  auto flush_seg = [&](int t) __attribute__((always_inline)) {
+    const int i0 = a.seg_start + t * a.seg_len;
+    const int rows = min(S, i0 + a.seg_len) - i0;
+    const float inv = 1.f / (float)(rows * G);
+    const float v0 = reduce_columns(acc0, l32) * inv;
+    const float v1 = reduce_columns(acc1, l32) * inv;
+    acc0 = f32x16_t{};
+    acc1 = f32x16_t{};
+    fmax0 = fmaxf(fmax0, v0);
+    fmax1 = fmaxf(fmax1, v1);
+    write_seg(t, v0, v1);
+    seg_low = t;
+  };
 
   if (q_first < S) {
     const int qb_hi = (S - 1) / kBlk;
     const int qb_lo = q_first / kBlk;
     const int n_pairs = (qb_hi - qb_lo + 1) * G;
+    // query-block mode: after the last pair of a block (its first query
+    // block, last head) or the last pair of the sweep, reduce and write
+    auto maybe_flush = [&](int p) __attribute__((always_inline)) {
+      if constexpr (kSeg) {
+        if (p >= n_pairs) return;
+        const int qrow = (qb_hi - p / G) * kBlk - a.seg_start;
+        if (p == n_pairs - 1 || (p % G == G - 1 && qrow % a.seg_len == 0))
+          flush_seg(qrow / a.seg_len);
+      }
+    };
     const int n_stages = (n_pairs + C::kSlots - 1) / C::kSlots;
     // Pair p is (query block qb_hi - p / G, head p % G).  For this wave,
     // pairs [p_full_lo, p_full) see every key with every query (no mask),
@@ -278,6 +352,7 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
           step(t1, t0, p0 + j, cq, cl, j + 1);
         else
           step(t0, t1, p0 + j, cq, cl, j + 1);
+        maybe_flush(p0 + j);
         if (more && j == kStoreA) {
           store_half(st + 1, 0, nq);
           issue_loads(st + 1, 1);
@@ -289,6 +364,7 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
       }
       __syncthreads();
       step(t1, t0, p0 + C::kSlots - 1, nq, nl, 0);
+      maybe_flush(p0 + C::kSlots - 1);
     };
 
     issue_loads(0, 0);
@@ -303,6 +379,13 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
       if (st + 1 >= n_stages) break;
       stage(std::integral_constant<int, 1>{}, st + 1);
     }
+  }
+
+  if constexpr (kSeg) {
+    // blocks wholly before the first query the tile sees: no attention, and
+    // the future score is the maximum of the later blocks
+    for (int t = seg_low - 1; t >= 0; --t) write_seg(t, 0.f, 0.f);
+    return;
   }
 
   // Column reduction: each lane holds one query column's partial sums for 32
@@ -329,9 +412,10 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
   if (key < S) a.mass[(size_t)(b * n_heads_out + ho) * S + key] = tot;
 }
 
-template <int D, typename T, int W>
+template <int D, typename T, int W, bool kSeg>
 hipError_t launch_mass_w(const void* q, const void* k, const float* lse, const Shape& sh,
-                         float scale, int window, int per_head, float* mass, hipStream_t stream) {
+                         float scale, int window, int per_head, float* mass, const SegOut& seg,
+                         hipStream_t stream) {
   using C = MassCfg<D, W>;
   MassArgs a;
   a.q = q;
@@ -346,37 +430,61 @@ hipError_t launch_mass_w(const void* q, const void* k, const float* lse, const S
   a.window = window;
   a.per_head = per_head;
   a.c = scale * kLog2e;
+  a.seg_start = seg.start;
+  a.seg_len = seg.len;
+  a.n_seg = seg.n;
+  a.seg_block = seg.block;
+  a.seg_future = seg.future;
   const int64_t n_tiles = (sh.S + C::kKeysPerWG - 1) / C::kKeysPerWG;
   const int64_t blocks = n_tiles * (int64_t)sh.B * (per_head ? sh.Hq : sh.Hkv);
-  hipLaunchKernelGGL((mass_kernel<D, T, W>), dim3((unsigned)blocks), dim3(C::kThreads), 0, stream,
-                     a);
+  hipLaunchKernelGGL((mass_kernel<D, T, W, kSeg>), dim3((unsigned)blocks), dim3(C::kThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
 // 512-key workgroups (one per CU) when the grid has at least two per CU;
 // otherwise 256-key workgroups (two per CU), which double the workgroup count
 // of short sequences.
-template <int D, typename T>
+template <int D, typename T, bool kSeg>
 hipError_t launch_mass_t(const void* q, const void* k, const float* lse, const Shape& sh,
-                         float scale, int window, int per_head, float* mass, hipStream_t stream) {
+                         float scale, int window, int per_head, float* mass, const SegOut& seg,
+                         hipStream_t stream) {
   const int64_t units = (int64_t)sh.B * (per_head ? sh.Hq : sh.Hkv);
   const int64_t blocks8 = units * ((sh.S + MassCfg<D, 8>::kKeysPerWG - 1) / MassCfg<D, 8>::kKeysPerWG);
   if (blocks8 >= 2 * kNumCUs)
-    return launch_mass_w<D, T, 8>(q, k, lse, sh, scale, window, per_head, mass, stream);
-  return launch_mass_w<D, T, 4>(q, k, lse, sh, scale, window, per_head, mass, stream);
+    return launch_mass_w<D, T, 8, kSeg>(q, k, lse, sh, scale, window, per_head, mass, seg, stream);
+  return launch_mass_w<D, T, 4, kSeg>(q, k, lse, sh, scale, window, per_head, mass, seg, stream);
 }
 
 }  // namespace
 
 hipError_t launch_mass(const void* q, const void* k, const float* lse, int dtype, const Shape& sh,
                        float scale, int window, int per_head, float* mass, hipStream_t stream) {
+  const SegOut none{0, 32, 0, nullptr, nullptr};
   if (sh.D == 128)
-    return dtype == 0
-               ? launch_mass_t<128, uint16_t>(q, k, lse, sh, scale, window, per_head, mass, stream)
-               : launch_mass_t<128, float>(q, k, lse, sh, scale, window, per_head, mass, stream);
-  return dtype == 0
-             ? launch_mass_t<64, uint16_t>(q, k, lse, sh, scale, window, per_head, mass, stream)
-             : launch_mass_t<64, float>(q, k, lse, sh, scale, window, per_head, mass, stream);
+    return dtype == 0 ? launch_mass_t<128, uint16_t, false>(q, k, lse, sh, scale, window, per_head,
+                                                            mass, none, stream)
+                      : launch_mass_t<128, float, false>(q, k, lse, sh, scale, window, per_head,
+                                                         mass, none, stream);
+  return dtype == 0 ? launch_mass_t<64, uint16_t, false>(q, k, lse, sh, scale, window, per_head,
+                                                         mass, none, stream)
+                    : launch_mass_t<64, float, false>(q, k, lse, sh, scale, window, per_head, mass,
+                                                      none, stream);
+}
+
+hipError_t launch_block_scores(const void* q, const void* k, const float* lse, int dtype,
+                               const Shape& sh, float scale, int window, int per_head,
+                               const SegOut& seg, hipStream_t stream) {
+  if (seg.n == 0) return hipSuccess;
+  if (sh.D == 128)
+    return dtype == 0 ? launch_mass_t<128, uint16_t, true>(q, k, lse, sh, scale, window, per_head,
+                                                           nullptr, seg, stream)
+                      : launch_mass_t<128, float, true>(q, k, lse, sh, scale, window, per_head,
+                                                        nullptr, seg, stream);
+  return dtype == 0 ? launch_mass_t<64, uint16_t, true>(q, k, lse, sh, scale, window, per_head,
+                                                        nullptr, seg, stream)
+                    : launch_mass_t<64, float, true>(q, k, lse, sh, scale, window, per_head,
+                                                     nullptr, seg, stream);
 }
 
 }  // namespace kvp

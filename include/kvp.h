@@ -24,6 +24,13 @@
  *   kvp_running_cutoff        static ranks and the per-query cutoff rank of
  *                             the running top-k (the sparse mask predicate).
  *
+ * A query-block variant of the transposed pass gives ForesightKV's labels:
+ *
+ *   kvp_block_future_scores   Golden-Eviction block scores (attention pooled
+ *                             over the rows of each query block and the heads
+ *                             of a group) and future scores (their maximum
+ *                             over the current and later blocks).
+ *
  * Sources, cited by page title and section/equation:
  *   [KVpop] "KVpop — Key-Value Cache Compression with Predictive Online
  *           Pruning" (arXiv 2607.05061);
@@ -31,7 +38,9 @@
  *           Selection for LLM KV Cache Eviction" (arXiv 2605.06676);
  *   [Tut]   the "transformer math" KV-compression tutorial (aicassindra),
  *           sections "H2O: evict by accumulated attention" and
- *           "StreamingLLM and the attention-sink surprise".
+ *           "StreamingLLM and the attention-sink surprise";
+ *   [FKV]   "ForesightKV: Optimizing KV Cache Eviction for Reasoning Models by
+ *           Learning Long-Term Contribution" (arXiv 2602.03203).
  *
  * Common conventions
  *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
@@ -179,6 +188,39 @@ int64_t kvp_keep_count(int64_t seq_len, int64_t window, int64_t n_sink, int64_t 
  *   dims : only batch, n_kv_heads and seq_len are read. */
 kvp_status kvp_select_topk(const float* mass, kvp_dims dims, int32_t window, int32_t n_sink,
                            int32_t top_k, int32_t* keep, hipStream_t stream);
+
+/* Number of query blocks [block_start + t * block_len, block_start + (t+1) *
+ * block_len) that intersect [0, seq_len): ceil((S - block_start) / block_len),
+ * 0 if S <= block_start.  Pure host function; -1 for invalid arguments. */
+int64_t kvp_block_count(int64_t seq_len, int64_t block_start, int64_t block_len);
+
+/* Golden-Eviction block and future scores ([FKV] §3.2 "Golden Eviction": the
+ * attention matrix pooled over the rows of each query block of length L
+ * after the first B tokens and over the query heads of each group; the
+ * appendix's block-level surrogate takes the mean over a block's queries;
+ * the future score at eviction step t is the largest block score of the
+ * steps from t on, [FKV] §1).  With p_g(i->j) = exp(scale <q_i,k_j> - lse_i):
+ *   block[b,u,t,j]  = (1 / (G_u * |Q_t|)) sum_{g in u} sum_{i in Q_t, i >= j + window} p_g(i->j)
+ *   future[b,u,t,j] = max_{t' >= t} block[b,u,t',j]
+ * where Q_t = [block_start + t L, block_start + (t+1) L) clipped to S (the
+ * last block may be shorter), t < kvp_block_count(S, block_start, L), and the
+ * unit u is a KV head with its G query heads (per_head = 0, the head pool is
+ * the mean) or a single query head (per_head = 1, G_u = 1).  Rows below
+ * block_start belong to no block.  Entries of keys that are not yet in the
+ * cache at step t (j >= block_start + t L) follow the same formula.
+ *   q, k, lse : as kvp_future_mass (lse from kvp_lse_fwd).
+ *   window    : >= 0 (0 in [FKV]; a query counts for a key iff i >= j + window).
+ *   block_start, block_len : >= 0 and >= 1; multiples of 32 (else
+ *               KVP_ERR_UNSUPPORTED).
+ *   block_scores  : device fp32 [B, U, n_blocks, S] or NULL (not written).
+ *   future_scores : device fp32 [B, U, n_blocks, S], written entirely;
+ *                   U = Hkv (per_head = 0) or Hq (per_head = 1).
+ * The same transposed pass as kvp_future_mass with the column sums flushed at
+ * every block boundary: no S x S map, no atomics, bitwise reproducible. */
+kvp_status kvp_block_future_scores(const void* q, const void* k, const float* lse,
+                                   kvp_dtype dtype, kvp_dims dims, float scale, int32_t window,
+                                   int32_t per_head, int32_t block_start, int32_t block_len,
+                                   float* block_scores, float* future_scores, hipStream_t stream);
 
 /* Bytes of device workspace kvp_running_cutoff needs for `dims` (batch,
  * n_kv_heads and seq_len are read) and `n_sink`: 20 * B * Hkv * (S - min(s, S)).

@@ -34,7 +34,8 @@ def test_header_declares_the_three_stages():
     names = declared_functions()
     for n in ("kvp_lse_fwd", "kvp_future_mass", "kvp_select_topk", "kvp_keep_count",
               "kvp_status_string", "kvp_abi_version", "kvp_future_mass_per_head",
-              "kvp_target_scores", "kvp_running_cutoff", "kvp_running_cutoff_workspace_bytes"):
+              "kvp_target_scores", "kvp_running_cutoff", "kvp_running_cutoff_workspace_bytes",
+              "kvp_block_count", "kvp_block_future_scores"):
         assert n in names
 
 
@@ -44,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.kvp_abi_version() == 3
+    assert lib.kvp_abi_version() == 4
     for code in range(5):
         assert lib.kvp_status_string(code)
     assert lib.kvp_status_string(99) == b"unknown status"
@@ -184,3 +185,33 @@ def test_running_cutoff_workspace_and_validation(lib):
     assert cutoff_call(lib, d=dims(S=(1 << 22) + 1)) == UNSUPPORTED
     assert cutoff_call(lib, score=None, rank=None, cut=None, ws=None, d=dims(B=0)) == OK
     assert cutoff_call(lib, score=None, rank=None, cut=None, ws=None, d=dims(S=0)) == OK
+
+
+def block_call(lib, q=FAKE, k=FAKE, lse=FAKE, dtype=0, d=None, w=0, ph=0, start=64, L=64,
+               blk=FAKE, fut=FAKE):
+    return lib.kvp_block_future_scores(q, k, lse, dtype, d or dims(S=512), 0.0, w, ph, start, L,
+                                       blk, fut, None)
+
+
+def test_block_scores_count_and_validation(lib, orc):
+    for S in (0, 1, 31, 32, 100, 1000):
+        for start in (0, 32, 96, 2000):
+            for L in (1, 32, 64, 256):
+                assert lib.kvp_block_count(S, start, L) == orc.block_count(S, start, L)
+    assert lib.kvp_block_count(10, -1, 32) == -1
+    assert lib.kvp_block_count(10, 0, 0) == -1
+    assert block_call(lib, q=None) == INVALID
+    assert block_call(lib, lse=None) == INVALID
+    assert block_call(lib, fut=None) == INVALID
+    assert block_call(lib, blk=FAKE + 2) == INVALID
+    assert block_call(lib, w=-1) == INVALID
+    assert block_call(lib, ph=2) == INVALID
+    assert block_call(lib, start=-32) == INVALID
+    assert block_call(lib, L=0) == INVALID
+    assert block_call(lib, start=48) == UNSUPPORTED     # not a multiple of 32
+    assert block_call(lib, L=100) == UNSUPPORTED
+    assert block_call(lib, d=dims(D=96, S=512)) == UNSUPPORTED
+    assert block_call(lib, d=dims(Hq=6, Hkv=4, S=512)) == INVALID
+    # no block (S <= block_start) or an empty batch: nothing to do
+    assert block_call(lib, q=None, k=None, lse=None, blk=None, fut=None, start=512) == OK
+    assert block_call(lib, q=None, k=None, lse=None, blk=None, fut=None, d=dims(B=0, S=512)) == OK
