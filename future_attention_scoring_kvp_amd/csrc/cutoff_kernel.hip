@@ -10,27 +10,25 @@
 // At query q an eligible token t is retained iff rank[t] <= cutoff[q].
 //
 // The page inserts each newly eligible rank into a Fenwick tree and finds the
-// k-th best by binary lifting.  Here the two passes exploit that the cutoff
-// never rises once k tokens are eligible (adding a token can only push the
-// k-th best to a better rank):
+// k-th best by binary lifting.  Here, two kernels:
 //   rank_kernel    one workgroup per row: stable LSD radix sort of the
-//                  order-preserving keys, one bit per pass (a block-wide
-//                  stable partition with wave ballots), passes whose bit is
-//                  the same for every key are skipped; then rank[pos[r]] = r;
-//   cutoff_kernel  one wave per row sweeps q in order.  While at most k
-//                  tokens are eligible the cutoff is the largest eligible
-//                  rank; afterwards a new token ranked below the cutoff moves
-//                  it down to the next rank whose token is already eligible
-//                  (pos[r] <= q - w).  The cutoff only moves down, so the
-//                  sweep is O(S) per row; ranks and positions are read 64 at
-//                  a time into lanes and consumed with uniform control flow.
+//                  order-preserving keys in 4-bit digits (see below); then
+//                  rank[pos[r]] = r;
+//   cutoff_kernel  one wave per chunk of 1024 queries of a row.  Its first
+//                  state is counted directly from the ranks; then, since the
+//                  cutoff never rises once k tokens are eligible (a new token
+//                  can only push the k-th best to a better rank), a new token
+//                  ranked below the cutoff moves it down to the next rank
+//                  whose token is already eligible (pos[r] <= q - w).  Ranks
+//                  and positions are read 64 at a time into lanes and consumed
+//                  with uniform control flow.
 #include "kvp_device.h"
 #include "kvp_launch.h"
 
 namespace kvp {
 namespace {
 
-constexpr int kRankThreads = 256;
+constexpr int kRankThreads = 1024;
 constexpr int kRankWaves = kRankThreads / kWave;
 
 __device__ __forceinline__ uint32_t order_key(float m) {
@@ -38,27 +36,6 @@ __device__ __forceinline__ uint32_t order_key(float m) {
   if (u == 0x80000000u) u = 0u;  // -0 ties +0
   const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return ~asc;  // ascending key order = descending priority
-}
-
-// Exclusive prefix over the workgroup (thread order) of a 0/1 flag, and the
-// total; wave ballots and one LDS slot per wave.
-__device__ __forceinline__ int rank_block_prefix(bool flag, int* wave_tot, int& total) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const uint64_t bal = __ballot(flag);
-  const int in_wave = __popcll(bal & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-  if (lane == 0) wave_tot[wave] = __popcll(bal);
-  __syncthreads();
-  int before = 0;
-  total = 0;
-#pragma unroll
-  for (int w = 0; w < kRankWaves; ++w) {
-    const int t = wave_tot[w];
-    if (w < wave) before += t;
-    total += t;
-  }
-  __syncthreads();
-  return before + in_wave;
 }
 
 struct CutoffArgs {
@@ -69,11 +46,26 @@ struct CutoffArgs {
   int S, s, window, top_k;
 };
 
+constexpr int kDigitBits = 4;
+constexpr int kDigits = 1 << kDigitBits;
+constexpr int kPasses = 32 / kDigitBits;
+
+// Stable LSD radix sort of one row, 4-bit digits.  One counting pass builds
+// the digit histograms of all eight passes; each pass then scatters the keys
+// chunk by chunk (one element per thread, in order): an element's slot is its digit's
+// running base + the count of equal digits in earlier waves of the chunk +
+// its rank among equal digits in its wave (four ballots give the lanes with
+// the same digit).  Passes whose digit is the same for every key are skipped.
 __global__ __launch_bounds__(kRankThreads) void rank_kernel(CutoffArgs a) {
-  __shared__ int wave_tot[kRankWaves];
-  __shared__ int zero_count;
+  __shared__ int hist[kPasses][kDigits];
+  __shared__ int whist[kRankWaves][kPasses][kDigits];  // per-wave copies: fewer atomic collisions
+  __shared__ int wave_cnt[kRankWaves][kDigits];
+  __shared__ int base[kDigits];
   const int S = a.S, s = a.s, n = S - s;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   const float* __restrict__ m = a.score + (size_t)blockIdx.x * S;
   int32_t* __restrict__ rk = a.rank + (size_t)blockIdx.x * S;
   uint32_t* pos = a.ws + (size_t)blockIdx.x * 5 * n;
@@ -82,41 +74,79 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(CutoffArgs a) {
   uint32_t* kb = ia + n;
   uint32_t* ib = kb + n;
 
+  for (int i = tid; i < kRankWaves * kPasses * kDigits; i += kRankThreads) (&whist[0][0][0])[i] = 0;
   for (int t = tid; t < s; t += kRankThreads) rk[t] = -1;
+  __syncthreads();
   for (int i = tid; i < n; i += kRankThreads) {
-    ka[i] = order_key(m[s + i]);
+    const uint32_t key = order_key(m[s + i]);
+    ka[i] = key;
     ia[i] = (uint32_t)(s + i);
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p)
+      atomicAdd(&whist[wave][p][(key >> (kDigitBits * p)) & (kDigits - 1)], 1);
+  }
+  __syncthreads();
+  if (tid < kPasses * kDigits) {
+    int tot = 0;
+    for (int w2 = 0; w2 < kRankWaves; ++w2) tot += (&whist[w2][0][0])[tid];
+    (&hist[0][0])[tid] = tot;
   }
   __syncthreads();
 
-  for (int bit = 0; bit < 32; ++bit) {
-    // zeros of this bit
-    if (tid == 0) zero_count = 0;
-    __syncthreads();
-    int local = 0;
-    for (int i = tid; i < n; i += kRankThreads) local += ((ka[i] >> bit) & 1u) ? 0 : 1;
-    atomicAdd(&zero_count, local);
-    __syncthreads();
-    const int zeros = zero_count;
-    __syncthreads();
-    if (zeros == 0 || zeros == n) continue;  // every key has the same bit: order unchanged
-    // stable partition: zeros first, then ones, each in their current order
-    int zeros_before = 0;
-    for (int base = 0; base < n; base += kRankThreads) {
-      const int i = base + tid;
+  for (int i = tid; i < kRankWaves * kDigits; i += kRankThreads) (&wave_cnt[0][0])[i] = 0;
+  for (int p = 0; p < kPasses; ++p) {
+    const int shift = kDigitBits * p;
+    bool trivial = false;
+#pragma unroll
+    for (int d = 0; d < kDigits; ++d) trivial |= hist[p][d] == n;
+    if (trivial || n == 0) continue;  // uniform: the order does not change
+    if (tid < kDigits) {
+      int acc = 0;
+      for (int d = 0; d < tid; ++d) acc += hist[p][d];
+      base[tid] = acc;
+    }
+    // the next chunk's key and index are loaded while this one is scattered
+    uint32_t nkey = tid < n ? ka[tid] : 0u;
+    uint32_t nidx = tid < n ? ia[tid] : 0u;
+    for (int c = 0; c < n; c += kRankThreads) {
+      const int i = c + tid;
       const bool valid = i < n;
-      const uint32_t key = valid ? ka[i] : 0u;
-      const uint32_t idx = valid ? ia[i] : 0u;
-      const bool zero = valid && !((key >> bit) & 1u);
-      int chunk_zeros = 0;
-      const int zpre = rank_block_prefix(zero, wave_tot, chunk_zeros);
-      if (valid) {
-        const int dst = zero ? zeros_before + zpre
-                             : zeros + (base - zeros_before) + (tid - zpre);
-        kb[dst] = key;
-        ib[dst] = idx;
+      const uint32_t key = nkey;
+      const uint32_t idx = nidx;
+      if (i + kRankThreads < n) {
+        nkey = ka[i + kRankThreads];
+        nidx = ia[i + kRankThreads];
       }
-      zeros_before += chunk_zeros;
+      const int d = (int)((key >> shift) & (kDigits - 1));
+      uint64_t same = __ballot(valid);
+#pragma unroll
+      for (int bbit = 0; bbit < kDigitBits; ++bbit) {
+        const uint64_t bal = __ballot(valid && ((d >> bbit) & 1));
+        same &= ((d >> bbit) & 1) ? bal : ~bal;
+      }
+      const int in_rank = __popcll(same & lt_mask);
+      // bases of this chunk final and the counts cleared (by wave 0, below)
+      __syncthreads();
+      if (valid && in_rank == 0) wave_cnt[wave][d] = __popcll(same);
+      __syncthreads();
+      if (valid) {
+        int before = base[d];
+        for (int w2 = 0; w2 < wave; ++w2) before += wave_cnt[w2][d];
+        kb[before + in_rank] = key;
+        ib[before + in_rank] = idx;
+      }
+      __syncthreads();
+      // wave 0 alone advances the bases and then clears the counts: both in
+      // its own program order, before the next chunk's first barrier
+      if (wave == 0) {
+        if (lane < kDigits) {
+          int tot = 0;
+#pragma unroll
+          for (int w2 = 0; w2 < kRankWaves; ++w2) tot += wave_cnt[w2][lane];
+          base[lane] += tot;
+        }
+        for (int e = lane; e < kRankWaves * kDigits; e += kWave) (&wave_cnt[0][0])[e] = 0;
+      }
     }
     __syncthreads();
     uint32_t* tk = ka; ka = kb; kb = tk;
@@ -129,26 +159,82 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(CutoffArgs a) {
   }
 }
 
-// One wave per row (4 rows per 256-thread block).
-__global__ __launch_bounds__(256) void cutoff_kernel(CutoffArgs a, int rows) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+constexpr int kChunk = 1024;  // queries swept by one wave
+
+// One wave per (row, chunk of kChunk queries).  The state before the chunk's
+// first query q0 is found directly: with c = |E(q0 - 1)| eligible tokens,
+// the cutoff is the largest eligible rank while c <= k (needed once c reaches
+// k), else the rank of the k-th best eligible token: the k-th rank r in
+// order whose token pos[r] <= q0 - 1 - w, counted 64 ranks at a time with
+// ballots.  The chunk then runs the sequential update: a new token ranked
+// below the cutoff moves it down to the next rank whose token is eligible.
+__global__ __launch_bounds__(256) void cutoff_kernel(CutoffArgs a, int rows, int n_chunks) {
+  // wave-uniform state lives in scalar registers (readfirstlane tells the
+  // compiler so), and the sweep's branches are scalar
+  const int gw = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int row = gw / n_chunks;
   if (row >= rows) return;
+  const int chunk = gw - row * n_chunks;
   const int lane = threadIdx.x & 63;
   const int S = a.S, s = a.s, w = a.window, k = a.top_k, n = S - s;
   const int32_t* __restrict__ rk = a.rank + (size_t)row * S;
   const uint32_t* __restrict__ pos = a.ws + (size_t)row * 5 * n;
   int32_t* __restrict__ out = a.cutoff + (size_t)row * S;
+  const int q_begin = chunk * kChunk;
+  const int q_end = min(S, q_begin + kChunk);
+  if (k == 0) {
+    for (int q = q_begin + lane; q < q_end; q += 64) out[q] = -1;
+    return;
+  }
 
-  int eligible = 0;  // uniform state
+  // state after the queries before q_begin
+  int eligible = max(0, min(n, q_begin - w - s));  // tokens s .. q_begin - 1 - w
   int tau = -1;
+  if (eligible > 0 && eligible <= k) {
+    int mx = -1;
+    for (int t = s + lane; t < s + eligible; t += 64) mx = max(mx, rk[t]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off));
+    tau = __builtin_amdgcn_readfirstlane(mx);
+  } else if (eligible > k) {
+    const int last = q_begin - 1 - w;  // eligible tokens are s .. last
+    int seen = 0;
+    tau = n - 1;  // not reached: more than k ranks qualify
+    constexpr int kAhead = 8;  // 64-rank groups whose positions are loaded together
+    bool found = false;
+    for (int r0 = 0; r0 < n && !found; r0 += 64 * kAhead) {
+      uint32_t pv[kAhead];
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u) {
+        const int r = r0 + 64 * u + lane;
+        pv[u] = r < n ? pos[r] : 0xFFFFFFFFu;
+      }
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u) {
+        if (found) break;
+        const bool ok = (int)pv[u] <= last && pv[u] != 0xFFFFFFFFu;
+        const uint64_t bal = __ballot(ok);
+        const int cnt = __popcll(bal);
+        if (seen + cnt >= k) {
+          const int need = k - seen;  // 1-based position among this group's hits
+          const int upto = __popcll(bal & (~0ull >> (63 - lane)));
+          const uint64_t hit = __ballot(ok && upto == need);
+          tau = __builtin_amdgcn_readfirstlane(r0 + 64 * u + (int)__builtin_ctzll(hit));
+          found = true;
+        }
+        seen += cnt;
+      }
+    }
+  }
+
   int pchunk = 1 << 30;  // start of the positions held in lanes (none yet)
   uint32_t plane = 0;
-  for (int q0 = 0; q0 < S; q0 += 64) {
+  for (int q0 = q_begin; q0 < q_end; q0 += 64) {
     // ranks of the tokens that enter at q0 .. q0 + 63 (t = q - w), -2 if none
     const int t_l = q0 + lane - w;
-    const int r_l = (t_l >= s && t_l < S && q0 + lane < S) ? rk[t_l] : -2;
+    const int r_l = (t_l >= s && t_l < S && q0 + lane < q_end) ? rk[t_l] : -2;
     int my_out = 0;
-    const int nq = min(64, S - q0);
+    const int nq = min(64, q_end - q0);
     for (int j = 0; j < nq; ++j) {
       const int q = q0 + j;
       const int r_new = __builtin_amdgcn_readlane(r_l, j);
@@ -172,8 +258,8 @@ __global__ __launch_bounds__(256) void cutoff_kernel(CutoffArgs a, int rows) {
           }
         }
       }
-      const int c = (k == 0) ? -1 : (eligible < k ? S : tau);
-      if (lane == j) my_out = c;
+      const int c = eligible < k ? S : tau;
+      my_out = lane == j ? c : my_out;
     }
     if (lane < nq) out[q0 + lane] = my_out;
   }
@@ -201,8 +287,10 @@ hipError_t launch_cutoff(const float* score, int64_t rows, int S, int window, in
   hipLaunchKernelGGL(rank_kernel, dim3((unsigned)rows), dim3(kRankThreads), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(cutoff_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a,
-                     (int)rows);
+  const int n_chunks = (S + kChunk - 1) / kChunk;
+  const int64_t waves = rows * n_chunks;
+  hipLaunchKernelGGL(cutoff_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a,
+                     (int)rows, n_chunks);
   return hipGetLastError();
 }
 

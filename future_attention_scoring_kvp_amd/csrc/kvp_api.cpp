@@ -216,6 +216,8 @@ kvp_status kvp_running_cutoff(const float* score, kvp_dims dims, int32_t window,
       !aligned(cutoff, 4))
     return KVP_ERR_INVALID;
   const int S = dims.seq_len;
+  // one wave per (row, 1024 queries), four waves per workgroup
+  if (rows * ((S + 1023) / 1024) > 4 * kMaxBlocks) return KVP_ERR_UNSUPPORTED;
   const int w = window > S ? S : window;
   const int s = n_sink > S ? S : n_sink;
   const size_t need = kvp::cutoff_workspace_bytes(rows, S, s);
