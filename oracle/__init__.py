@@ -17,6 +17,7 @@ Every function cites what it follows in the C++ source header:
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 import threading
@@ -283,3 +284,73 @@ def _target_scores(mass, window, n_kv_heads, per_head, group_size, normalize, ag
         r = r + steps * lg
         r = np.where(t <= query, r, -np.inf)
     return r
+
+
+def _laplace_cdf(z):
+    return np.where(z >= 0, 1.0 - 0.5 * np.exp(-np.abs(z)), 0.5 * np.exp(-np.abs(z)))
+
+
+def soft_topk(x: np.ndarray, k, tau: float = 1.0):
+    """LKV's Soft-TopK (§3.2 "The Differentiable Soft-TopK Operator", App. A.1)
+    in fp64, row by row over the last axis: y_i = f(z_i - lam) with z = x / tau,
+    f the Laplace CDF, and the threshold lam for which sum_i y_i = k.
+
+    Following App. A.1: sort z descending; for a split m (the m largest
+    elements in the saturation region) the budget equation is the quadratic
+    S1 y^2 + 2 (k - m) y - S2 = 0 in y = e^lam, with S1 = sum_{i<=m} e^{-z_(i)}
+    and S2 = sum_{i>m} e^{z_(i)}; the split is the one whose root lies between
+    z_(m+1) and z_(m) (the first such m).  S1 and S2 are kept as logarithms
+    (cumulative log-sum-exp), and their product, at most m (n - m), is formed
+    from the sum of the logarithms.  The page keeps 1 <= m < n; m = 0 (lam
+    above every element) and m = n (below every element) use the same
+    equation's limits, y = S2 / (2k) and y = 2 (n - k) / S1.
+    Returns (y, lam) with lam in units of z.  k: scalar or one per row, in
+    (0, n)."""
+    x = np.asarray(x, dtype=np.float64)
+    rows = x.reshape(-1, x.shape[-1])
+    n = rows.shape[1]
+    kk = np.broadcast_to(np.asarray(k, dtype=np.float64), (rows.shape[0],))
+    y = np.empty_like(rows)
+    lam = np.empty(rows.shape[0])
+    for r in range(rows.shape[0]):
+        z = rows[r] / tau
+        zs = np.sort(z)[::-1]
+        m = np.arange(n + 1)
+        # log S1(m) for m = 0..n (log 0 = -inf) and log S2(m)
+        log_s1 = np.concatenate([[-np.inf], np.logaddexp.accumulate(-zs)])
+        log_s2 = np.concatenate([np.logaddexp.accumulate(zs[::-1])[::-1], [-np.inf]])
+        a = kk[r] - m
+        with np.errstate(divide="ignore", invalid="ignore", over="ignore", under="ignore"):
+            log_p = log_s1 + log_s2                          # log S1 S2; S1 S2 <= m (n - m)
+            root = np.sqrt(a * a + np.exp(log_p))
+            # log(y S1) with y S1 = sqrt(a^2 + S1 S2) - a, taken without
+            # cancellation for a > 0 and without forming a vanishing product
+            log_ys1 = np.where(a > 0, log_p - np.log(root + a),
+                               np.where(a == 0, 0.5 * log_p, np.log(root - a)))
+            cand = log_ys1 - log_s1
+            cand[0] = log_s2[0] - math.log(2.0 * kk[r])       # m = 0
+            cand[n] = math.log(2.0 * (n - kk[r])) - log_s1[n]  # m = n
+        hi = np.concatenate([[np.inf], zs])                  # z_(m), m = 0..n
+        lo = np.concatenate([zs, [-np.inf]])                 # z_(m+1)
+        ok = np.isfinite(cand) & (lo <= cand) & (cand <= hi)
+        if not ok.any():
+            raise ValueError("no consistent split (k outside (0, n)?)")
+        lam[r] = cand[np.argmax(ok)]
+        y[r] = _laplace_cdf(z - lam[r])
+    return y.reshape(x.shape), lam.reshape(x.shape[:-1])
+
+
+def soft_topk_backward(x: np.ndarray, lam: np.ndarray, dy: np.ndarray, tau: float = 1.0):
+    """Gradients of the Soft-TopK (LKV App. A.2, implicit function theorem):
+    with f'(z) = e^{-|z|} / 2 and u_i = z_i - lam,
+      d lam / d z_j = f'(u_j) / sum_i f'(u_i),   d lam / d k = -1 / sum_i f'(u_i),
+    so for upstream dy:  dz_j = f'(u_j) (dy_j - sum_i dy_i f'(u_i) / sum_i f'(u_i)),
+    dx = dz / tau and dk = sum_i dy_i f'(u_i) / sum_i f'(u_i)."""
+    x = np.asarray(x, dtype=np.float64)
+    lam = np.asarray(lam, dtype=np.float64)[..., None]
+    dy = np.asarray(dy, dtype=np.float64)
+    fp = 0.5 * np.exp(-np.abs(x / tau - lam))
+    a = (dy * fp).sum(-1, keepdims=True)
+    b = fp.sum(-1, keepdims=True)
+    dz = fp * (dy - a / b)
+    return dz / tau, (a / b)[..., 0]
