@@ -124,8 +124,9 @@ def next_rows(kvp, torch, wl, L, q_all, k_all, lse_all, stream) -> dict:
     the same resident layers (not part of the timed steps): the per-query-head
     mass pass (every layer), the target epilogue over all layers' per-head
     masses in one launch, the running top-k cutoff over all (layer, KV head)
-    rows of those scores in one launch, and the Golden-Eviction block and
-    future scores (every layer)."""
+    rows of those scores in one launch, LKV's Soft-TopK forward and backward
+    over those rows, and the Golden-Eviction block and future scores (every
+    layer)."""
     B, Hq, Hkv, S, D = wl.B, wl.Hq, wl.Hkv, wl.S, wl.D
     w, s, k = wl.window, wl.n_sink, wl.top_k
     dev = q_all.device
@@ -168,8 +169,20 @@ def next_rows(kvp, torch, wl, L, q_all, k_all, lse_all, stream) -> dict:
     rows = L * B * Hkv
     ws = torch.empty(max(1, 20 * rows * (S - min(s, S))), dtype=torch.uint8, device=dev)
     cut_ms = timed(lambda: kvp.running_cutoff(score, w, s, k, workspace=ws), 3)
+    # LKV Soft-TopK over the same rows with the same budget, forward and backward
+    st_k = torch.full((rows,), float(k), dtype=torch.float32, device=dev)
+    st_in = score.view(rows, S)
+    st_out = {}
+
+    def st_fwd():
+        st_out["y"], st_out["lam"] = kvp.soft_topk(st_in, st_k, 1.0)
+
+    st_fwd_ms = timed(st_fwd, 3)
+    st_dy = torch.ones_like(st_in)
+    st_bwd_ms = timed(lambda: kvp.soft_topk_backward(st_in, st_out["lam"], st_dy, 1.0), 3)
     log(f"bench: per-head mass {ph_ms:.3f} ms/layer, target {tgt_ms:.4f} ms, "
-        f"running cutoff {cut_ms:.3f} ms ({rows} rows), block scores {blk_ms:.3f} ms/layer")
+        f"running cutoff {cut_ms:.3f} ms ({rows} rows), soft top-k {st_fwd_ms:.3f} + "
+        f"{st_bwd_ms:.3f} ms, block scores {blk_ms:.3f} ms/layer")
     return {
         "mass_per_head": {"ms_per_layer": round(ph_ms, 4),
                           "gpairs_per_s": round(pairs / (ph_ms * 1e-3) / 1e9, 3),
@@ -181,6 +194,8 @@ def next_rows(kvp, torch, wl, L, q_all, k_all, lse_all, stream) -> dict:
                           "agg": "mean of logs, count-normalised, eps 1e-6"},
         "running_cutoff": {"ms_all_layers": round(cut_ms, 4), "rows": rows, "keys_per_row": S,
                            "mkeys_per_s": round(rows * S / (cut_ms * 1e-3) / 1e6, 1)},
+        "soft_topk": {"fwd_ms_all_rows": round(st_fwd_ms, 4), "bwd_ms_all_rows": round(st_bwd_ms, 4),
+                      "rows": rows, "n": S, "k": k},
         "block_future_scores": {"ms_per_layer": round(blk_ms, 4), "block_start": b_start,
                                 "block_len": b_len, "blocks": nb,
                                 "gpairs_per_s": round(blk_pairs / (blk_ms * 1e-3) / 1e9, 3)

@@ -23,6 +23,11 @@ The running top-k mask of every query position:
 ForesightKV's Golden-Eviction scores (query blocks of L rows after the first B):
 
     blk, fut = block_future_scores(q, k, lse, B, L)     # fp32 [B, Hkv, n_blocks, S] each
+
+LKV's differentiable Soft-TopK over any score rows:
+
+    y, lam = soft_topk(x, k, tau)                       # y sums to k per row
+    dx, dk = soft_topk_backward(x, lam, dy, tau)
 """
 from __future__ import annotations
 
@@ -34,7 +39,8 @@ from typing import Optional
 import torch
 
 __all__ = ["lse_fwd", "future_mass", "future_mass_per_head", "target_scores", "select_topk",
-           "keep_count", "running_cutoff", "block_count", "block_future_scores", "KvpError", "library_path", "load_library", "AGG_LOG_MEAN",
+           "keep_count", "running_cutoff", "block_count", "block_future_scores", "soft_topk", "soft_topk_backward",
+           "KvpError", "library_path", "load_library", "AGG_LOG_MEAN",
            "AGG_MEAN_LOG", "AGG_MAX_LOG"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -88,6 +94,10 @@ def load_library():
             lib.kvp_block_future_scores.restype = ctypes.c_int
             lib.kvp_block_future_scores.argtypes = [vp, vp, vp, ctypes.c_int, _Dims, f32, i32, i32,
                                                     i32, i32, vp, vp, vp]
+            lib.kvp_soft_topk_fwd.restype = ctypes.c_int
+            lib.kvp_soft_topk_fwd.argtypes = [vp, i64, i32, vp, f32, vp, vp, vp]
+            lib.kvp_soft_topk_bwd.restype = ctypes.c_int
+            lib.kvp_soft_topk_bwd.argtypes = [vp, vp, vp, i64, i32, f32, vp, vp, vp]
             lib.kvp_running_cutoff_workspace_bytes.restype = ctypes.c_size_t
             lib.kvp_running_cutoff_workspace_bytes.argtypes = [_Dims, i32]
             lib.kvp_running_cutoff.restype = ctypes.c_int
@@ -331,3 +341,47 @@ def block_future_scores(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, blo
                                        fut.data_ptr(), _stream_ptr(stream)),
            "kvp_block_future_scores")
     return blk, fut
+
+
+def _rows_of(t: torch.Tensor):
+    n = t.shape[-1]
+    return (t.numel() // n if n else 0), n
+
+
+def soft_topk(x: torch.Tensor, k, tau: float = 1.0, stream=None):
+    """LKV Soft-TopK per row of ``x`` (fp32 [..., n]): returns (y, lam), y of
+    the shape of x summing to k per row, lam fp32 [...] in units of x / tau.
+    ``k`` is a float or an fp32 GPU tensor with one budget per row."""
+    lib = load_library()
+    _require_device(x)
+    if x.dtype != torch.float32 or x.dim() < 1:
+        raise KvpError("x must be fp32 [..., n]")
+    rows, n = _rows_of(x)
+    if not torch.is_tensor(k):
+        k = torch.full(x.shape[:-1], float(k), dtype=torch.float32, device=x.device)
+    _require_device(k)
+    if k.dtype != torch.float32 or k.numel() != rows:
+        raise KvpError("k must be fp32 with one budget per row")
+    y = torch.empty_like(x)
+    lam = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _check(lib.kvp_soft_topk_fwd(x.data_ptr(), rows, n, k.data_ptr(), float(tau), y.data_ptr(),
+                                 lam.data_ptr(), _stream_ptr(stream)), "kvp_soft_topk_fwd")
+    return y, lam
+
+
+def soft_topk_backward(x: torch.Tensor, lam: torch.Tensor, dy: torch.Tensor, tau: float = 1.0,
+                       stream=None):
+    """Gradients of the Soft-TopK: (dx like x, dk fp32 [...])."""
+    lib = load_library()
+    _require_device(x, lam, dy)
+    if x.dtype != torch.float32 or dy.dtype != torch.float32 or lam.dtype != torch.float32:
+        raise KvpError("x, lam and dy must be fp32")
+    rows, n = _rows_of(x)
+    if dy.shape != x.shape or lam.numel() != rows:
+        raise KvpError("dy must match x and lam must hold one value per row")
+    dx = torch.empty_like(x)
+    dk = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _check(lib.kvp_soft_topk_bwd(x.data_ptr(), lam.data_ptr(), dy.data_ptr(), rows, n, float(tau),
+                                 dx.data_ptr(), dk.data_ptr(), _stream_ptr(stream)),
+           "kvp_soft_topk_bwd")
+    return dx, dk

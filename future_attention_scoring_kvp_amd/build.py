@@ -14,7 +14,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libkvp.so")
 
 SOURCES = ["kvp_api.cpp", "lse_kernel.hip", "mass_kernel.hip", "select_kernel.hip",
-           "target_kernel.hip", "cutoff_kernel.hip"]
+           "target_kernel.hip", "cutoff_kernel.hip",
+           "softtopk_kernel.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled for every device compilation.

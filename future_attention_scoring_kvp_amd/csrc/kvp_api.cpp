@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 4;
+constexpr int32_t kAbiVersion = 5;
 // Limits that keep every index the kernels form in 32-bit ints, and the bytes
 // of one head (S * d * 4 at most) within a 32-bit buffer range.
 constexpr int64_t kMaxSeq = int64_t(1) << 22;
@@ -194,6 +194,28 @@ kvp_status kvp_block_future_scores(const void* q, const void* k, const float* ls
                         future_scores};
   return from_hip(kvp::launch_block_scores(q, k, lse, dtype == KVP_BF16 ? 0 : 1, sh,
                                            resolve_scale(scale, sh.D), w, per_head, seg, stream));
+}
+
+kvp_status kvp_soft_topk_fwd(const float* x, int64_t rows, int32_t n, const float* k, float tau,
+                             float* y, float* lam, hipStream_t stream) {
+  if (rows < 0 || n < 0 || !(tau > 0.f) || std::isinf(tau)) return KVP_ERR_INVALID;
+  if (rows > kMaxBlocks || n > (1 << 30)) return KVP_ERR_UNSUPPORTED;
+  if (rows == 0 || n == 0) return KVP_OK;
+  if (!x || !k || !y || !aligned(x, 4) || !aligned(k, 4) || !aligned(y, 4) ||
+      (lam && !aligned(lam, 4)))
+    return KVP_ERR_INVALID;
+  return from_hip(kvp::launch_soft_topk_fwd(x, k, rows, n, tau, y, lam, stream));
+}
+
+kvp_status kvp_soft_topk_bwd(const float* x, const float* lam, const float* dy, int64_t rows,
+                             int32_t n, float tau, float* dx, float* dk, hipStream_t stream) {
+  if (rows < 0 || n < 0 || !(tau > 0.f) || std::isinf(tau)) return KVP_ERR_INVALID;
+  if (rows > kMaxBlocks || n > (1 << 30)) return KVP_ERR_UNSUPPORTED;
+  if (rows == 0 || n == 0) return KVP_OK;
+  if (!x || !lam || !dy || !dx || !aligned(x, 4) || !aligned(lam, 4) || !aligned(dy, 4) ||
+      !aligned(dx, 4) || (dk && !aligned(dk, 4)))
+    return KVP_ERR_INVALID;
+  return from_hip(kvp::launch_soft_topk_bwd(x, lam, dy, rows, n, tau, dx, dk, stream));
 }
 
 size_t kvp_running_cutoff_workspace_bytes(kvp_dims dims, int32_t n_sink) {

@@ -46,4 +46,10 @@ hipError_t launch_cutoff(const float* score, int64_t rows, int S, int window, in
                          int top_k, int32_t* rank, int32_t* cutoff, void* workspace,
                          hipStream_t stream);
 
+// LKV Soft-TopK per row of n scores: forward (y, lam) and backward (dx, dk).
+hipError_t launch_soft_topk_fwd(const float* x, const float* k, int64_t rows, int n, float tau,
+                                float* y, float* lam, hipStream_t stream);
+hipError_t launch_soft_topk_bwd(const float* x, const float* lam, const float* dy, int64_t rows,
+                                int n, float tau, float* dx, float* dk, hipStream_t stream);
+
 }  // namespace kvp

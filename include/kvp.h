@@ -31,6 +31,11 @@
  *                             of a group) and future scores (their maximum
  *                             over the current and later blocks).
  *
+ * And a differentiable stand-in for the top-k selection:
+ *
+ *   kvp_soft_topk_fwd / _bwd  LKV's Soft-TopK soft mask (closed-form
+ *                             threshold) and its gradients.
+ *
  * Sources, cited by page title and section/equation:
  *   [KVpop] "KVpop — Key-Value Cache Compression with Predictive Online
  *           Pruning" (arXiv 2607.05061);
@@ -221,6 +226,32 @@ kvp_status kvp_block_future_scores(const void* q, const void* k, const float* ls
                                    kvp_dtype dtype, kvp_dims dims, float scale, int32_t window,
                                    int32_t per_head, int32_t block_start, int32_t block_len,
                                    float* block_scores, float* future_scores, hipStream_t stream);
+
+/* LKV Soft-TopK forward ([LKV] §3.2 "The Differentiable Soft-TopK Operator",
+ * App. A.1).  Per row r of n scores x, with z = x / tau:
+ *   y[r,i] = f(z_i - lam[r]),  f(u) = 1 - e^{-u}/2 for u >= 0, e^{u}/2 for u < 0
+ * (the Laplace CDF), lam[r] the threshold with sum_i y[r,i] = k[r]: the root
+ * of S1 e^{2 lam} + 2 (k - m) e^{lam} - S2 = 0 for the split m of elements
+ * above it (S1 = sum over them of e^{-z_i}, S2 = sum over the rest of e^{z_i}).
+ * Outputs lie in (0, 1), sum to k, keep the order of x and do not change
+ * when a constant is added to x; tau -> 0 tends to the hard top-k.  Gumbel
+ * noise ([LKV] §3.4), if wanted, is added to x by the caller.
+ *   x   : device fp32 [rows, n];  k : device fp32 [rows], budgets in (0, n)
+ *         (k <= 0 gives y = 0, lam = +inf; k >= n gives y = 1, lam = -inf).
+ *   tau : temperature > 0.
+ *   y   : device fp32 [rows, n];  lam : device fp32 [rows] (units of z) or NULL.
+ * Computed in fp64 per row (no sort: the split is found by bisection on the
+ * scores' bit patterns, at most 32 reductions); x must be finite. */
+kvp_status kvp_soft_topk_fwd(const float* x, int64_t rows, int32_t n, const float* k, float tau,
+                             float* y, float* lam, hipStream_t stream);
+
+/* Soft-TopK backward ([LKV] App. A.2): with f'(u) = e^{-|u|}/2, u_i = z_i - lam,
+ * A = sum_i dy_i f'(u_i), B = sum_i f'(u_i):
+ *   dx[r,j] = f'(u_j) (dy[r,j] - A / B) / tau,   dk[r] = A / B.
+ *   x, lam : as passed to / returned by kvp_soft_topk_fwd;  dy : device fp32
+ *   [rows, n];  dx : device fp32 [rows, n];  dk : device fp32 [rows] or NULL. */
+kvp_status kvp_soft_topk_bwd(const float* x, const float* lam, const float* dy, int64_t rows,
+                             int32_t n, float tau, float* dx, float* dk, hipStream_t stream);
 
 /* Bytes of device workspace kvp_running_cutoff needs for `dims` (batch,
  * n_kv_heads and seq_len are read) and `n_sink`: 20 * B * Hkv * (S - min(s, S)).

@@ -35,7 +35,8 @@ def test_header_declares_the_three_stages():
     for n in ("kvp_lse_fwd", "kvp_future_mass", "kvp_select_topk", "kvp_keep_count",
               "kvp_status_string", "kvp_abi_version", "kvp_future_mass_per_head",
               "kvp_target_scores", "kvp_running_cutoff", "kvp_running_cutoff_workspace_bytes",
-              "kvp_block_count", "kvp_block_future_scores"):
+              "kvp_block_count", "kvp_block_future_scores", "kvp_soft_topk_fwd",
+              "kvp_soft_topk_bwd"):
         assert n in names
 
 
@@ -45,7 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.kvp_abi_version() == 4
+    assert lib.kvp_abi_version() == 5
     for code in range(5):
         assert lib.kvp_status_string(code)
     assert lib.kvp_status_string(99) == b"unknown status"
@@ -215,3 +216,21 @@ def test_block_scores_count_and_validation(lib, orc):
     # no block (S <= block_start) or an empty batch: nothing to do
     assert block_call(lib, q=None, k=None, lse=None, blk=None, fut=None, start=512) == OK
     assert block_call(lib, q=None, k=None, lse=None, blk=None, fut=None, d=dims(B=0, S=512)) == OK
+
+
+def test_soft_topk_validation(lib):
+    fwd, bwd = lib.kvp_soft_topk_fwd, lib.kvp_soft_topk_bwd
+    assert fwd(None, 2, 16, FAKE, 1.0, FAKE, FAKE, None) == INVALID
+    assert fwd(FAKE, 2, 16, None, 1.0, FAKE, FAKE, None) == INVALID
+    assert fwd(FAKE, 2, 16, FAKE, 1.0, None, FAKE, None) == INVALID
+    assert fwd(FAKE, 2, 16, FAKE, 0.0, FAKE, FAKE, None) == INVALID      # tau > 0
+    assert fwd(FAKE, 2, 16, FAKE, float("nan"), FAKE, FAKE, None) == INVALID
+    assert fwd(FAKE, 2, 16, FAKE, float("inf"), FAKE, FAKE, None) == INVALID
+    assert fwd(FAKE + 2, 2, 16, FAKE, 1.0, FAKE, FAKE, None) == INVALID
+    assert fwd(FAKE, -1, 16, FAKE, 1.0, FAKE, FAKE, None) == INVALID
+    assert fwd(None, 0, 16, None, 1.0, None, None, None) == OK            # nothing to do
+    assert fwd(None, 2, 0, None, 1.0, None, None, None) == OK
+    assert bwd(FAKE, None, FAKE, 2, 16, 1.0, FAKE, FAKE, None) == INVALID
+    assert bwd(FAKE, FAKE, FAKE, 2, 16, -1.0, FAKE, FAKE, None) == INVALID
+    assert bwd(FAKE, FAKE, None, 2, 16, 1.0, FAKE, FAKE, None) == INVALID
+    assert bwd(None, None, None, 0, 16, 1.0, None, None, None) == OK
