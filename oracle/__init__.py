@@ -58,6 +58,10 @@ def _bind(lib):
     lib.oracle_keep_count.argtypes = [i64, i64, i64, i64]
     lib.oracle_select.restype = cint
     lib.oracle_select.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp]
+    if hasattr(lib, "oracle_sparse_lse"):
+        lib.oracle_sparse_lse.restype = cint
+        lib.oracle_sparse_lse.argtypes = [vp, vp, cint, i64, i64, i64, i64, i64, dbl, i64, vp, vp,
+                                          cint, vp]
     if hasattr(lib, "oracle_block_scores"):
         lib.oracle_block_scores.restype = cint
         lib.oracle_block_scores.argtypes = [vp, vp, cint, i64, i64, i64, i64, i64, dbl, i64, i64,
@@ -144,6 +148,30 @@ def future_mass(q: np.ndarray, k: np.ndarray, window: int, scale: float = 0.0, *
         out["winmass"] = winmass
     if mass_heads is not None:
         out["mass_heads"] = mass_heads
+    return out
+
+
+def sparse_lse(q: np.ndarray, k: np.ndarray, window: int, rank: np.ndarray, cutoff: np.ndarray,
+               scale: float = 0.0, *, f32_exact: bool = False, nthreads: Optional[int] = None,
+               lib=None) -> np.ndarray:
+    """KVpop §3.2 sparse log-normaliser [B, Hq, S] (fp64): the LSE of each
+    query row over the running top-k pattern (window, sinks, eligible tokens
+    of rank <= cutoff); rank / cutoff int32 [B, Hkv, S] from running_cutoff."""
+    lib = lib or load()
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    rank = np.ascontiguousarray(rank, dtype=np.int32)
+    cutoff = np.ascontiguousarray(cutoff, dtype=np.int32)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if rank.shape != (B, Hkv, S) or cutoff.shape != (B, Hkv, S):
+        raise ValueError("rank and cutoff must be [B, Hkv, S]")
+    out = np.empty((B, Hq, S), dtype=np.float64)
+    rc = lib.oracle_sparse_lse(q.ctypes.data, k.ctypes.data, _dtype_code(q, f32_exact), B, Hq, Hkv,
+                               S, D, float(scale), int(window), rank.ctypes.data,
+                               cutoff.ctypes.data, nthreads or default_threads(), out.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_sparse_lse rejected the arguments (rc={rc})")
     return out
 
 

@@ -405,6 +405,52 @@ int oracle_running_cutoff(const double* score, int64_t B, int64_t Hkv, int64_t S
   return 0;
 }
 
+/* Log-normaliser of the running top-k sparse attention ([KVpop] §3.2: the
+ * student's sparse attention keeps, at query q, the sinks, the protected
+ * window and the eligible tokens of rank at most the cutoff tau_q; its
+ * per-query log-normalisers stand in for the dense ones in the target):
+ *   lse[b,g,i] = ln sum_{j in K(i)} exp(l_g(i,j)),
+ *   K(i) = { j <= i : i - j < window  or  rank[b,h,j] <= cutoff[b,h,i] }
+ * with rank / cutoff as oracle_running_cutoff writes them (rank -1 for the
+ * sinks, so they are always kept; cutoff S keeps every eligible token, -1
+ * none).  An empty K(i) gives -inf.  Returns 0, or 1 on invalid arguments. */
+int oracle_sparse_lse(const void* q, const void* k, int dtype, int64_t B, int64_t Hq, int64_t Hkv,
+                      int64_t S, int64_t D, double scale, int64_t window, const int32_t* rank,
+                      const int32_t* cutoff, int nthreads, double* lse) {
+  if (!q || !k || !rank || !cutoff || !lse || B < 0 || Hq < 1 || Hkv < 1 || S < 0 || D < 1 ||
+      Hq % Hkv != 0 || window < 0 || dtype < 0 || dtype > 2)
+    return 1;
+  if (!(scale > 0.0)) scale = 1.0 / std::sqrt(static_cast<double>(D));
+  const int64_t G = Hq / Hkv;
+  parallel_items(B * Hq, nthreads, [&](int64_t item) {
+    const int64_t b = item / Hq, g = item % Hq, h = g / G;
+    std::vector<double> qg, kh;
+    widen_head(q, dtype, (b * Hq + g) * S * D, S, D, qg);
+    widen_head(k, dtype, (b * Hkv + h) * S * D, S, D, kh);
+    const int32_t* rk = rank + (b * Hkv + h) * S;
+    const int32_t* cut = cutoff + (b * Hkv + h) * S;
+    std::vector<double> logit(static_cast<size_t>(S > 0 ? S : 1));
+    for (int64_t i = 0; i < S; ++i) {
+      double m = -INFINITY;
+      for (int64_t j = 0; j <= i; ++j) {
+        const bool keep = (i - j < window) || (rk[j] <= cut[i]);
+        if (!keep) continue;
+        double dot = 0.0;
+        for (int64_t c = 0; c < D; ++c) dot += qg[i * D + c] * kh[j * D + c];
+        logit[j] = scale * dot;
+        m = std::max(m, logit[j]);
+      }
+      double z = 0.0;
+      for (int64_t j = 0; j <= i; ++j) {
+        const bool keep = (i - j < window) || (rk[j] <= cut[i]);
+        if (keep) z += std::exp(logit[j] - m);
+      }
+      lse[(b * Hq + g) * S + i] = z > 0.0 ? m + std::log(z) : -INFINITY;
+    }
+  });
+  return 0;
+}
+
 /* ForesightKV Golden-Eviction block scores and future scores ("ForesightKV:
  * Optimizing KV Cache Eviction for Reasoning Models by Learning Long-Term
  * Contribution", §3.2 "Golden Eviction" and the appendix's block-level
