@@ -124,9 +124,9 @@ def next_rows(kvp, torch, wl, L, q_all, k_all, lse_all, stream) -> dict:
     the same resident layers (not part of the timed steps): the per-query-head
     mass pass (every layer), the target epilogue over all layers' per-head
     masses in one launch, the running top-k cutoff over all (layer, KV head)
-    rows of those scores in one launch, LKV's Soft-TopK forward and backward
-    over those rows, and the Golden-Eviction block and future scores (every
-    layer)."""
+    rows of those scores in one launch, the sparse LSE of layer 0 under that
+    cutoff, LKV's Soft-TopK forward and backward over those rows, and the
+    Golden-Eviction block and future scores (every layer)."""
     B, Hq, Hkv, S, D = wl.B, wl.Hq, wl.Hkv, wl.S, wl.D
     w, s, k = wl.window, wl.n_sink, wl.top_k
     dev = q_all.device
@@ -169,6 +169,13 @@ def next_rows(kvp, torch, wl, L, q_all, k_all, lse_all, stream) -> dict:
     rows = L * B * Hkv
     ws = torch.empty(max(1, 20 * rows * (S - min(s, S))), dtype=torch.uint8, device=dev)
     cut_ms = timed(lambda: kvp.running_cutoff(score, w, s, k, workspace=ws), 3)
+    # the sparse normaliser of KVpop's student on layer 0, with the running
+    # cutoff of its own target scores (window, sinks, budget of the workload)
+    rk_all, ct_all = kvp.running_cutoff(score, w, s, k, workspace=ws)
+    sp_out = torch.empty_like(lse_all[0])
+    sp_ms = timed(lambda: kvp.lse_sparse(q_all[0], k_all[0], rk_all[:B], ct_all[:B], w,
+                                         out=sp_out), 3)
+    lse_pairs = B * Hq * S * (S + 1) // 2
     # LKV Soft-TopK over the same rows with the same budget, forward and backward
     st_k = torch.full((rows,), float(k), dtype=torch.float32, device=dev)
     st_in = score.view(rows, S)
@@ -181,7 +188,8 @@ def next_rows(kvp, torch, wl, L, q_all, k_all, lse_all, stream) -> dict:
     st_dy = torch.ones_like(st_in)
     st_bwd_ms = timed(lambda: kvp.soft_topk_backward(st_in, st_out["lam"], st_dy, 1.0), 3)
     log(f"bench: per-head mass {ph_ms:.3f} ms/layer, target {tgt_ms:.4f} ms, "
-        f"running cutoff {cut_ms:.3f} ms ({rows} rows), soft top-k {st_fwd_ms:.3f} + "
+        f"running cutoff {cut_ms:.3f} ms ({rows} rows), sparse LSE {sp_ms:.3f} ms/layer, "
+        f"soft top-k {st_fwd_ms:.3f} + "
         f"{st_bwd_ms:.3f} ms, block scores {blk_ms:.3f} ms/layer")
     return {
         "mass_per_head": {"ms_per_layer": round(ph_ms, 4),
@@ -194,6 +202,10 @@ def next_rows(kvp, torch, wl, L, q_all, k_all, lse_all, stream) -> dict:
                           "agg": "mean of logs, count-normalised, eps 1e-6"},
         "running_cutoff": {"ms_all_layers": round(cut_ms, 4), "rows": rows, "keys_per_row": S,
                            "mkeys_per_s": round(rows * S / (cut_ms * 1e-3) / 1e6, 1)},
+        "lse_sparse": {"ms_per_layer": round(sp_ms, 4),
+                       "gpairs_per_s": round(lse_pairs / (sp_ms * 1e-3) / 1e9, 3),
+                       "frac_bf16_peak": round(lse_pairs * 2 * D / (sp_ms * 1e-3) / 1e12
+                                               / PEAK_BF16_TFLOPS, 4)},
         "soft_topk": {"fwd_ms_all_rows": round(st_fwd_ms, 4), "bwd_ms_all_rows": round(st_bwd_ms, 4),
                       "rows": rows, "n": S, "k": k},
         "block_future_scores": {"ms_per_layer": round(blk_ms, 4), "block_start": b_start,

@@ -19,6 +19,7 @@ KVpop's training target from the masses:
 The running top-k mask of every query position:
 
     rank, cutoff = running_cutoff(r, window, n_sink, k)   # int32 [B, Hkv, S] each
+    lse_s = lse_sparse(q, k, rank, cutoff, window)         # LSE of that sparse attention
 
 ForesightKV's Golden-Eviction scores (query blocks of L rows after the first B):
 
@@ -38,7 +39,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["lse_fwd", "future_mass", "future_mass_per_head", "target_scores", "select_topk",
+__all__ = ["lse_fwd", "lse_sparse", "future_mass", "future_mass_per_head", "target_scores", "select_topk",
            "keep_count", "running_cutoff", "block_count", "block_future_scores", "soft_topk", "soft_topk_backward",
            "KvpError", "library_path", "load_library", "AGG_LOG_MEAN",
            "AGG_MEAN_LOG", "AGG_MAX_LOG"]
@@ -77,6 +78,8 @@ def load_library():
             vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
             lib.kvp_lse_fwd.restype = ctypes.c_int
             lib.kvp_lse_fwd.argtypes = [vp, vp, ctypes.c_int, _Dims, f32, vp, vp]
+            lib.kvp_lse_sparse.restype = ctypes.c_int
+            lib.kvp_lse_sparse.argtypes = [vp, vp, ctypes.c_int, _Dims, f32, vp, vp, i32, vp, vp]
             lib.kvp_future_mass.restype = ctypes.c_int
             lib.kvp_future_mass.argtypes = [vp, vp, vp, ctypes.c_int, _Dims, f32, i32, vp, vp]
             lib.kvp_future_mass_per_head.restype = ctypes.c_int
@@ -167,6 +170,30 @@ def lse_fwd(q: torch.Tensor, k: torch.Tensor, scale: float = 0.0,
         raise KvpError("lse out must be fp32 [B, Hq, S]")
     _check(lib.kvp_lse_fwd(q.data_ptr(), k.data_ptr(), _dtype_code(q), d, float(scale),
                            out.data_ptr(), _stream_ptr(stream)), "kvp_lse_fwd")
+    return out
+
+
+def lse_sparse(q: torch.Tensor, k: torch.Tensor, rank: torch.Tensor, cutoff: torch.Tensor,
+               window: int, scale: float = 0.0, out: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """Per-query LSE over the running top-k pattern (window, sinks and the
+    eligible keys with rank <= cutoff), fp32 [B, Hq, S]; rank / cutoff int32
+    [B, Hkv, S] from running_cutoff."""
+    lib = load_library()
+    _require_device(q, k, rank, cutoff)
+    d = _dims(q, k)
+    shape = (d.batch, d.n_kv_heads, d.seq_len)
+    for t in (rank, cutoff):
+        if t.dtype != torch.int32 or tuple(t.shape) != shape:
+            raise KvpError("rank and cutoff must be int32 [B, Hkv, S]")
+    if out is None:
+        out = torch.empty((d.batch, d.n_q_heads, d.seq_len), dtype=torch.float32, device=q.device)
+    _require_device(out)
+    if out.dtype != torch.float32 or tuple(out.shape) != (d.batch, d.n_q_heads, d.seq_len):
+        raise KvpError("lse out must be fp32 [B, Hq, S]")
+    _check(lib.kvp_lse_sparse(q.data_ptr(), k.data_ptr(), _dtype_code(q), d, float(scale),
+                              rank.data_ptr(), cutoff.data_ptr(), int(window), out.data_ptr(),
+                              _stream_ptr(stream)), "kvp_lse_sparse")
     return out
 
 

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 5;
+constexpr int32_t kAbiVersion = 6;
 // Limits that keep every index the kernels form in 32-bit ints, and the bytes
 // of one head (S * d * 4 at most) within a 32-bit buffer range.
 constexpr int64_t kMaxSeq = int64_t(1) << 22;
@@ -84,6 +84,23 @@ kvp_status kvp_lse_fwd(const void* q, const void* k, kvp_dtype dtype, kvp_dims d
     return KVP_ERR_INVALID;
   return from_hip(kvp::launch_lse(q, k, dtype == KVP_BF16 ? 0 : 1, sh,
                                   resolve_scale(scale, sh.D), lse, stream));
+}
+
+kvp_status kvp_lse_sparse(const void* q, const void* k, kvp_dtype dtype, kvp_dims dims, float scale,
+                          const int32_t* rank, const int32_t* cutoff, int32_t window, float* lse,
+                          hipStream_t stream) {
+  kvp::Shape sh;
+  const kvp_status st = check_dims(dims, true, sh);
+  if (st != KVP_OK) return st;
+  if (!valid_dtype(dtype)) return KVP_ERR_UNSUPPORTED;
+  if (std::isnan(scale) || std::isinf(scale) || window < 0) return KVP_ERR_INVALID;
+  if (sh.B == 0 || sh.S == 0) return KVP_OK;
+  if (!q || !k || !lse || !rank || !cutoff || !aligned(q, 16) || !aligned(k, 16) ||
+      !aligned(lse, 4) || !aligned(rank, 4) || !aligned(cutoff, 4))
+    return KVP_ERR_INVALID;
+  const int w = window > sh.S ? sh.S : window;
+  return from_hip(kvp::launch_lse_sparse(q, k, dtype == KVP_BF16 ? 0 : 1, sh,
+                                         resolve_scale(scale, sh.D), rank, cutoff, w, lse, stream));
 }
 
 kvp_status kvp_future_mass(const void* q, const void* k, const float* lse, kvp_dtype dtype,

@@ -15,6 +15,11 @@ struct Shape {
 // dtype: 0 = bf16, 1 = fp32 (rounded to bf16 on load).
 hipError_t launch_lse(const void* q, const void* k, int dtype, const Shape& sh, float scale,
                       float* lse, hipStream_t stream);
+// LSE over the running top-k pattern: j counts for i iff j <= i and
+// (i - j < window or rank[j] <= cutoff[i]); rank, cutoff [B, Hkv, S].
+hipError_t launch_lse_sparse(const void* q, const void* k, int dtype, const Shape& sh, float scale,
+                             const int32_t* rank, const int32_t* cutoff, int window, float* lse,
+                             hipStream_t stream);
 // per_head = 0: mass [B, Hkv, S] summed over each group; 1: mass [B, Hq, S].
 hipError_t launch_mass(const void* q, const void* k, const float* lse, int dtype, const Shape& sh,
                        float scale, int window, int per_head, float* mass, hipStream_t stream);

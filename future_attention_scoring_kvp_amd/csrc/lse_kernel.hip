@@ -25,6 +25,13 @@
 //     between the VALU operations of block p;
 //   * every workgroup of a (batch, KV head) walks the same key sequence
 //     (shared L2), and workgroups run longest first.
+// Sparse mode (the running top-k pattern of KVpop §3.2, whose per-query
+// log-normalisers the student returns): key j counts for query i iff j <= i
+// and (i - j < w or rank[j] <= cutoff[i]).  Each staged key block carries its
+// 32 ranks in LDS, read into registers with the block's operands; each lane
+// holds the cutoffs of its two query columns.  Leading key blocks outside
+// every query's window need only the rank test (pipelined like the dense
+// path); the window band and the diagonal take the general test.
 // The shift u of a row is the largest logit of its first key block (which
 // always holds key 0, valid for every row), so the running sum is >= 1 and
 // cannot underflow; it could only overflow if a later logit exceeded that by
@@ -59,17 +66,36 @@ struct LseArgs {
   int B, Hq, Hkv, S, G;
   int n_wg;  // workgroups per (batch, KV head)
   float c;   // scale * log2(e)
+  // sparse mode (running top-k pattern): key j counts for query i iff
+  // j <= i and (i - j < window or rank[j] <= cutoff[i]); [B, Hkv, S] each
+  const int32_t* rank;
+  const int32_t* cutoff;
+  int window;
 };
 
+template <bool kSp>
 struct LTile {
   f32x16_t s0, s1;  // logits: 32 keys (rows) x query half 0 / 1 (columns)
 };
+template <>
+struct LTile<true> {
+  f32x16_t s0, s1;
+  u32x4_t rk0, rk1, rk2, rk3;  // ranks of this lane's 16 key rows (sparse mode)
+  __device__ __forceinline__ int rank_of(int v) const {
+    const u32x4_t& q = v < 4 ? rk0 : v < 8 ? rk1 : v < 12 ? rk2 : rk3;
+    return (int)q[v & 3];
+  }
+};
 
-template <int D, typename T, int W>
+template <int D, typename T, int W, bool kSp>
 __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
   using C = LseCfg<D, W>;
+  using Tile = LTile<kSp>;
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[C::kStageBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[C::kStageBytes];
+  // sparse mode: ranks of the staged key blocks, one int per key
+  __shared__ __attribute__((aligned(16))) int r_lds0[kSp ? C::kSlots * kBlk : 4];
+  __shared__ __attribute__((aligned(16))) int r_lds1[kSp ? C::kSlots * kBlk : 4];
 
   const int S = a.S, G = a.G;
   int unit, tile;
@@ -129,6 +155,19 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
   const int iq0 = p0 + l32;
   const int iq1 = iq0 + 32;
 
+  // sparse mode: the cutoffs of this lane's two query columns, and the
+  // leading key blocks that lie outside every query's window (the rank test
+  // alone decides there)
+  const size_t kv_row = (size_t)(b * a.Hkv + h) * S;
+  int cut0 = 0, cut1 = 0, kb_rank_end = 0;
+  if constexpr (kSp) {
+    cut0 = iq0 < S ? a.cutoff[kv_row + iq0] : -1;
+    cut1 = iq1 < S ? a.cutoff[kv_row + iq1] : -1;
+    const int lim = p0 - a.window + 1;  // keys j <= p0 - w are outside all windows
+    kb_rank_end = active && lim > 0 ? min(kb_full, lim / kBlk) : 0;
+  }
+  int rank_pref = 0;
+
   // ---- staging: wave w copies key block 4 * st + w of stage st, in halves
   constexpr int kHalf = C::kKSteps / 2;
   u32x4_t stage_regs[kHalf];
@@ -136,13 +175,23 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
   auto issue_loads = [&](int st, int half) __attribute__((always_inline)) {
     const int kb = st * C::kSlots + wave;
     if (kb >= n_kb) return;
+    if constexpr (kSp) {
+      if (half == 0 && lane < kBlk) {
+        const int j = kb * kBlk + lane;
+        rank_pref = j < S ? a.rank[kv_row + j] : 0x7FFFFFFF;
+      }
+    }
     const uint32_t e0 = (uint32_t)(kb * kBlk + l32) * D + 8 * h32;
 #pragma unroll
     for (int t = 0; t < kHalf; ++t)  // keys >= S read 0
       stage_regs[t] = buf_load8(kr, e0 + 16 * (half * kHalf + t), static_cast<const T*>(nullptr));
   };
-  auto store_half = [&](int st, int half, unsigned char* kdst) __attribute__((always_inline)) {
+  auto store_half = [&](int st, int half, unsigned char* kdst, int* rdst)
+                        __attribute__((always_inline)) {
     if (st * C::kSlots + wave >= n_kb) return;
+    if constexpr (kSp) {
+      if (half == 1 && lane < kBlk) rdst[wave * kBlk + lane] = rank_pref;
+    }
     unsigned char* slot = kdst + wave * C::kSlotBytes + lane * 16;
 #pragma unroll
     for (int t = 0; t < kHalf; ++t)
@@ -150,8 +199,17 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
   };
 
   // ---- compute
-  auto mfma_block = [&](LTile& t, const unsigned char* ksrc, int slot) __attribute__((always_inline)) {
+  auto mfma_block = [&](Tile& t, const unsigned char* ksrc, const int* rsrc, int slot)
+                        __attribute__((always_inline)) {
     const unsigned char* src = ksrc + slot * C::kSlotBytes + lane * 16;
+    if constexpr (kSp) {
+      // ranks of rows 8 g + 4 h32 + (0..3): the rows of values 4 g .. 4 g + 3
+      const int* rp = rsrc + slot * kBlk + 4 * h32;
+      t.rk0 = *reinterpret_cast<const u32x4_t*>(rp);
+      t.rk1 = *reinterpret_cast<const u32x4_t*>(rp + 8);
+      t.rk2 = *reinterpret_cast<const u32x4_t*>(rp + 16);
+      t.rk3 = *reinterpret_cast<const u32x4_t*>(rp + 24);
+    }
 #pragma unroll
     for (int ks = 0; ks < C::kKSteps; ++ks) {
       const u32x4_t ak = *reinterpret_cast<const u32x4_t*>(src + ks * C::kFragBytes);
@@ -159,7 +217,7 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
       t.s1 = mfma_32x32x16(ak, qf[1][ks], ks ? t.s1 : f32x16_t{});
     }
   };
-  auto exp_full = [&](const LTile& t) __attribute__((always_inline)) {
+  auto exp_full = [&](const Tile& t) __attribute__((always_inline)) {
     float t0 = 0.f, t1 = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -169,7 +227,47 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
     sum0 += t0;
     sum1 += t1;
   };
-  auto exp_masked = [&](const LTile& t, int kb) __attribute__((always_inline)) {
+  // sparse mode, blocks outside every window: a key counts iff its rank is
+  // at most the query's cutoff
+  auto exp_rank = [&](const Tile& t) __attribute__((always_inline)) {
+    if constexpr (kSp) {
+      float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rk = t.rank_of(v);
+        const float x0 = __builtin_fmaf(t.s0[v], c, -u0);
+        const float x1 = __builtin_fmaf(t.s1[v], c, -u1);
+        t0 += fast_exp2(rk <= cut0 ? x0 : -__builtin_inff());
+        t1 += fast_exp2(rk <= cut1 ? x1 : -__builtin_inff());
+      }
+      sum0 += t0;
+      sum1 += t1;
+    }
+  };
+  // sparse mode, other blocks: causal, and window or rank
+  auto exp_sparse = [&](const Tile& t, int kb) __attribute__((always_inline)) {
+    if constexpr (kSp) {
+      const int lim0 = min(iq0, S - 1) - kb * kBlk - 4 * h32;  // causal: r <= lim
+      const int lim1 = min(iq1, S - 1) - kb * kBlk - 4 * h32;
+      const int win0 = iq0 - a.window - kb * kBlk - 4 * h32;   // window: r > win
+      const int win1 = iq1 - a.window - kb * kBlk - 4 * h32;
+      float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + (v & 3);
+        const int rk = t.rank_of(v);
+        const bool k0 = r <= lim0 && (r > win0 || rk <= cut0);
+        const bool k1 = r <= lim1 && (r > win1 || rk <= cut1);
+        const float x0 = __builtin_fmaf(t.s0[v], c, -u0);
+        const float x1 = __builtin_fmaf(t.s1[v], c, -u1);
+        t0 += fast_exp2(k0 ? x0 : -__builtin_inff());
+        t1 += fast_exp2(k1 ? x1 : -__builtin_inff());
+      }
+      sum0 += t0;
+      sum1 += t1;
+    }
+  };
+  auto exp_masked = [&](const Tile& t, int kb) __attribute__((always_inline)) {
     // key j = 32 kb + 8 (v / 4) + 4 h32 + v % 4 counts iff j <= min(i, S - 1),
     // i.e. iff the constant 8 (v / 4) + v % 4 <= lim
     const int lim0 = min(iq0, S - 1) - kb * kBlk - 4 * h32;
@@ -187,7 +285,7 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
     sum1 += t1;
   };
   // Shifts from the first key block (key 0 is valid for every row).
-  auto set_shift = [&](const LTile& t) __attribute__((always_inline)) {
+  auto set_shift = [&](const Tile& t) __attribute__((always_inline)) {
     float m0 = -__builtin_inff(), m1 = -__builtin_inff();
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -201,31 +299,43 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
     u1 = m1 * c;
   };
   // Exponentials of block kb (in cur) and MFMAs of block kb + 1 (into nxt).
-  auto step = [&](LTile& cur, LTile& nxt, int kb, const unsigned char* nk, int nslot)
+  auto step = [&](Tile& cur, Tile& nxt, int kb, const unsigned char* nk, const int* nr, int nslot)
                   __attribute__((always_inline)) {
     const bool m_ok = kb + 1 < kb_end;
-    const bool full = kb < kb_full;
-    if (m_ok && full) {
-      mfma_block(nxt, nk, nslot);
-      exp_full(cur);
+    // dense: blocks below every query; sparse: blocks also outside every window
+    const bool fast = kSp ? kb < kb_rank_end : kb < kb_full;
+    constexpr int kValuPerMfma = (kSp ? 5 : 3) * 32 / C::kMfmaPerBlock;
+    if (m_ok && fast) {
+      mfma_block(nxt, nk, nr, nslot);
+      if constexpr (kSp)
+        exp_rank(cur);
+      else
+        exp_full(cur);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
       for (int m = 0; m < C::kMfmaPerBlock; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, C::kValuPerBlock / C::kMfmaPerBlock, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
         if ((m & 1) == 1 && m < 2 * C::kKSteps - 2)
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     } else {
-      if (m_ok) mfma_block(nxt, nk, nslot);
-      if (full)
-        exp_full(cur);
-      else if (kb < kb_end)
-        exp_masked(cur, kb);
+      if (m_ok) mfma_block(nxt, nk, nr, nslot);
+      if (fast) {
+        if constexpr (kSp)
+          exp_rank(cur);
+        else
+          exp_full(cur);
+      } else if (kb < kb_end) {
+        if constexpr (kSp)
+          exp_sparse(cur, kb);
+        else
+          exp_masked(cur, kb);
+      }
     }
   };
 
-  LTile t0, t1;
+  Tile t0, t1;
   // One stage: the exponentials of its kSlots key blocks, the MFMAs of each
   // next block one step ahead (the last step's from the other buffer, after
   // the barrier); the next stage's copies are stored in two halves.
@@ -238,32 +348,34 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
     constexpr int kBuf = decltype(bufc)::value;
     unsigned char* ck = kBuf ? k_lds1 : k_lds0;
     unsigned char* nk = kBuf ? k_lds0 : k_lds1;
+    int* cr = kBuf ? r_lds1 : r_lds0;
+    int* nr = kBuf ? r_lds0 : r_lds1;
     const bool more = st + 1 < n_stages;
     if (more) issue_loads(st + 1, 0);
     const int kb0 = st * C::kSlots;
 #pragma unroll
     for (int j = 0; j < C::kSlots - 1; ++j) {
       if (j & 1)
-        step(t1, t0, kb0 + j, ck, j + 1);
+        step(t1, t0, kb0 + j, ck, cr, j + 1);
       else
-        step(t0, t1, kb0 + j, ck, j + 1);
+        step(t0, t1, kb0 + j, ck, cr, j + 1);
       if (more && j == kStoreA) {
-        store_half(st + 1, 0, nk);
+        store_half(st + 1, 0, nk, nr);
         issue_loads(st + 1, 1);
       }
-      if (more && j == kStoreB) store_half(st + 1, 1, nk);
+      if (more && j == kStoreB) store_half(st + 1, 1, nk, nr);
     }
     __syncthreads();
-    step(t1, t0, kb0 + C::kSlots - 1, nk, 0);
+    step(t1, t0, kb0 + C::kSlots - 1, nk, nr, 0);
   };
 
   issue_loads(0, 0);
-  store_half(0, 0, k_lds0);
+  store_half(0, 0, k_lds0, r_lds0);
   issue_loads(0, 1);
-  store_half(0, 1, k_lds0);
+  store_half(0, 1, k_lds0, r_lds0);
   __syncthreads();
   if (0 < kb_end) {
-    mfma_block(t0, k_lds0, 0);
+    mfma_block(t0, k_lds0, r_lds0, 0);
     set_shift(t0);
   }
   for (int st = 0; st < n_stages; st += 2) {
@@ -279,16 +391,23 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
     float* out = a.lse + (size_t)(b * a.Hq + h * G + g) * S;
     const float l0 = (u0 + __log2f(sum0)) * kLn2;
     const float l1 = (u1 + __log2f(sum1)) * kLn2;
-    // A non-finite sum (overflow) is flagged as +inf for the exact fallback.
-    if (iq0 < S) out[iq0] = (sum0 < __builtin_inff() && l0 == l0) ? l0 : __builtin_inff();
-    if (iq1 < S) out[iq1] = (sum1 < __builtin_inff() && l1 == l1) ? l1 : __builtin_inff();
+    // A non-finite sum (overflow) is flagged as +inf for the exact fallback;
+    // in sparse mode so is a sum too small to trust (the shift comes from
+    // every key of the first block, kept or not) or an empty pattern.
+    const float lo = kSp ? 0x1p-60f : 0.f;
+    const bool ok0 = sum0 < __builtin_inff() && l0 == l0 && (!kSp || sum0 >= lo);
+    const bool ok1 = sum1 < __builtin_inff() && l1 == l1 && (!kSp || sum1 >= lo);
+    if (iq0 < S) out[iq0] = ok0 ? l0 : __builtin_inff();
+    if (iq1 < S) out[iq1] = ok1 ? l1 : __builtin_inff();
   }
 }
 
 // Exact recomputation of the rows flagged +inf (or NaN) by lse_kernel: one
-// wave per flagged row, max pass then sum pass, fp32.  Rows that are finite
-// are left as they are; the kernel only reads them when nothing is flagged.
-template <int D, typename T>
+// wave per flagged row, max pass then sum pass over the row's counted keys
+// (all of j <= i, or the sparse pattern), fp32; an empty pattern gives -inf.
+// Rows that are finite are left as they are; the kernel only reads them when
+// nothing is flagged.
+template <int D, typename T, bool kSp>
 __global__ __launch_bounds__(256) void lse_fix_kernel(LseArgs a, float scale) {
   const int64_t rows = (int64_t)a.B * a.Hq * a.S;
   const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -329,21 +448,38 @@ __global__ __launch_bounds__(256) void lse_fix_kernel(LseArgs a, float scale) {
       }
       return dot * scale;
     };
+    const size_t kv_row = (size_t)(bb * a.Hkv + hh) * a.S;
+    const int cut = kSp ? a.cutoff[kv_row + i] : 0;
+    auto counts = [&](int j) {
+      if constexpr (kSp) return (i - j < a.window) || (a.rank[kv_row + j] <= cut);
+      return true;
+    };
     float m = -__builtin_inff();
-    for (int j = lane; j <= i; j += 64) m = fmaxf(m, logit(j));
+    for (int j = lane; j <= i; j += 64)
+      if (counts(j)) m = fmaxf(m, logit(j));
     for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
     float s = 0.f;
-    for (int j = lane; j <= i; j += 64) s += __expf(logit(j) - m);
+    for (int j = lane; j <= i; j += 64)
+      if (counts(j)) s += __expf(logit(j) - m);
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == 0) a.lse[r] = m + __logf(s);
+    if (lane == 0) a.lse[r] = s > 0.f ? m + __logf(s) : -__builtin_inff();
   }
 }
 
-template <int D, typename T, int W>
+struct SparseIn {
+  const int32_t* rank;
+  const int32_t* cutoff;
+  int window;
+};
+
+template <int D, typename T, int W, bool kSp>
 hipError_t launch_lse_w(const void* q, const void* k, const Shape& sh, float scale, float* lse,
-                        hipStream_t stream) {
+                        const SparseIn& sp, hipStream_t stream) {
   using C = LseCfg<D, W>;
   LseArgs a;
+  a.rank = sp.rank;
+  a.cutoff = sp.cutoff;
+  a.window = sp.window;
   a.q = q;
   a.k = k;
   a.lse = lse;
@@ -356,37 +492,49 @@ hipError_t launch_lse_w(const void* q, const void* k, const Shape& sh, float sca
   const int64_t n_pb = (sh.S + C::kQueriesPerWave - 1) / C::kQueriesPerWave;
   a.n_wg = (int)((n_pb * sh.G + C::kWaves - 1) / C::kWaves);
   const int64_t blocks = (int64_t)a.n_wg * sh.B * sh.Hkv;
-  hipLaunchKernelGGL((lse_kernel<D, T, W>), dim3((unsigned)blocks), dim3(C::kThreads), 0, stream,
-                     a);
+  hipLaunchKernelGGL((lse_kernel<D, T, W, kSp>), dim3((unsigned)blocks), dim3(C::kThreads), 0,
+                     stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t rows = (int64_t)sh.B * sh.Hq * sh.S;
   const int64_t fix_blocks = (rows + 255) / 256;
-  hipLaunchKernelGGL((lse_fix_kernel<D, T>), dim3((unsigned)fix_blocks), dim3(256), 0, stream, a,
-                     scale);
+  hipLaunchKernelGGL((lse_fix_kernel<D, T, kSp>), dim3((unsigned)fix_blocks), dim3(256), 0, stream,
+                     a, scale);
   return hipGetLastError();
 }
 
 // 8-wave workgroups (one per CU) when the grid holds at least two per CU,
 // else 4-wave workgroups (two per CU).
-template <int D, typename T>
+template <int D, typename T, bool kSp>
 hipError_t launch_lse_t(const void* q, const void* k, const Shape& sh, float scale, float* lse,
-                        hipStream_t stream) {
+                        const SparseIn& sp, hipStream_t stream) {
   const int64_t n_pb = (sh.S + LseCfg<D, 8>::kQueriesPerWave - 1) / LseCfg<D, 8>::kQueriesPerWave;
   const int64_t blocks8 = (n_pb * sh.G + 7) / 8 * sh.B * sh.Hkv;
-  if (blocks8 >= 2 * kNumCUs) return launch_lse_w<D, T, 8>(q, k, sh, scale, lse, stream);
-  return launch_lse_w<D, T, 4>(q, k, sh, scale, lse, stream);
+  if (blocks8 >= 2 * kNumCUs) return launch_lse_w<D, T, 8, kSp>(q, k, sh, scale, lse, sp, stream);
+  return launch_lse_w<D, T, 4, kSp>(q, k, sh, scale, lse, sp, stream);
 }
 
 }  // namespace
 
 hipError_t launch_lse(const void* q, const void* k, int dtype, const Shape& sh, float scale,
                       float* lse, hipStream_t stream) {
+  const SparseIn none{nullptr, nullptr, 0};
   if (sh.D == 128)
-    return dtype == 0 ? launch_lse_t<128, uint16_t>(q, k, sh, scale, lse, stream)
-                      : launch_lse_t<128, float>(q, k, sh, scale, lse, stream);
-  return dtype == 0 ? launch_lse_t<64, uint16_t>(q, k, sh, scale, lse, stream)
-                    : launch_lse_t<64, float>(q, k, sh, scale, lse, stream);
+    return dtype == 0 ? launch_lse_t<128, uint16_t, false>(q, k, sh, scale, lse, none, stream)
+                      : launch_lse_t<128, float, false>(q, k, sh, scale, lse, none, stream);
+  return dtype == 0 ? launch_lse_t<64, uint16_t, false>(q, k, sh, scale, lse, none, stream)
+                    : launch_lse_t<64, float, false>(q, k, sh, scale, lse, none, stream);
+}
+
+hipError_t launch_lse_sparse(const void* q, const void* k, int dtype, const Shape& sh, float scale,
+                             const int32_t* rank, const int32_t* cutoff, int window, float* lse,
+                             hipStream_t stream) {
+  const SparseIn sp{rank, cutoff, window};
+  if (sh.D == 128)
+    return dtype == 0 ? launch_lse_t<128, uint16_t, true>(q, k, sh, scale, lse, sp, stream)
+                      : launch_lse_t<128, float, true>(q, k, sh, scale, lse, sp, stream);
+  return dtype == 0 ? launch_lse_t<64, uint16_t, true>(q, k, sh, scale, lse, sp, stream)
+                    : launch_lse_t<64, float, true>(q, k, sh, scale, lse, sp, stream);
 }
 
 }  // namespace kvp

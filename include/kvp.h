@@ -19,10 +19,11 @@
  *                             over the group and the temporal decay.
  *
  * And one gives the keep-set of every query position rather than only the
- * last one:
+ * last one, with the normaliser of the attention that keeps it:
  *
  *   kvp_running_cutoff        static ranks and the per-query cutoff rank of
- *                             the running top-k (the sparse mask predicate).
+ *                             the running top-k (the sparse mask predicate);
+ *   kvp_lse_sparse            the per-query LSE over that sparse pattern.
  *
  * A query-block variant of the transposed pass gives ForesightKV's labels:
  *
@@ -112,6 +113,24 @@ typedef struct {
  * an exact per-row fallback, so every finite input yields a finite LSE. */
 kvp_status kvp_lse_fwd(const void* q, const void* k, kvp_dtype dtype, kvp_dims dims,
                        float scale, float* lse, hipStream_t stream);
+
+/* Stage 1, sparse — the log-normaliser of the running top-k sparse attention
+ * ([KVpop] §3.2: the student's sparse attention keeps, at query q, the sink
+ * tokens, the protected window and the top-k eligible tokens, and the
+ * per-query log-normalisers it returns stand in for the dense ones in the
+ * target; pass the result to kvp_future_mass in place of kvp_lse_fwd's):
+ *   lse[b,g,i] = ln sum_{j in K(i)} exp(scale * <q[b,g,i], k[b,g/G,j]>),
+ *   K(i) = { j <= i : i - j < window  or  rank[b,h,j] <= cutoff[b,h,i] }.
+ *   rank, cutoff : device int32 [B, Hkv, S] as written by kvp_running_cutoff
+ *                  with the same window (sinks have rank -1 and are always
+ *                  kept; cutoff S keeps every eligible token, -1 none).
+ *   lse          : device fp32 [B, Hq, S], natural log; -inf for an empty K(i)
+ *                  (window 0, no sinks and no budget).
+ * The same MFMA pass as kvp_lse_fwd with the pattern tested per (query, key)
+ * pair; rows whose sum leaves the fp32 range are recomputed exactly. */
+kvp_status kvp_lse_sparse(const void* q, const void* k, kvp_dtype dtype, kvp_dims dims, float scale,
+                          const int32_t* rank, const int32_t* cutoff, int32_t window, float* lse,
+                          hipStream_t stream);
 
 /* Stage 2 — transposed future-attention-mass pass.
  *   mass[b, h, j] = sum_{g : g/G = h} sum_{i = j + window}^{S-1}

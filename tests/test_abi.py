@@ -36,7 +36,7 @@ def test_header_declares_the_three_stages():
               "kvp_status_string", "kvp_abi_version", "kvp_future_mass_per_head",
               "kvp_target_scores", "kvp_running_cutoff", "kvp_running_cutoff_workspace_bytes",
               "kvp_block_count", "kvp_block_future_scores", "kvp_soft_topk_fwd",
-              "kvp_soft_topk_bwd"):
+              "kvp_soft_topk_bwd", "kvp_lse_sparse"):
         assert n in names
 
 
@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.kvp_abi_version() == 5
+    assert lib.kvp_abi_version() == 6
     for code in range(5):
         assert lib.kvp_status_string(code)
     assert lib.kvp_status_string(99) == b"unknown status"
@@ -234,3 +234,15 @@ def test_soft_topk_validation(lib):
     assert bwd(FAKE, FAKE, FAKE, 2, 16, -1.0, FAKE, FAKE, None) == INVALID
     assert bwd(FAKE, FAKE, None, 2, 16, 1.0, FAKE, FAKE, None) == INVALID
     assert bwd(None, None, None, 0, 16, 1.0, None, None, None) == OK
+
+
+def test_lse_sparse_validation(lib):
+    f = lib.kvp_lse_sparse
+    assert f(FAKE, FAKE, 0, dims(), 0.0, None, FAKE, 4, FAKE, None) == INVALID   # rank
+    assert f(FAKE, FAKE, 0, dims(), 0.0, FAKE, None, 4, FAKE, None) == INVALID   # cutoff
+    assert f(FAKE, FAKE, 0, dims(), 0.0, FAKE, FAKE, -1, FAKE, None) == INVALID  # window
+    assert f(FAKE, FAKE, 0, dims(), 0.0, FAKE + 2, FAKE, 4, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, 0, dims(), 0.0, FAKE, FAKE, 4, None, None) == INVALID
+    assert f(FAKE, FAKE, 0, dims(D=96), 0.0, FAKE, FAKE, 4, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, FAKE, 7, dims(), 0.0, FAKE, FAKE, 4, FAKE, None) == UNSUPPORTED
+    assert f(None, None, 0, dims(S=0), 0.0, None, None, 4, None, None) == OK
