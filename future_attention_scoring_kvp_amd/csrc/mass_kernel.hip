@@ -74,6 +74,9 @@ struct MassArgs {
   int B, Hq, Hkv, S, G, window;
   int per_head;  // 0: one unit per (batch, KV head), masses summed over its G
                  // query heads; 1: one unit per (batch, query head)
+  int head_split;  // 1, or 2: the G heads of a group in two halves, each added
+                   // into the zeroed output by an atomic (two terms: the sum
+                   // does not depend on their order)
   float c;       // scale * log2(e)
   // query-block mode: blocks [seg_start + t seg_len, ...) clipped to S, both
   // multiples of 32; per block the mean over its rows and the unit's heads
@@ -120,13 +123,16 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
   // A unit is a (batch, KV head) whose G query heads are swept together, or
   // in per-head mode a single (batch, query head) with the keys of its KV head.
   const int n_heads_out = a.per_head ? a.Hq : a.Hkv;
-  const int G = a.per_head ? 1 : a.G;  // query heads swept per unit
+  const int split = a.head_split;
+  const int G = a.per_head ? 1 : a.G / split;  // query heads swept per unit
   int unit, tile;
-  xcd_map(blockIdx.x, a.B * n_heads_out, unit, tile);
+  xcd_map(blockIdx.x, a.B * n_heads_out * split, unit, tile);
+  const int part = unit % split;
+  unit /= split;
   const int b = unit / n_heads_out;
   const int ho = unit - b * n_heads_out;                  // output row within the batch
   const int h = a.per_head ? ho / a.G : ho;               // KV head
-  const int g0 = a.per_head ? ho : ho * a.G;              // first query head swept
+  const int g0 = a.per_head ? ho : ho * a.G + part * G;   // first query head swept
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -409,13 +415,24 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
 #pragma unroll
   for (int col = 0; col < 32; ++col) tot += red[lane * C::kRedStride + col];
   const int key = key0 + lane;
-  if (key < S) a.mass[(size_t)(b * n_heads_out + ho) * S + key] = tot;
+  if (key < S) {
+    float* dst = a.mass + (size_t)(b * n_heads_out + ho) * S + key;
+    if (split > 1)
+      atomicAdd(dst, tot);
+    else
+      *dst = tot;
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_fill_kernel(float* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = 0.f;
 }
 
 template <int D, typename T, int W, bool kSeg>
 hipError_t launch_mass_w(const void* q, const void* k, const float* lse, const Shape& sh,
-                         float scale, int window, int per_head, float* mass, const SegOut& seg,
-                         hipStream_t stream) {
+                         float scale, int window, int per_head, int split, float* mass,
+                         const SegOut& seg, hipStream_t stream) {
   using C = MassCfg<D, W>;
   MassArgs a;
   a.q = q;
@@ -429,6 +446,7 @@ hipError_t launch_mass_w(const void* q, const void* k, const float* lse, const S
   a.G = sh.G;
   a.window = window;
   a.per_head = per_head;
+  a.head_split = split;
   a.c = scale * kLog2e;
   a.seg_start = seg.start;
   a.seg_len = seg.len;
@@ -436,7 +454,12 @@ hipError_t launch_mass_w(const void* q, const void* k, const float* lse, const S
   a.seg_block = seg.block;
   a.seg_future = seg.future;
   const int64_t n_tiles = (sh.S + C::kKeysPerWG - 1) / C::kKeysPerWG;
-  const int64_t blocks = n_tiles * (int64_t)sh.B * (per_head ? sh.Hq : sh.Hkv);
+  const int64_t blocks = n_tiles * (int64_t)sh.B * (per_head ? sh.Hq : sh.Hkv) * split;
+  if (split > 1) {
+    const int64_t n = (int64_t)sh.B * sh.Hkv * sh.S;
+    const int64_t fill_blocks = min((n + 255) / 256, (int64_t)4 * kNumCUs);
+    hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)fill_blocks), dim3(256), 0, stream, mass, n);
+  }
   hipLaunchKernelGGL((mass_kernel<D, T, W, kSeg>), dim3((unsigned)blocks), dim3(C::kThreads), 0,
                      stream, a);
   return hipGetLastError();
@@ -444,16 +467,24 @@ hipError_t launch_mass_w(const void* q, const void* k, const float* lse, const S
 
 // 512-key workgroups (one per CU) when the grid has at least two per CU;
 // otherwise 256-key workgroups (two per CU), which double the workgroup count
-// of short sequences.
+// of short sequences.  Group sums whose 256-key grid still has fewer than two
+// workgroups per CU also split each group's heads in two halves.
 template <int D, typename T, bool kSeg>
 hipError_t launch_mass_t(const void* q, const void* k, const float* lse, const Shape& sh,
                          float scale, int window, int per_head, float* mass, const SegOut& seg,
                          hipStream_t stream) {
-  const int64_t units = (int64_t)sh.B * (per_head ? sh.Hq : sh.Hkv);
+  int64_t units = (int64_t)sh.B * (per_head ? sh.Hq : sh.Hkv);
+  int split = 1;
+  if (!kSeg && !per_head && sh.G % 2 == 0 &&
+      units * ((sh.S + MassCfg<D, 4>::kKeysPerWG - 1) / MassCfg<D, 4>::kKeysPerWG) < 2 * kNumCUs)
+    split = 2;
+  units *= split;
   const int64_t blocks8 = units * ((sh.S + MassCfg<D, 8>::kKeysPerWG - 1) / MassCfg<D, 8>::kKeysPerWG);
   if (blocks8 >= 2 * kNumCUs)
-    return launch_mass_w<D, T, 8, kSeg>(q, k, lse, sh, scale, window, per_head, mass, seg, stream);
-  return launch_mass_w<D, T, 4, kSeg>(q, k, lse, sh, scale, window, per_head, mass, seg, stream);
+    return launch_mass_w<D, T, 8, kSeg>(q, k, lse, sh, scale, window, per_head, split, mass, seg,
+                                        stream);
+  return launch_mass_w<D, T, 4, kSeg>(q, k, lse, sh, scale, window, per_head, split, mass, seg,
+                                      stream);
 }
 
 }  // namespace

@@ -139,6 +139,27 @@ def test_deterministic():
                               y.view(np.uint32) if y.dtype == np.float32 else y)
 
 
+def test_split_group_sums_deterministic_and_equal_to_head_sums():
+    """Short sequences split each group's heads over two workgroups that add
+    into the zeroed output: two terms, so repeated runs are bitwise equal,
+    and the result is the sum of the per-head masses up to fp32 rounding."""
+    import torch
+    import future_attention_scoring_kvp_amd as kvp
+    wl = kvp_inputs.workload(2).with_(S=2000, seed=21)  # 8 KV heads x 8 tiles: a small grid
+    li = kvp_inputs.make_layer(wl)
+    say("[parity] split group sums")
+    q, k = to_dev(li.q), to_dev(li.k)
+    lse = kvp.lse_fwd(q, k)
+    runs = [kvp.future_mass(q, k, lse, 64) for _ in range(3)]
+    mh = kvp.future_mass_per_head(q, k, lse, 64)
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        assert torch.equal(r.view(torch.int32), runs[0].view(torch.int32))
+    G = wl.Hq // wl.Hkv
+    ref = mh.view(1, wl.Hkv, G, wl.S).double().sum(2)
+    assert ((runs[0].double() - ref).abs() <= 1e-6 + 1e-5 * ref.abs()).all()
+
+
 def test_empty_inputs():
     q = torch.empty(1, 4, 0, 128, dtype=torch.bfloat16, device="cuda")
     lse = kvp.lse_fwd(q, q[:, :2])
