@@ -144,7 +144,10 @@ kvp_status kvp_lse_sparse(const void* q, const void* k, kvp_dtype dtype, kvp_dim
  *   window : w >= 0.
  *   mass   : device fp32 [B, Hkv, S], written entirely.
  * Each key is owned by one workgroup, which reduces over all its future
- * queries on chip: no atomics, and the result is bitwise reproducible. */
+ * queries on chip and writes it once.  When the grid is too small to fill the
+ * GPU (short sequences), each group's heads are split over two workgroups
+ * that add into the output after a zero fill: two terms, so the sum does not
+ * depend on their order.  Either way the result is bitwise reproducible. */
 kvp_status kvp_future_mass(const void* q, const void* k, const float* lse, kvp_dtype dtype,
                            kvp_dims dims, float scale, int32_t window, float* mass,
                            hipStream_t stream);
