@@ -1,15 +1,11 @@
 // Device-side building blocks shared by the gfx950 kernels of libkvp.
 //
-// Matrix-core tiles (both kernels put KEYS on the rows = A operand and
+// Matrix-core tile (both dense kernels put KEYS on the rows = A operand and
 // QUERIES on the columns = B operand):
 //   v_mfma_f32_32x32x16_bf16, D = A (32 x 16) * B (16 x 32):
 //     lane l supplies A[l % 32][8*(l/32) + e] and B[8*(l/32) + e][l % 32],
 //     e = 0..7, and receives D[8*(v/4) + 4*(l/32) + (v%4)][l % 32] in result
-//     register v = 0..15;
-//   v_mfma_f32_16x16x32_bf16, D = A (16 x 32) * B (32 x 16):
-//     lane l supplies A[l % 16][8*(l/16) + e] and B[8*(l/16) + e][l % 16],
-//     e = 0..7, and receives D[4*(l/16) + v][l % 16] in result register
-//     v = 0..3.
+//     register v = 0..15.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -38,11 +34,6 @@ __device__ __forceinline__ f32x16_t mfma_32x32x16(u32x4_t a, u32x4_t b, f32x16_t
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ f32x4_t mfma_16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
 // Buffer resource (raw, stride 0) over `bytes` bytes from `base`.  Loads whose
 // per-lane offset is at or beyond `bytes` return zeros instead of touching
 // memory (the check covers the per-lane offset only, so every offset here is
@@ -52,19 +43,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            0x00020000);
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// Direct global -> LDS copy of 16 bytes per lane: lane l's 16 bytes at byte
-// `offset` of the resource land at lds_base + 16 * l (lds_base is uniform).
-// Out-of-range lanes write zeros.  Completion is tracked by vmcnt.
-__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, void* lds_base,
-                                              uint32_t offset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_base, 16, offset, 0, 0, 0);
-}
-
-// Eight elements at element offset `elem` of a buffer, as eight bf16 values
-// (16 bytes): bf16 is passed through, fp32 is rounded to nearest even.
-// Out-of-range reads give zeros.
 // One fp32 store through a buffer resource; offsets at or past the range of
 // the resource are dropped by the hardware bounds check.
 __device__ __forceinline__ void buf_store_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_offset,
@@ -72,6 +50,9 @@ __device__ __forceinline__ void buf_store_f32(__amdgpu_buffer_rsrc_t r, uint32_t
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_offset, 0, 0);
 }
 
+// Eight elements at element offset `elem` of a buffer, as eight bf16 values
+// (16 bytes): bf16 is passed through, fp32 is rounded to nearest even.
+// Out-of-range reads give zeros.
 __device__ __forceinline__ u32x4_t buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t elem,
                                              const uint16_t*) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, elem * 2, 0, 0));
