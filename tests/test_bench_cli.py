@@ -1,0 +1,56 @@
+"""bench.py's host-side contract, checked without a GPU: the one-GPU rule,
+the kernel-source hash and the lookup of the recorded HBM traffic."""
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def run_bench(*args):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                          capture_output=True, text=True, timeout=120)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = run_bench("--gpus", "2")
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_sha_flag_prints_the_mass_kernel_hash():
+    r = run_bench("--sha")
+    assert r.returncode == 0
+    assert re.fullmatch(r"[0-9a-f]{64}\n", r.stdout)
+    assert r.stdout.strip() == bench.mass_sources_sha256()
+
+
+def test_recorded_traffic_lookup(tmp_path, monkeypatch):
+    summary = tmp_path / "summary.md"
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", "summary.md")
+    # sources are hashed from the real tree
+    monkeypatch.setattr(bench, "MASS_SOURCES", tuple(os.path.join(ROOT, p) for p in bench.MASS_SOURCES))
+    assert bench.recorded_traffic("w") is None                      # no summary
+    sha = bench.mass_sources_sha256()
+    summary.write_text(f"text\nworkload: w\nkernel_sources_sha256: {sha}\n"
+                       "traffic_bytes_per_launch: 12345\n")
+    assert bench.recorded_traffic("w") == 12345
+    assert bench.recorded_traffic("other") is None                  # another workload
+    summary.write_text(f"workload: w\nkernel_sources_sha256: {'0' * 64}\n"
+                       "traffic_bytes_per_launch: 12345\n")
+    assert bench.recorded_traffic("w") is None                      # the kernel changed since
+
+
+def test_mass_pairs_counts_the_future_triangle():
+    # S = 4, w = 1: keys 0..2 have 3, 2, 1 future queries, key 3 none
+    assert bench.mass_pairs(1, 1, 4, 1) == 6
+    assert bench.mass_pairs(2, 3, 4, 1) == 36
+    assert bench.mass_pairs(1, 1, 4, 4) == 0
+    assert bench.mass_pairs(1, 1, 4, 9) == 0
