@@ -99,24 +99,43 @@ def copy_probe(nbytes: int, reps: int) -> None:
     print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}))
 
 
-def cpu_baseline(wl, li0, n_heads: int) -> dict:
+def cpu_baseline(wl, li0, n_heads: int, max_pairs: float = 4.5e9) -> dict:
     """The CPU oracle (dense fp64 softmax rows + explicit column sums), as it
-    stands, on whole (batch 0, KV head) units 0 .. n_heads-1 of layer 0: every
-    query row of their G query heads.  Returns the future-mass pairs per
-    second the sample covers (its LSE work included in the time)."""
+    stands, on whole (batch 0, KV head) units 0 .. n_heads-1 of layer 0: the
+    query rows of their G query heads from row_lo on, row_lo = 0 unless that
+    would exceed max_pairs future-mass pairs (long sequences: the last rows,
+    each computed in full).  Returns the future-mass pairs per second the
+    sample covers (its LSE work included in the time)."""
     import oracle
     S, w, G = wl.S, wl.window, wl.G
     n_heads = max(1, min(n_heads, wl.Hkv))
+
+    def pairs_from(row_lo):  # future-mass pairs of rows >= row_lo: keys j <= i - w
+        lo = max(row_lo, w)
+        n = S - w
+        return n_heads * G * (n * (n + 1) // 2 - (lo - w) * (lo - w + 1) // 2) if lo < S else 0
+
+    row_lo = 0
+    if pairs_from(0) > max_pairs:
+        lo, hi = 0, S
+        while hi - lo > 1:
+            mid = (lo + hi) // 2
+            if pairs_from(mid) > max_pairs:
+                lo = mid
+            else:
+                hi = mid
+        row_lo = hi
     threads = oracle.default_threads()
     t0 = time.perf_counter()
     for h in range(n_heads):
-        oracle.future_mass(li0.q, li0.k, w, b_only=0, h_only=h, nthreads=threads)
+        oracle.future_mass(li0.q, li0.k, w, b_only=0, h_only=h, row_lo=row_lo, nthreads=threads)
     dt = time.perf_counter() - t0
-    pairs = n_heads * mass_pairs(1, G, S, w)
+    pairs = pairs_from(row_lo)
+    rows = "all" if row_lo == 0 else f"the last {S - row_lo} of"
     return {"value": pairs / dt / 1e9, "unit": "G query-key pairs/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 3),
             "sample": (f"layer 0, batch 0, KV heads 0..{n_heads - 1} ({n_heads * G} query heads), "
-                       f"all {S} query rows: {pairs} future-mass pairs, LSE included")}
+                       f"{rows} {S} query rows: {pairs} future-mass pairs, LSE included")}
 
 
 def next_rows(kvp, torch, wl, L, q_all, k_all, lse_all, stream) -> dict:

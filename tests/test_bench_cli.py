@@ -54,3 +54,21 @@ def test_mass_pairs_counts_the_future_triangle():
     assert bench.mass_pairs(2, 3, 4, 1) == 36
     assert bench.mass_pairs(1, 1, 4, 4) == 0
     assert bench.mass_pairs(1, 1, 4, 9) == 0
+
+
+def test_cpu_baseline_sample_is_bounded():
+    import kvp_inputs
+    wl = kvp_inputs.workload(1)                      # S = 256, w = 16, one head
+    li = kvp_inputs.make_layer(wl, 0)
+    full = bench.mass_pairs(1, 1, wl.S, wl.window)
+    whole = bench.cpu_baseline(wl, li, 1)
+    assert whole["kind"] == "oracle" and whole["value"] > 0
+    assert f"all {wl.S} query rows: {full} future-mass pairs" in whole["sample"]
+    part = bench.cpu_baseline(wl, li, 1, max_pairs=full / 4)
+    m = re.search(r"the last (\d+) of 256 query rows: (\d+) future-mass pairs", part["sample"])
+    assert m, part["sample"]
+    rows, pairs = int(m.group(1)), int(m.group(2))
+    # the pairs of the last `rows` rows, and the largest such count within the bound
+    tail = sum(i - wl.window + 1 for i in range(wl.S - rows, wl.S) if i >= wl.window)
+    assert pairs == tail <= full / 4
+    assert tail + (wl.S - rows - 1 - wl.window + 1) > full / 4
