@@ -304,7 +304,12 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
     const bool m_ok = kb + 1 < kb_end;
     // dense: blocks below every query; sparse: blocks also outside every window
     const bool fast = kSp ? kb < kb_rank_end : kb < kb_full;
-    constexpr int kValuPerMfma = (kSp ? 5 : 3) * 32 / C::kMfmaPerBlock;
+    // VALU and transcendental (exp2) operations per MFMA: dense fma + add
+    // and one exp2 per value.  The sparse rank test adds a compare and a
+    // select per value; that path keeps a single VALU group (its compiled
+    // order came out worse with a separate exp2 group).
+    constexpr int kValuPerMfma = (kSp ? 5 : 2) * 32 / C::kMfmaPerBlock;
+    constexpr int kTransPerMfma = 32 / C::kMfmaPerBlock;
     if (m_ok && fast) {
       mfma_block(nxt, nk, nr, nslot);
       if constexpr (kSp)
@@ -316,6 +321,7 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
       for (int m = 0; m < C::kMfmaPerBlock; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
+        if constexpr (!kSp) __builtin_amdgcn_sched_group_barrier(0x400, kTransPerMfma, 0);
         if ((m & 1) == 1 && m < 2 * C::kKSteps - 2)
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }

@@ -57,7 +57,9 @@ struct MassCfg {
   static constexpr int kSlots = kWaves;                 // wave w stages slot w
   static constexpr int kStageBytes = kSlots * kSlotBytes;
   static constexpr int kMfmaPerPair = 2 * kKSteps;
-  static constexpr int kValuPerPair = 3 * 32;           // fma + exp + add per value
+  // per value: fma and add on the VALU, exp2 on the transcendental unit
+  static constexpr int kAluPerPair = 2 * 32;
+  static constexpr int kTransPerPair = 32;
   static constexpr int kRedStride = 33;                 // column partials per key (+1 pad)
   static constexpr int kRedWaveFloats = kKeysPerWave * kRedStride;
   // the final reduction reuses the two stage buffers when they hold every
@@ -313,13 +315,18 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
       if (m_ok && full) {
         mfma_pair(nxt, nq, nl, nslot);
         exp_full(cur);
-        // issue order: operand reads ahead, then each MFMA followed by six
-        // VALU operations, one more operand read after every second MFMA
+        // issue order: operand reads ahead, then each MFMA followed by its
+        // share of the VALU work (at d = 128: two fma, two add, two exp2),
+        // one more operand read after every second MFMA.  The scheduler
+        // counts exp2 as transcendental (0x400), not VALU (0x002): without
+        // its own group the exps ride along and the last MFMAs of the pair
+        // go out with no VALU work beside them.
         __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
         for (int m = 0; m < C::kMfmaPerPair; ++m) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, C::kValuPerPair / C::kMfmaPerPair, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, C::kAluPerPair / C::kMfmaPerPair, 0);
+          __builtin_amdgcn_sched_group_barrier(0x400, C::kTransPerPair / C::kMfmaPerPair, 0);
           if ((m & 1) == 1 && m < 2 * C::kKSteps - 4)
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
