@@ -80,10 +80,12 @@ struct LTile {
 template <>
 struct LTile<true> {
   f32x16_t s0, s1;
-  u32x4_t rk0, rk1, rk2, rk3;  // ranks of this lane's 16 key rows (sparse mode)
-  __device__ __forceinline__ int rank_of(int v) const {
+  // ranks of this lane's 16 key rows (sparse mode), as fp32 bit patterns
+  // (exact: ranks lie in [-1, S) and S <= 2^22)
+  u32x4_t rk0, rk1, rk2, rk3;
+  __device__ __forceinline__ float rank_of(int v) const {
     const u32x4_t& q = v < 4 ? rk0 : v < 8 ? rk1 : v < 12 ? rk2 : rk3;
-    return (int)q[v & 3];
+    return __uint_as_float(q[v & 3]);
   }
 };
 
@@ -159,10 +161,13 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
   // leading key blocks that lie outside every query's window (the rank test
   // alone decides there)
   const size_t kv_row = (size_t)(b * a.Hkv + h) * S;
-  int cut0 = 0, cut1 = 0, kb_rank_end = 0;
+  // The cutoffs are held as cut + 1 in fp32, clamped to [-1, S] first (no
+  // rank lies outside [-1, S), so the test rank <= cut is unchanged and exact).
+  float cut0 = 0.f, cut1 = 0.f;
+  int kb_rank_end = 0;
   if constexpr (kSp) {
-    cut0 = iq0 < S ? a.cutoff[kv_row + iq0] : -1;
-    cut1 = iq1 < S ? a.cutoff[kv_row + iq1] : -1;
+    cut0 = (float)(iq0 < S ? min(max(a.cutoff[kv_row + iq0], -1), S) : -1) + 1.f;
+    cut1 = (float)(iq1 < S ? min(max(a.cutoff[kv_row + iq1], -1), S) : -1) + 1.f;
     const int lim = p0 - a.window + 1;  // keys j <= p0 - w are outside all windows
     kb_rank_end = active && lim > 0 ? min(kb_full, lim / kBlk) : 0;
   }
@@ -190,7 +195,7 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
                         __attribute__((always_inline)) {
     if (st * C::kSlots + wave >= n_kb) return;
     if constexpr (kSp) {
-      if (half == 1 && lane < kBlk) rdst[wave * kBlk + lane] = rank_pref;
+      if (half == 1 && lane < kBlk) rdst[wave * kBlk + lane] = __float_as_int((float)rank_pref);
     }
     unsigned char* slot = kdst + wave * C::kSlotBytes + lane * 16;
 #pragma unroll
@@ -202,19 +207,21 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
   auto mfma_block = [&](Tile& t, const unsigned char* ksrc, const int* rsrc, int slot)
                         __attribute__((always_inline)) {
     const unsigned char* src = ksrc + slot * C::kSlotBytes + lane * 16;
-    if constexpr (kSp) {
-      // ranks of rows 8 g + 4 h32 + (0..3): the rows of values 4 g .. 4 g + 3
-      const int* rp = rsrc + slot * kBlk + 4 * h32;
-      t.rk0 = *reinterpret_cast<const u32x4_t*>(rp);
-      t.rk1 = *reinterpret_cast<const u32x4_t*>(rp + 8);
-      t.rk2 = *reinterpret_cast<const u32x4_t*>(rp + 16);
-      t.rk3 = *reinterpret_cast<const u32x4_t*>(rp + 24);
-    }
 #pragma unroll
     for (int ks = 0; ks < C::kKSteps; ++ks) {
       const u32x4_t ak = *reinterpret_cast<const u32x4_t*>(src + ks * C::kFragBytes);
       t.s0 = mfma_32x32x16(ak, qf[0][ks], ks ? t.s0 : f32x16_t{});
       t.s1 = mfma_32x32x16(ak, qf[1][ks], ks ? t.s1 : f32x16_t{});
+    }
+    if constexpr (kSp) {
+      // ranks of rows 8 g + 4 h32 + (0..3): the rows of values 4 g .. 4 g + 3
+      // (read after the operands, so the operand reads keep their place in
+      // the issue order)
+      const int* rp = rsrc + slot * kBlk + 4 * h32;
+      t.rk0 = *reinterpret_cast<const u32x4_t*>(rp);
+      t.rk1 = *reinterpret_cast<const u32x4_t*>(rp + 8);
+      t.rk2 = *reinterpret_cast<const u32x4_t*>(rp + 16);
+      t.rk3 = *reinterpret_cast<const u32x4_t*>(rp + 24);
     }
   };
   auto exp_full = [&](const Tile& t) __attribute__((always_inline)) {
@@ -228,17 +235,23 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
     sum1 += t1;
   };
   // sparse mode, blocks outside every window: a key counts iff its rank is
-  // at most the query's cutoff
+  // at most the query's cutoff.  The 0/1 weight is one clamped subtract,
+  // clamp((cut + 1) - rank, 0, 1), applied in the accumulating fma: no
+  // compare masks in scalar registers.  (A dropped term whose exponential
+  // overflowed gives inf * 0 = NaN, which is flagged for the exact pass like
+  // any overflow.)
   auto exp_rank = [&](const Tile& t) __attribute__((always_inline)) {
     if constexpr (kSp) {
       float t0 = 0.f, t1 = 0.f;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int rk = t.rank_of(v);
+        const float rk = t.rank_of(v);
+        const float w0 = __builtin_amdgcn_fmed3f(cut0 - rk, 0.f, 1.f);
+        const float w1 = __builtin_amdgcn_fmed3f(cut1 - rk, 0.f, 1.f);
         const float x0 = __builtin_fmaf(t.s0[v], c, -u0);
         const float x1 = __builtin_fmaf(t.s1[v], c, -u1);
-        t0 += fast_exp2(rk <= cut0 ? x0 : -__builtin_inff());
-        t1 += fast_exp2(rk <= cut1 ? x1 : -__builtin_inff());
+        t0 = __builtin_fmaf(fast_exp2(x0), w0, t0);
+        t1 = __builtin_fmaf(fast_exp2(x1), w1, t1);
       }
       sum0 += t0;
       sum1 += t1;
@@ -255,9 +268,9 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = 8 * (v >> 2) + (v & 3);
-        const int rk = t.rank_of(v);
-        const bool k0 = r <= lim0 && (r > win0 || rk <= cut0);
-        const bool k1 = r <= lim1 && (r > win1 || rk <= cut1);
+        const float rk = t.rank_of(v);
+        const bool k0 = r <= lim0 && (r > win0 || rk < cut0);
+        const bool k1 = r <= lim1 && (r > win1 || rk < cut1);
         const float x0 = __builtin_fmaf(t.s0[v], c, -u0);
         const float x1 = __builtin_fmaf(t.s1[v], c, -u1);
         t0 += fast_exp2(k0 ? x0 : -__builtin_inff());
@@ -304,11 +317,10 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
     const bool m_ok = kb + 1 < kb_end;
     // dense: blocks below every query; sparse: blocks also outside every window
     const bool fast = kSp ? kb < kb_rank_end : kb < kb_full;
-    // VALU and transcendental (exp2) operations per MFMA: dense fma + add
-    // and one exp2 per value.  The sparse rank test adds a compare and a
-    // select per value; that path keeps a single VALU group (its compiled
-    // order came out worse with a separate exp2 group).
-    constexpr int kValuPerMfma = (kSp ? 5 : 2) * 32 / C::kMfmaPerBlock;
+    // VALU and transcendental (exp2) operations per MFMA: per value an fma
+    // and an add (dense) or a clamped subtract and two fma (rank test), and
+    // one exp2
+    constexpr int kValuPerMfma = (kSp ? 3 : 2) * 32 / C::kMfmaPerBlock;
     constexpr int kTransPerMfma = 32 / C::kMfmaPerBlock;
     if (m_ok && fast) {
       mfma_block(nxt, nk, nr, nslot);
@@ -321,9 +333,11 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
       for (int m = 0; m < C::kMfmaPerBlock; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
-        if constexpr (!kSp) __builtin_amdgcn_sched_group_barrier(0x400, kTransPerMfma, 0);
+        __builtin_amdgcn_sched_group_barrier(0x400, kTransPerMfma, 0);
         if ((m & 1) == 1 && m < 2 * C::kKSteps - 2)
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (kSp && m == C::kKSteps - 1)  // the next block's four rank reads
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
       }
     } else {
       if (m_ok) mfma_block(nxt, nk, nr, nslot);
