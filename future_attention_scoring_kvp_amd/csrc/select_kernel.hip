@@ -7,16 +7,22 @@
 // (e.g. the log targets, which are negative).  Ranking: score descending,
 // equal scores by ascending index.
 //
-// One workgroup (256 threads) per (batch, KV head) row:
+// One workgroup per (batch, KV head) row, in two steps:
 //   1. radix select, most significant byte first, on an order-preserving
 //      32-bit key of each fp32 score (any sign; see score_key): four passes of a
 //      256-bin LDS histogram over the candidates that match the bytes fixed
 //      so far give the k-th largest value T exactly and the number r of
 //      copies of T that belong to the top-k (the r lowest-indexed ones);
-//   2. one ordered sweep over the row in chunks of 256 positions: per chunk,
-//      wave ballots plus a 4-wave LDS scan give every kept position its
-//      output slot and every copy of T its tie rank, so the output is written
-//      ascending with no sort.
+//   2. ordered emission: position j is kept iff it is a sink or in the
+//      window, or its key is above T, or it is among the first r copies of T;
+//      its output slot is the number of kept positions before it, so the
+//      output is ascending with no sort.
+// Rows of up to 32768 scores (select_reg_kernel, 1024 threads): each thread
+// holds KPT consecutive keys in registers, so the row is read from memory
+// once; the passes histogram from registers into per-wave LDS copies, and
+// one block-wide scan of (kept, tie) counts places every kept position.
+// Longer rows (select_kernel, 256 threads) re-read the row from memory per
+// pass and emit in chunks of 256 positions with a ballot scan per chunk.
 #include "kvp_device.h"
 #include "kvp_launch.h"
 
@@ -142,6 +148,210 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelArgs a) {
   }
 }
 
+
+// ---- rows of up to kRegThreads * KPT scores: keys held in registers
+
+constexpr int kRegThreads = 1024;
+constexpr int kRegWaves = kRegThreads / kWave;
+
+template <int KPT>
+__global__ __launch_bounds__(kRegThreads) void select_reg_kernel(SelArgs a, bool vec4) {
+  static_assert(KPT % 4 == 0 && KPT <= 32 && kRegThreads * KPT <= 32768,
+                "packed 16-bit counts need rows of at most 32768 scores");
+  constexpr int kChunks = KPT / 4;               // chunks of 4 * kRegThreads positions
+  constexpr int kChunkLen = 4 * kRegThreads;
+  __shared__ __attribute__((aligned(16))) int hist[kRegWaves][256];  // per-wave copies: fewer colliding atomics
+  __shared__ uint32_t wave_sum[kChunks][kRegWaves];
+  __shared__ uint32_t sel_digit;
+  __shared__ int sel_above;
+  __shared__ int32_t out_lds[kRegThreads * KPT];  // the row's keep list, written out coalesced
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int S = a.S;
+  const float* __restrict__ m = a.mass + (size_t)blockIdx.x * S;
+  int32_t* __restrict__ out = a.keep + (size_t)blockIdx.x * a.n_keep;
+
+  const int e_lo = a.n_sink;                 // eligible range [e_lo, e_hi)
+  const int e_hi = S - a.window;             // may be <= e_lo (empty)
+  const int n_elig = e_hi > e_lo ? e_hi - e_lo : 0;
+  const int kk = a.top_k < n_elig ? a.top_k : n_elig;
+  const bool take_all = kk == n_elig;
+
+  // Element e of this thread is position pos(e): chunk e / 4, four
+  // consecutive positions per thread within a chunk, so every load
+  // instruction of a wave reads 1 KB of consecutive scores.  Positions >= S
+  // hold key 0 and take part in nothing.
+  auto pos = [&](int e) __attribute__((always_inline)) {
+    return (e >> 2) * kChunkLen + 4 * tid + (e & 3);
+  };
+  uint32_t key[KPT];
+  if (vec4) {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int j = c * kChunkLen + 4 * tid;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j < S) v = *reinterpret_cast<const float4*>(m + j);  // S % 4 == 0
+      key[4 * c] = score_key(v.x);
+      key[4 * c + 1] = score_key(v.y);
+      key[4 * c + 2] = score_key(v.z);
+      key[4 * c + 3] = score_key(v.w);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) key[e] = pos(e) < S ? score_key(m[pos(e)]) : 0u;
+  }
+
+  // --- 1. threshold T and tie count r (only when 0 < kk < n_elig)
+  uint32_t prefix = 0, pmask = 0;
+  int r = kk;
+  if (!take_all && kk > 0) {
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      for (int i = tid; i < kRegWaves * 256; i += kRegThreads) (&hist[0][0])[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < KPT; ++e) {
+        const int j = pos(e);
+        if (j >= e_lo && j < e_hi && (key[e] & pmask) == prefix)
+          atomicAdd(&hist[wave][(key[e] >> shift) & 255u], 1);
+      }
+      __syncthreads();
+      if (tid < 256) {  // merge the wave copies into copy 0 (column tid is this thread's)
+        int t = 0;
+#pragma unroll
+        for (int w = 0; w < kRegWaves; ++w) t += hist[w][tid];
+        hist[0][tid] = t;
+      }
+      __syncthreads();
+      if (wave == 0) {
+        // lane l owns bins 4l .. 4l + 3; counts from the top bin down
+        const int4 c4 = *reinterpret_cast<const int4*>(&hist[0][4 * lane]);
+        const int c[4] = {c4.x, c4.y, c4.z, c4.w};
+        const int own = c[0] + c[1] + c[2] + c[3];
+        int suf = own;  // candidates in bins >= 4 lane
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+          const int o = __shfl_down(suf, off);
+          if (lane + off < kWave) suf += o;
+        }
+        const int above = suf - own;  // candidates in bins > 4 lane + 3
+        // the digit d is the largest with (count in bins > d) < r <= (count
+        // in bins >= d); exactly one lane holds it (r >= 1, total >= r)
+        if (above < r && r <= suf) {
+          int acc = above, d = 4 * lane + 3;
+#pragma unroll
+          for (int i = 3; i > 0; --i) {
+            if (acc + c[i] >= r) break;
+            acc += c[i];
+            --d;
+          }
+          sel_digit = (uint32_t)d;
+          sel_above = acc;
+        }
+      }
+      __syncthreads();
+      prefix |= sel_digit << shift;
+      pmask |= 255u << shift;
+      r -= sel_above;
+    }
+  }
+  const uint32_t T = prefix;
+
+  // --- 2. ordered emission.  Per position: forced-or-above (sink, window,
+  // key > T, or every eligible one when all are taken) or a tie (key == T),
+  // as one bit each.  Kept before position j = (forced-or-above before j) +
+  // min(ties before j, r).
+  uint32_t fa_bits = 0, tie_bits = 0;
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    const int j = pos(e);
+    bool fa = false, tie = false;
+    if (j < S) {
+      if (j < a.n_sink || j >= e_hi) {
+        fa = true;
+      } else if (kk > 0) {
+        fa = take_all || key[e] > T;
+        tie = !take_all && key[e] == T;
+      }
+    }
+    fa_bits |= (uint32_t)fa << e;
+    tie_bits |= (uint32_t)tie << e;
+  }
+  // Counts before each (chunk, thread) in position order: per chunk, an
+  // in-wave inclusive scan of (forced-or-above << 16 | ties), unsigned (row
+  // totals of either count are at most 32768, so the tie half never
+  // carries); then one wave turns the (chunk, wave) totals into exclusive
+  // offsets.
+  uint32_t packed[kChunks], incl[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const uint32_t nib = 0xFu << (4 * c);
+    packed[c] = ((uint32_t)__popc(fa_bits & nib) << 16) | (uint32_t)__popc(tie_bits & nib);
+    uint32_t x = packed[c];
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const uint32_t o = __shfl_up(x, off);
+      if (lane >= off) x += o;
+    }
+    incl[c] = x;
+    if (lane == kWave - 1) wave_sum[c][wave] = x;
+  }
+  __syncthreads();
+  constexpr int kTot = kChunks * kRegWaves;  // <= 128 (chunk, wave) totals
+  static_assert(kTot <= 2 * kWave, "one wave scans the totals, two per lane");
+  uint32_t total = 0;
+  if (wave == 0) {
+    uint32_t* flat = &wave_sum[0][0];
+    const uint32_t v0 = 2 * lane < kTot ? flat[2 * lane] : 0u;
+    const uint32_t v1 = 2 * lane + 1 < kTot ? flat[2 * lane + 1] : 0u;
+    uint32_t x = v0 + v1;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const uint32_t o = __shfl_up(x, off);
+      if (lane >= off) x += o;
+    }
+    const uint32_t ex = x - v0 - v1;
+    if (2 * lane < kTot) flat[2 * lane] = ex;
+    if (2 * lane + 1 < kTot) flat[2 * lane + 1] = ex + v0;
+  }
+  __syncthreads();
+  // kept positions in the row: forced-or-above + min(ties, r), from the last
+  // (chunk, wave) offset plus that wave's totals
+  {
+    const uint32_t last = wave_sum[kChunks - 1][kRegWaves - 1];
+    const uint32_t t = __shfl(incl[kChunks - 1], kWave - 1);
+    total = wave == kRegWaves - 1 ? last + t : 0u;
+  }
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const uint32_t base = wave_sum[c][wave] + incl[c] - packed[c];
+    int fa_before = (int)(base >> 16);
+    int tie_before = (int)(base & 0xFFFFu);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = 4 * c + q;
+      const bool fa = (fa_bits >> e) & 1u;
+      const bool tie = (tie_bits >> e) & 1u;
+      if (fa || (tie && tie_before < r)) {
+        const int slot = fa_before + min(tie_before, r);
+        if (slot < a.n_keep) out_lds[slot] = pos(e);
+      }
+      fa_before += fa;
+      tie_before += tie;
+    }
+  }
+  // the last wave knows the row's kept count; publish it through sel_above
+  if (wave == kRegWaves - 1 && lane == 0) {
+    const int n_fa = (int)(total >> 16), n_tie = (int)(total & 0xFFFFu);
+    sel_above = n_fa + min(n_tie, r);
+  }
+  __syncthreads();
+  const int n_out = min((int64_t)sel_above, a.n_keep);
+  for (int i = tid; i < n_out; i += kRegThreads) out[i] = out_lds[i];
+}
+
 }  // namespace
 
 hipError_t launch_select(const float* mass, int64_t rows, int S, int window, int n_sink,
@@ -154,7 +364,17 @@ hipError_t launch_select(const float* mass, int64_t rows, int S, int window, int
   a.n_sink = n_sink;
   a.top_k = top_k;
   a.n_keep = n_keep;
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)rows), dim3(kSelThreads), 0, stream, a);
+  // 16-byte loads when every row starts 16-byte aligned
+  const bool vec4 = S % 4 == 0 && reinterpret_cast<uintptr_t>(mass) % 16 == 0;
+  const dim3 grid((unsigned)rows), reg_block(kRegThreads);
+  if (S <= kRegThreads * 8)
+    hipLaunchKernelGGL(select_reg_kernel<8>, grid, reg_block, 0, stream, a, vec4);
+  else if (S <= kRegThreads * 16)
+    hipLaunchKernelGGL(select_reg_kernel<16>, grid, reg_block, 0, stream, a, vec4);
+  else if (S <= kRegThreads * 32)
+    hipLaunchKernelGGL(select_reg_kernel<32>, grid, reg_block, 0, stream, a, vec4);
+  else
+    hipLaunchKernelGGL(select_kernel, grid, dim3(kSelThreads), 0, stream, a);
   return hipGetLastError();
 }
 
