@@ -119,6 +119,32 @@ def test_select_exact_with_ties():
         assert np.array_equal(keep, ref)
 
 
+def test_select_row_lengths_and_alignment():
+    """Every row-length path of the selection (8, 16 or 32 scores per thread
+    up to 32768, the long-row kernel beyond), on both sides of each bound, with
+    rows that are or are not 16-byte aligned, mixed-sign scores with ties,
+    and more rows than compute units: bit-exact against the oracle's sort."""
+    rng = np.random.default_rng(17)
+    for S in (8192, 8193, 16384, 16385, 32767, 32768, 32769):
+        w, s, k = 64, 4, S // 3
+        rows = 3
+        m = (np.round(rng.standard_normal((rows, S)) * 8) / 8).astype(np.float32)  # signed, with ties
+        ref = oracle.select(m.reshape(rows, 1, S).astype(np.float64), w, s, k)
+        for offset in (0, 1):  # offset 1: the rows start 4 bytes past a 16-byte boundary
+            say(f"[parity] select rows S={S} offset={offset}")
+            buf = torch.zeros(rows * S + offset, dtype=torch.float32, device="cuda")
+            buf[offset:] = torch.from_numpy(m.reshape(-1)).cuda()
+            dev = buf[offset:].view(rows, 1, S)
+            keep = kvp.select_topk(dev, w, s, k).cpu().numpy()
+            assert np.array_equal(keep, ref), (S, offset)
+    # 300 rows (more than one round of workgroups), rank-like scores
+    S, w, s, k = 4096, 128, 4, 1000
+    m = (rng.random((300, 1, S)) ** 8 * 50).astype(np.float32)
+    say("[parity] select 300 rows S=4096")
+    keep = kvp.select_topk(torch.from_numpy(m).cuda(), w, s, k).cpu().numpy()
+    assert np.array_equal(keep, oracle.select(m.astype(np.float64), w, s, k))
+
+
 def test_select_zero_and_denormal_masses():
     S = 3000
     m = np.zeros((1, 1, S), np.float32)
