@@ -22,6 +22,10 @@ def scores(kind, rows, n, seed):
         v = np.log(1e-6 + rng.random((rows, n)) ** 6)
     elif kind == "ties":
         v = np.round(rng.standard_normal((rows, n)) * 2) / 2
+    elif kind == "equal":
+        v = np.full((rows, n), 1.25)
+    elif kind == "gap":  # two clusters 1000 apart: exponentials across the gap underflow
+        v = rng.standard_normal((rows, n)) + np.where(np.arange(n) % 2 == 0, -500.0, 500.0)
     else:
         raise ValueError(kind)
     return v.astype(np.float32)
@@ -47,6 +51,9 @@ def check_fwd(x32, k, tau):
     ("normal", 4, 100, 10.0, 1.0), ("normal", 3, 777, 123.4, 0.5), ("logmass", 2, 4096, 2048.0, 1.0),
     ("ties", 3, 500, 50.0, 1.0), ("normal", 2, 64, 0.3, 1.0), ("normal", 2, 64, 63.7, 1.0),
     ("normal", 2, 300, 30.0, 0.01), ("normal", 5, 1, 0.5, 1.0), ("normal", 2, 2, 1.0, 1.0),
+    ("equal", 2, 300, 100.0, 1.0), ("equal", 2, 300, 150.0, 1.0), ("equal", 2, 300, 250.0, 1.0),
+    ("gap", 2, 1000, 500.0, 0.01), ("gap", 2, 1000, 300.0, 0.1), ("gap", 2, 1000, 700.0, 1.0),
+    ("normal", 2, 40000, 20000.0, 1.0), ("gap", 2, 40000, 20000.0, 0.01),
 ])
 def test_soft_topk_forward(kind, rows, n, k, tau):
     check_fwd(scores(kind, rows, n, n + rows), k, tau)
