@@ -262,8 +262,10 @@ kvp_status kvp_block_future_scores(const void* q, const void* k, const float* ls
  *         (k <= 0 gives y = 0, lam = +inf; k >= n gives y = 1, lam = -inf).
  *   tau : temperature > 0.
  *   y   : device fp32 [rows, n];  lam : device fp32 [rows] (units of z) or NULL.
- * Computed in fp64 per row (no sort: the split is found by bisection on the
- * scores' bit patterns, at most 32 reductions); x must be finite. */
+ * No sort: rows of n <= 32768 bracket the split with an fp32 Newton search
+ * and confirm it, and form the sums and y, in fp64; longer rows find it by
+ * bisection on the scores' bit patterns (at most 32 fp64 reductions).  x
+ * must be finite. */
 kvp_status kvp_soft_topk_fwd(const float* x, int64_t rows, int32_t n, const float* k, float tau,
                              float* y, float* lam, hipStream_t stream);
 
