@@ -21,7 +21,8 @@
 //                  ranked below the cutoff moves it down to the next rank
 //                  whose token is already eligible (pos[r] <= q - w).  Ranks
 //                  and positions are read 64 at a time into lanes and consumed
-//                  with uniform control flow.
+//                  with uniform control flow; when k << n the walks are long
+//                  and test 64 ranks per ballot.
 #include "kvp_device.h"
 #include "kvp_launch.h"
 
@@ -168,6 +169,7 @@ constexpr int kChunk = 1024;  // queries swept by one wave
 // order whose token pos[r] <= q0 - 1 - w, counted 64 ranks at a time with
 // ballots.  The chunk then runs the sequential update: a new token ranked
 // below the cutoff moves it down to the next rank whose token is eligible.
+template <bool kWindowWalk>
 __global__ __launch_bounds__(256) void cutoff_kernel(CutoffArgs a, int rows, int n_chunks) {
   // wave-uniform state lives in scalar registers (readfirstlane tells the
   // compiler so), and the sweep's branches are scalar
@@ -227,8 +229,15 @@ __global__ __launch_bounds__(256) void cutoff_kernel(CutoffArgs a, int rows, int
     }
   }
 
-  int pchunk = 1 << 30;  // start of the positions held in lanes (none yet)
-  uint32_t plane = 0;
+  // Positions of the ranks [pchunk, pchunk + 64) are held in lanes; the
+  // window walk also loads the window below ahead of use.  Ranks outside
+  // [0, n) hold 0 and are never tested.
+  auto load_win = [&](int base) __attribute__((always_inline)) {
+    const int r = base + lane;
+    return (r >= 0 && r < n) ? pos[r] : 0u;
+  };
+  int pchunk = 1 << 30, pnext_base = -(1 << 30);  // no window yet
+  uint32_t plane = 0, pnext = 0;
   for (int q0 = q_begin; q0 < q_end; q0 += 64) {
     // ranks of the tokens that enter at q0 .. q0 + 63 (t = q - w), -2 if none
     const int t_l = q0 + lane - w;
@@ -243,18 +252,50 @@ __global__ __launch_bounds__(256) void cutoff_kernel(CutoffArgs a, int rows, int
         if (eligible <= k) {
           tau = max(tau, r_new);
         } else if (r_new < tau) {
-          // next lower rank whose token is already eligible (pos <= q - w);
-          // the new token itself qualifies, so the walk ends at r_new at the
-          // latest (also the loop bound)
-          for (;;) {
-            --tau;
-            if (tau <= r_new) break;
-            if (tau < pchunk) {
-              pchunk = max(0, tau - 63);
-              plane = (pchunk + lane < n) ? pos[pchunk + lane] : 0u;
+          // The new cutoff: the largest rank in (r_new, tau) whose token is
+          // already eligible (pos <= q - w), else r_new itself (the new token
+          // qualifies).
+          if constexpr (kWindowWalk) {
+            // long walks (k << n): 64 ranks per ballot, from the top window
+            // down
+            int hi_r = tau, result = r_new;
+            for (;;) {
+              const int want = hi_r - 1;  // highest untested rank
+              if (want <= r_new) break;
+              if (want < pchunk || want >= pchunk + 64) {
+                if (want >= pnext_base && want < pnext_base + 64) {  // the window loaded ahead
+                  pchunk = pnext_base;
+                  plane = pnext;
+                } else {  // place the window to end at want
+                  pchunk = max(0, want - 63);
+                  plane = load_win(pchunk);
+                }
+                pnext_base = pchunk - 64;
+                pnext = load_win(pnext_base);
+              }
+              const int r = pchunk + lane;
+              const uint64_t hit = __ballot(r > r_new && r < hi_r && r < n && (int)plane <= q - w);
+              if (hit) {
+                result = pchunk + 63 - (int)__builtin_clzll(hit);
+                break;
+              }
+              hi_r = pchunk;  // nothing in [pchunk, hi_r)
+              if (pchunk <= 0) break;
             }
-            const int p = (int)__builtin_amdgcn_readlane((int)plane, tau - pchunk);
-            if (p <= q - w) break;
+            tau = result;
+          } else {
+            // short walks: rank by rank; the walk ends at r_new at the latest
+            // (also the loop bound)
+            for (;;) {
+              --tau;
+              if (tau <= r_new) break;
+              if (tau < pchunk) {
+                pchunk = max(0, tau - 63);
+                plane = load_win(pchunk);
+              }
+              const int p = (int)__builtin_amdgcn_readlane((int)plane, tau - pchunk);
+              if (p <= q - w) break;
+            }
           }
         }
       }
@@ -289,8 +330,15 @@ hipError_t launch_cutoff(const float* score, int64_t rows, int S, int window, in
   if (err != hipSuccess) return err;
   const int n_chunks = (S + kChunk - 1) / kChunk;
   const int64_t waves = rows * n_chunks;
-  hipLaunchKernelGGL(cutoff_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a,
-                     (int)rows, n_chunks);
+  // The walk from one cutoff to the next crosses about n / k ranks per step
+  // once k tokens are eligible: long walks test 64 ranks per ballot, short
+  // ones go rank by rank.
+  const int64_t n = S > n_sink ? (int64_t)S - n_sink : 0;
+  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+  if ((int64_t)top_k * 8 <= n)
+    hipLaunchKernelGGL(cutoff_kernel<true>, grid, block, 0, stream, a, (int)rows, n_chunks);
+  else
+    hipLaunchKernelGGL(cutoff_kernel<false>, grid, block, 0, stream, a, (int)rows, n_chunks);
   return hipGetLastError();
 }
 
