@@ -23,7 +23,6 @@
 // Backward (App. A.2): with f'(u) = e^{-|u|} / 2 and u_i = z_i - lam,
 //   dz_j = f'(u_j) (dy_j - A / B),  A = sum_i dy_i f'(u_i),  B = sum_i f'(u_i),
 //   dx = dz / tau,  dk = A / B.
-#include <type_traits>
 #include <utility>
 
 #include "kvp_device.h"
