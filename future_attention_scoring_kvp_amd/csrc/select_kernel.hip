@@ -160,11 +160,17 @@ __global__ __launch_bounds__(kRegThreads) void select_reg_kernel(SelArgs a, bool
                 "packed 16-bit counts need rows of at most 32768 scores");
   constexpr int kChunks = KPT / 4;               // chunks of 4 * kRegThreads positions
   constexpr int kChunkLen = 4 * kRegThreads;
-  __shared__ __attribute__((aligned(16))) int hist[kRegWaves][256];  // per-wave copies: fewer colliding atomics
+  // Histogram copies per (wave, lane group): lanes of a wave whose keys share
+  // a digit add to kSub different words (different banks), which cuts the
+  // serialised collisions of skewed rows.  They live in the keep-list buffer,
+  // which is free until the emission.
+  constexpr int kSub = KPT / 4;  // 2, 4 or 8 lane groups: exactly the buffer
+  static_assert(kRegWaves * 256 * kSub == kRegThreads * KPT, "histogram copies fill the keep-list buffer");
+  __shared__ __attribute__((aligned(16))) int hist[4][256];  // merged partial counts
   __shared__ uint32_t wave_sum[kChunks][kRegWaves];
   __shared__ uint32_t sel_digit;
   __shared__ int sel_above;
-  __shared__ int32_t out_lds[kRegThreads * KPT];  // the row's keep list, written out coalesced
+  __shared__ __attribute__((aligned(16))) int32_t out_lds[kRegThreads * KPT];  // the row's keep list, written out coalesced
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -209,21 +215,29 @@ __global__ __launch_bounds__(kRegThreads) void select_reg_kernel(SelArgs a, bool
   if (!take_all && kk > 0) {
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
-      for (int i = tid; i < kRegWaves * 256; i += kRegThreads) (&hist[0][0])[i] = 0;
+      int* const sh = out_lds;  // [wave][bin][lane group]
+      for (int i = 4 * tid; i < kRegWaves * 256 * kSub; i += 4 * kRegThreads)
+        *reinterpret_cast<int4*>(sh + i) = make_int4(0, 0, 0, 0);
       __syncthreads();
+      const int sub = lane & (kSub - 1);
 #pragma unroll
       for (int e = 0; e < KPT; ++e) {
         const int j = pos(e);
         if (j >= e_lo && j < e_hi && (key[e] & pmask) == prefix)
-          atomicAdd(&hist[wave][(key[e] >> shift) & 255u], 1);
+          atomicAdd(&sh[(wave * 256 + (int)((key[e] >> shift) & 255u)) * kSub + sub], 1);
       }
       __syncthreads();
-      if (tid < 256) {  // merge the wave copies into copy 0 (column tid is this thread's)
+      {  // merge: thread t adds the copies of bin t % 256 from a quarter of the waves
+        const int bin = tid & 255, part = tid >> 8;
         int t = 0;
 #pragma unroll
-        for (int w = 0; w < kRegWaves; ++w) t += hist[w][tid];
-        hist[0][tid] = t;
+        for (int w = 4 * part; w < 4 * part + 4; ++w)
+#pragma unroll
+          for (int u = 0; u < kSub; ++u) t += sh[(w * 256 + bin) * kSub + u];
+        hist[part][bin] = t;
       }
+      __syncthreads();
+      if (tid < 256) hist[0][tid] += hist[1][tid] + hist[2][tid] + hist[3][tid];  // its own column
       __syncthreads();
       if (wave == 0) {
         // lane l owns bins 4l .. 4l + 3; counts from the top bin down
