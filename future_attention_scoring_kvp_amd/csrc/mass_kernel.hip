@@ -79,6 +79,9 @@ struct MassArgs {
   int head_split;  // 1, or 2: the G heads of a group in two halves, each added
                    // into the zeroed output by an atomic (two terms: the sum
                    // does not depend on their order)
+  int n_tiles;     // key tiles per unit (paired mode: block x sweeps key tiles
+                   // x' and n_tiles - 1 - x' of its unit, x' the tile index
+                   // xcd_map gives)
   float c;       // scale * log2(e)
   // query-block mode: blocks [seg_start + t seg_len, ...) clipped to S, both
   // multiples of 32; per block the mean over its rows and the unit's heads
@@ -112,7 +115,7 @@ __device__ __forceinline__ float reduce_columns(f32x16_t& x, int l32) {
   return x[0] + __shfl_xor(x[0], 1);
 }
 
-template <int D, typename T, int W, bool kSeg>
+template <int D, typename T, int W, bool kSeg, bool kPair>
 __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
   using C = MassCfg<D, W>;
   __shared__ __attribute__((aligned(1024))) unsigned char q_lds0[C::kStageBytes];
@@ -135,12 +138,25 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
   const int ho = unit - b * n_heads_out;                  // output row within the batch
   const int h = a.per_head ? ho / a.G : ho;               // KV head
   const int g0 = a.per_head ? ho : ho * a.G + part * G;   // first query head swept
-  const int tid = threadIdx.x;
+  // Paired mode: the workgroup sweeps key tile `tile` and then tile
+  // n_tiles - 1 - tile of the same unit.  The two add up to the same work for
+  // every workgroup (a long and a short column band of the triangle), so the
+  // grid needs no second round whose start depends on the order in which the
+  // hardware hands out workgroups.
+  const int tile_last = kPair ? a.n_tiles - 1 - tile : tile;
+  const int n_rep = tile_last != tile ? 2 : 1;
+  for (int rep = 0; rep < n_rep; ++rep) {
+  // the previous tile's column reduction has read the stage buffers
+  if (rep) __syncthreads();
+  // lane indices are re-derived per tile from an opaque copy of the thread
+  // id, so that nothing computed from them stays live across both tiles
+  int tid = threadIdx.x;
+  if constexpr (kPair) asm volatile("" : "+v"(tid));
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;  // query column / key row within a 32-block
   const int h32 = lane >> 5;  // which 8-element half of a 16-wide slice of d
-  const int tile_key0 = tile * C::kKeysPerWG;
+  const int tile_key0 = (rep ? tile_last : tile) * C::kKeysPerWG;
   const int key0 = tile_key0 + wave * C::kKeysPerWave;
 
   const T* __restrict__ kbase = static_cast<const T*>(a.k) + (size_t)(b * a.Hkv + h) * S * D;
@@ -429,6 +445,7 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
     else
       *dst = tot;
   }
+  }  // tiles of the workgroup
 }
 
 __global__ __launch_bounds__(256) void zero_fill_kernel(float* p, int64_t n) {
@@ -461,14 +478,31 @@ hipError_t launch_mass_w(const void* q, const void* k, const float* lse, const S
   a.seg_block = seg.block;
   a.seg_future = seg.future;
   const int64_t n_tiles = (sh.S + C::kKeysPerWG - 1) / C::kKeysPerWG;
-  const int64_t blocks = n_tiles * (int64_t)sh.B * (per_head ? sh.Hq : sh.Hkv) * split;
+  const int64_t units = (int64_t)sh.B * (per_head ? sh.Hq : sh.Hkv) * split;
+  a.n_tiles = (int)n_tiles;
+  // One-workgroup-per-CU grids pair each long key tile with a short one when
+  // the equal-work pairs fill whole rounds of the CUs (at least 95%).
+  bool pair = false;
+  if (W == 8 && !kSeg && n_tiles >= 2) {
+    const int64_t pairs = units * ((n_tiles + 1) / 2);
+    const int64_t rounds = (pairs + kNumCUs - 1) / kNumCUs;
+    pair = pairs * 20 >= rounds * kNumCUs * 19;
+  }
+  const int64_t blocks = units * (pair ? (n_tiles + 1) / 2 : n_tiles);
   if (split > 1) {
     const int64_t n = (int64_t)sh.B * sh.Hkv * sh.S;
     const int64_t fill_blocks = min((n + 255) / 256, (int64_t)4 * kNumCUs);
     hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)fill_blocks), dim3(256), 0, stream, mass, n);
   }
-  hipLaunchKernelGGL((mass_kernel<D, T, W, kSeg>), dim3((unsigned)blocks), dim3(C::kThreads), 0,
-                     stream, a);
+  if constexpr (W == 8 && !kSeg) {
+    if (pair) {
+      hipLaunchKernelGGL((mass_kernel<D, T, W, kSeg, true>), dim3((unsigned)blocks),
+                         dim3(C::kThreads), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((mass_kernel<D, T, W, kSeg, false>), dim3((unsigned)blocks),
+                     dim3(C::kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
