@@ -64,7 +64,9 @@ struct LseArgs {
   const void* k;
   float* lse;
   int B, Hq, Hkv, S, G;
-  int n_wg;  // workgroups per (batch, KV head)
+  int n_wg;  // tiles of 8 (or 4) waves per (batch, KV head); paired mode:
+             // block x takes tiles x' and n_wg - 1 - x' of its unit (x' the
+             // tile index xcd_map gives)
   float c;   // scale * log2(e)
   // sparse mode (running top-k pattern): key j counts for query i iff
   // j <= i and (i - j < window or rank[j] <= cutoff[i]); [B, Hkv, S] each
@@ -89,7 +91,7 @@ struct LTile<true> {
   }
 };
 
-template <int D, typename T, int W, bool kSp>
+template <int D, typename T, int W, bool kSp, bool kPair>
 __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
   using C = LseCfg<D, W>;
   using Tile = LTile<kSp>;
@@ -104,7 +106,18 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
   xcd_map(blockIdx.x, a.B * a.Hkv, unit, tile);
   const int b = unit / a.Hkv;
   const int h = unit - b * a.Hkv;
-  const int tid = threadIdx.x;
+  // Paired mode: the workgroup takes tile `tile` and then tile n_wg - 1 -
+  // tile of the same unit, the longest rows with the shortest, so every
+  // workgroup of the grid has the same work.
+  const int tile_last = kPair ? a.n_wg - 1 - tile : tile;
+  const int n_rep = tile_last != tile ? 2 : 1;
+  for (int rep = 0; rep < n_rep; ++rep) {
+  // the previous tile's last stage has read the stage buffers
+  if (rep) __syncthreads();
+  // lane indices are re-derived per tile from an opaque copy of the thread
+  // id, so that nothing computed from them stays live across both tiles
+  int tid = threadIdx.x;
+  if constexpr (kPair) asm volatile("" : "+v"(tid));
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
@@ -114,7 +127,7 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
   // (the longest rows).
   const int n_pb = (S + C::kQueriesPerWave - 1) / C::kQueriesPerWave;
   const int n_pairs = n_pb * G;
-  const int pair0 = (a.n_wg - 1 - tile) * C::kWaves;
+  const int pair0 = (a.n_wg - 1 - (rep ? tile_last : tile)) * C::kWaves;
   const int my_pair = pair0 + wave;
   const bool active = my_pair < n_pairs;
   const int pb = my_pair / G;
@@ -420,6 +433,7 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
     if (iq0 < S) out[iq0] = ok0 ? l0 : __builtin_inff();
     if (iq1 < S) out[iq1] = ok1 ? l1 : __builtin_inff();
   }
+  }  // tiles of the workgroup
 }
 
 // Exact recomputation of the rows flagged +inf (or NaN) by lse_kernel: one
@@ -511,9 +525,28 @@ hipError_t launch_lse_w(const void* q, const void* k, const Shape& sh, float sca
   a.c = scale * kLog2e;
   const int64_t n_pb = (sh.S + C::kQueriesPerWave - 1) / C::kQueriesPerWave;
   a.n_wg = (int)((n_pb * sh.G + C::kWaves - 1) / C::kWaves);
-  const int64_t blocks = (int64_t)a.n_wg * sh.B * sh.Hkv;
-  hipLaunchKernelGGL((lse_kernel<D, T, W, kSp>), dim3((unsigned)blocks), dim3(C::kThreads), 0,
-                     stream, a);
+  const int64_t units = (int64_t)sh.B * sh.Hkv;
+  // One-workgroup-per-CU grids pair the tile of the longest rows with the
+  // tile of the shortest when the equal-work pairs fill whole rounds of the
+  // CUs (at least 95%).
+  bool pair = false;
+  if (W == 8 && a.n_wg >= 2) {
+    const int64_t pairs = units * ((a.n_wg + 1) / 2);
+    const int64_t rounds = (pairs + kNumCUs - 1) / kNumCUs;
+    pair = pairs * 20 >= rounds * kNumCUs * 19;
+  }
+  const int64_t blocks = units * (pair ? (a.n_wg + 1) / 2 : a.n_wg);
+  if constexpr (W == 8) {
+    if (pair)
+      hipLaunchKernelGGL((lse_kernel<D, T, W, kSp, true>), dim3((unsigned)blocks),
+                         dim3(C::kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((lse_kernel<D, T, W, kSp, false>), dim3((unsigned)blocks),
+                         dim3(C::kThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((lse_kernel<D, T, W, kSp, false>), dim3((unsigned)blocks),
+                       dim3(C::kThreads), 0, stream, a);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t rows = (int64_t)sh.B * sh.Hq * sh.S;
