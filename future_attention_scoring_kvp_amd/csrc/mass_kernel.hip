@@ -237,24 +237,35 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
       }
     };
     const int n_stages = (n_pairs + C::kSlots - 1) / C::kSlots;
-    // Pair p is (query block qb_hi - p / G, head p % G).  For this wave,
-    // pairs [p_full_lo, p_full) see every key with every query (no mask),
-    // the other pairs below p_end need the mask, pairs >= p_end see nothing.
-    // A partial last block (rows >= S) is masked too.
-    const int p_full_lo = (S % kBlk) ? G : 0;
+    // Pair p is (query block qb_of(p), head p % G).  The query blocks are
+    // swept from the last one down, except in the second tile of a paired
+    // workgroup, which sweeps them upwards from the first block it sees: the
+    // second tiles of all workgroups start at staggered times, and sweeping
+    // upwards puts all of them on the same query rows at the same time
+    // (shared L2), as the first tiles are while they sweep down.
+    const bool asc = kPair && rep == 1;
+    const int qb_step = asc ? 1 : -1;
+    const int qb_first = asc ? qb_lo : qb_hi;
+    // For this wave, pairs [p_vis_lo, p_vis_hi) see at least one query;
+    // those in [p_full_lo, p_full_hi) see every key with every query (no
+    // mask), the others need the mask.  A partial last block (rows >= S) is
+    // masked too.
+    const int p_part = (S % kBlk) ? G : 0;
     const int qb_full = (key0 + C::kKeysPerWave - 1 + w + kBlk - 1) / kBlk;
-    const int p_full = max(0, min(n_pairs, (qb_hi - qb_full + 1) * G));
     const int qb_min = (key0 + w) / kBlk;  // first block with a query i >= key0 + w
-    const int p_end = max(0, min(n_pairs, (qb_hi - qb_min + 1) * G));
+    const int p_vis_lo = asc ? min(n_pairs, (qb_min - qb_lo) * G) : 0;
+    const int p_vis_hi = asc ? n_pairs : max(0, min(n_pairs, (qb_hi - qb_min + 1) * G));
+    const int p_full_lo = asc ? min(n_pairs, (qb_full - qb_lo) * G) : p_part;
+    const int p_full_hi = asc ? n_pairs - p_part : max(0, min(n_pairs, (qb_hi - qb_full + 1) * G));
 
     // ---- staging: this wave copies pair 4 * st + wave of stage st
-    int ld_qb = qb_hi - wave / G;
+    int ld_qb = qb_first + qb_step * (wave / G);
     int ld_g = wave % G;
     auto advance = [&](int& qb, int& g) __attribute__((always_inline)) {
       g += C::kSlots;
       while (g >= G) {
         g -= G;
-        --qb;
+        qb += qb_step;
       }
     };
     // Copies go HBM -> VGPR -> LDS in two halves of the d slices, so that
@@ -313,7 +324,7 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
     auto exp_masked = [&](const Tile& t, int p) __attribute__((always_inline)) {
       // query i counts for key j = key0 + 32 b + 8 (v / 4) + 4 h32 + v % 4 iff
       // i >= j + w, i.e. iff the constant 8 (v / 4) + v % 4 <= lim - 32 b
-      const int lim = (qb_hi - p / G) * kBlk + l32 - key0 - w - 4 * h32;
+      const int lim = (qb_first + qb_step * (p / G)) * kBlk + l32 - key0 - w - 4 * h32;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = 8 * (v >> 2) + (v & 3);
@@ -326,8 +337,8 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
     // Exponentials of pair p (in cur) and MFMAs of pair p + 1 (into nxt).
     auto step = [&](Tile& cur, Tile& nxt, int p, const unsigned char* nq, const float* nl,
                     int nslot) __attribute__((always_inline)) {
-      const bool m_ok = p + 1 < p_end;
-      const bool full = p >= p_full_lo && p < p_full;
+      const bool m_ok = p + 1 >= p_vis_lo && p + 1 < p_vis_hi;
+      const bool full = p >= p_full_lo && p < p_full_hi;
       if (m_ok && full) {
         mfma_pair(nxt, nq, nl, nslot);
         exp_full(cur);
@@ -350,7 +361,7 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
         if (m_ok) mfma_pair(nxt, nq, nl, nslot);
         if (full)
           exp_full(cur);
-        else if (p < p_end)
+        else if (p >= p_vis_lo && p < p_vis_hi)
           exp_masked(cur, p);
       }
     };
@@ -402,7 +413,7 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
     store_half(0, 1, q_lds0);
     finish_loads(0, l_lds0);
     __syncthreads();
-    if (0 < p_end) mfma_pair(t0, q_lds0, l_lds0, 0);
+    if (p_vis_lo <= 0 && 0 < p_vis_hi) mfma_pair(t0, q_lds0, l_lds0, 0);
     for (int st = 0; st < n_stages; st += 2) {
       stage(std::integral_constant<int, 0>{}, st);
       if (st + 1 >= n_stages) break;

@@ -1,0 +1,53 @@
+"""GPU parity for the grids that give each workgroup two tiles: in the mass
+pass a workgroup sweeps key tile m with the query blocks descending and then
+key tile T-1-m with them ascending; in the LSE pass it takes the tile of the
+longest rows and then the tile of the shortest.  These grids are chosen for
+one-workgroup-per-CU launches, so the shapes are Qwen3-4B-sized (32 query /
+8 KV heads, d = 128, S near 32K): an odd number of key tiles (the middle tile
+has no partner), and a sequence that is not a multiple of 32 (a partial last
+query block, masked in both sweep directions).  Two whole units per shape are
+compared with the oracle, for the group sums and the per-head masses; every
+unit is checked through the w = 0 row-sum identity."""
+import numpy as np
+import pytest
+import torch
+
+import future_attention_scoring_kvp_amd as kvp
+import kvp_inputs
+import oracle
+from parity import assert_lse, assert_mass, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("S,w", [
+    (32000, 77),    # 63 key tiles of 512: tile 31 sweeps alone; S % 512 = 256
+    (32749, 300),   # 64 key tiles, the last one partial; S % 32 = 13
+])
+def test_paired_tiles(S, w):
+    wl = kvp_inputs.workload(4).with_(S=S, window=w, seed=4242 + S)
+    say(f"[paired] S={S} w={w}: generating inputs")
+    li = kvp_inputs.make_layer(wl)
+    q, k = to_dev(li.q), to_dev(li.k)
+    say(f"[paired] S={S} w={w}: GPU path")
+    lse = kvp.lse_fwd(q, k)
+    mass = kvp.future_mass(q, k, lse, w)
+    per_head = kvp.future_mass_per_head(q, k, lse, w)
+    total0 = kvp.future_mass(q, k, lse, 0).double().sum(dim=2)
+    torch.cuda.synchronize()
+    lse_h, mass_h, ph_h = lse.cpu().numpy(), mass.cpu().numpy(), per_head.cpu().numpy()
+    G = wl.G
+    assert np.all(mass_h[:, :, S - w:] == 0)
+    # w = 0: every softmax row sums to one, so each KV head's total is G * S
+    np.testing.assert_allclose(total0.cpu().numpy(), G * S, rtol=1e-4)
+    # the group sum is the sum of its heads' masses
+    np.testing.assert_allclose(ph_h.reshape(1, wl.Hkv, G, S).astype(np.float64).sum(axis=2),
+                               mass_h, rtol=1e-5, atol=1e-6)
+    for h in (0, wl.Hkv - 1):
+        say(f"[paired] S={S} w={w}: oracle unit h={h}")
+        ref = oracle.future_mass(li.q, li.k, w, b_only=0, h_only=h, want_per_head=True)
+        g0 = h * G
+        assert_lse(lse_h[0, g0:g0 + G], ref["lse"][0, g0:g0 + G], f"paired S={S} lse h={h}")
+        assert_mass(mass_h[0, h], ref["mass"][0, h], f"paired S={S} mass h={h}")
+        assert_mass(ph_h[0, g0:g0 + G], ref["mass_heads"][0, g0:g0 + G],
+                    f"paired S={S} per-head h={h}")
