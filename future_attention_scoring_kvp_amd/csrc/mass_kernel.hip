@@ -242,8 +242,10 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
     // workgroup, which sweeps them upwards from the first block it sees: the
     // second tiles of all workgroups start at staggered times, and sweeping
     // upwards puts all of them on the same query rows at the same time
-    // (shared L2), as the first tiles are while they sweep down.
-    const bool asc = kPair && rep == 1;
+    // (shared L2), as the first tiles are while they sweep down.  Query-block
+    // mode keeps both tiles descending: its future score is a running
+    // maximum over the blocks after the current one.
+    const bool asc = kPair && !kSeg && rep == 1;
     const int qb_step = asc ? 1 : -1;
     const int qb_first = asc ? qb_lo : qb_hi;
     // For this wave, pairs [p_vis_lo, p_vis_hi) see at least one query;
@@ -425,7 +427,7 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
     // blocks wholly before the first query the tile sees: no attention, and
     // the future score is the maximum of the later blocks
     for (int t = seg_low - 1; t >= 0; --t) write_seg(t, 0.f, 0.f);
-    return;
+    continue;
   }
 
   // Column reduction: each lane holds one query column's partial sums for 32
@@ -494,7 +496,7 @@ hipError_t launch_mass_w(const void* q, const void* k, const float* lse, const S
   // One-workgroup-per-CU grids pair each long key tile with a short one when
   // the equal-work pairs fill whole rounds of the CUs (at least 95%).
   bool pair = false;
-  if (W == 8 && !kSeg && n_tiles >= 2) {
+  if (W == 8 && n_tiles >= 2) {
     const int64_t pairs = units * ((n_tiles + 1) / 2);
     const int64_t rounds = (pairs + kNumCUs - 1) / kNumCUs;
     pair = pairs * 20 >= rounds * kNumCUs * 19;
@@ -505,7 +507,7 @@ hipError_t launch_mass_w(const void* q, const void* k, const float* lse, const S
     const int64_t fill_blocks = min((n + 255) / 256, (int64_t)4 * kNumCUs);
     hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)fill_blocks), dim3(256), 0, stream, mass, n);
   }
-  if constexpr (W == 8 && !kSeg) {
+  if constexpr (W == 8) {
     if (pair) {
       hipLaunchKernelGGL((mass_kernel<D, T, W, kSeg, true>), dim3((unsigned)blocks),
                          dim3(C::kThreads), 0, stream, a);

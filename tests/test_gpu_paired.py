@@ -7,7 +7,11 @@ one-workgroup-per-CU launches, so the shapes are Qwen3-4B-sized (32 query /
 has no partner), and a sequence that is not a multiple of 32 (a partial last
 query block, masked in both sweep directions).  Two whole units per shape are
 compared with the oracle, for the group sums and the per-head masses; every
-unit is checked through the w = 0 row-sum identity."""
+unit is checked through the w = 0 row-sum identity.  The query-block mode
+(Golden-Eviction scores) is checked on the same shapes, group and per head,
+against the oracle-checked masses: with blocks from row 0 the block means
+times their row and head counts add up to the mass, and the future score is
+the running maximum of the block scores from the end (exact)."""
 import numpy as np
 import pytest
 import torch
@@ -43,6 +47,7 @@ def test_paired_tiles(S, w):
     # the group sum is the sum of its heads' masses
     np.testing.assert_allclose(ph_h.reshape(1, wl.Hkv, G, S).astype(np.float64).sum(axis=2),
                                mass_h, rtol=1e-5, atol=1e-6)
+    check_blocks(q, k, lse, S, w, G, mass_h, ph_h, li)
     for h in (0, wl.Hkv - 1):
         say(f"[paired] S={S} w={w}: oracle unit h={h}")
         ref = oracle.future_mass(li.q, li.k, w, b_only=0, h_only=h, want_per_head=True)
@@ -51,3 +56,19 @@ def test_paired_tiles(S, w):
         assert_mass(mass_h[0, h], ref["mass"][0, h], f"paired S={S} mass h={h}")
         assert_mass(ph_h[0, g0:g0 + G], ref["mass_heads"][0, g0:g0 + G],
                     f"paired S={S} per-head h={h}")
+
+
+def check_blocks(q, k, lse, S, w, G, mass_h, ph_h, li):
+    L = 1024                      # blocks [0, 1024), ..., the last one partial
+    n = kvp.block_count(S, 0, L)
+    rows = np.array([min(S, (t + 1) * L) - t * L for t in range(n)], np.float64)
+    for per_head, ref, heads in ((False, mass_h, G), (True, ph_h, 1)):
+        say(f"[paired] S={S} w={w}: block scores per_head={per_head}")
+        blk, fut = kvp.block_future_scores(q, k, lse, 0, L, window=w, per_head=per_head)
+        torch.cuda.synchronize()
+        blk, fut = blk.cpu().numpy(), fut.cpu().numpy()
+        assert blk.shape[2] == n
+        total = (blk.astype(np.float64) * (rows * heads)[None, None, :, None]).sum(axis=2)
+        np.testing.assert_allclose(total, ref, rtol=2e-5, atol=1e-6)
+        suffix = np.maximum.accumulate(blk[:, :, ::-1], axis=2)[:, :, ::-1]
+        assert np.array_equal(fut, suffix), f"future scores S={S} per_head={per_head}"
