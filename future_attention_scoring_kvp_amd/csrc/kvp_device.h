@@ -103,4 +103,23 @@ __device__ __forceinline__ void xcd_map(int bid, int n_units, int& unit, int& ti
   }
 }
 
+// Unit-major variant for grids whose blocks all carry the same work: block
+// `bid` of an XCD takes tile `bid / 8 % n_per_unit` of the XCD's
+// `bid / 8 / n_per_unit`-th unit, so each round of an XCD's CUs covers whole
+// units and every tile of a unit sweeps the unit's rows together (one L2).
+// Falls back to unit-major order over the grid when the unit count is not a
+// multiple of 8.
+__device__ __forceinline__ void xcd_map_units(int bid, int n_units, int n_per_unit, int& unit,
+                                              int& tile) {
+  if ((n_units & 7) == 0) {
+    const int slot = bid >> 3;
+    const int u_local = slot / n_per_unit;
+    tile = slot - u_local * n_per_unit;
+    unit = u_local * 8 + (bid & 7);
+  } else {
+    unit = bid / n_per_unit;
+    tile = bid - unit * n_per_unit;
+  }
+}
+
 }  // namespace kvp

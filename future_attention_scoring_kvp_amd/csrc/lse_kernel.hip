@@ -66,7 +66,7 @@ struct LseArgs {
   int B, Hq, Hkv, S, G;
   int n_wg;  // tiles of 8 (or 4) waves per (batch, KV head); paired mode:
              // block x takes tiles x' and n_wg - 1 - x' of its unit (x' the
-             // tile index xcd_map gives)
+             // tile index the block mapping gives)
   float c;   // scale * log2(e)
   // sparse mode (running top-k pattern): key j counts for query i iff
   // j <= i and (i - j < window or rank[j] <= cutoff[i]); [B, Hkv, S] each
@@ -103,7 +103,12 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
 
   const int S = a.S, G = a.G;
   int unit, tile;
-  xcd_map(blockIdx.x, a.B * a.Hkv, unit, tile);
+  // paired grids carry equal work per block: whole units per round of an
+  // XCD; otherwise longest tiles first
+  if constexpr (kPair)
+    xcd_map_units(blockIdx.x, a.B * a.Hkv, (a.n_wg + 1) / 2, unit, tile);
+  else
+    xcd_map(blockIdx.x, a.B * a.Hkv, unit, tile);
   const int b = unit / a.Hkv;
   const int h = unit - b * a.Hkv;
   // Paired mode: the workgroup takes tile `tile` and then tile n_wg - 1 -

@@ -81,7 +81,7 @@ struct MassArgs {
                    // does not depend on their order)
   int n_tiles;     // key tiles per unit (paired mode: block x sweeps key tiles
                    // x' and n_tiles - 1 - x' of its unit, x' the tile index
-                   // xcd_map gives)
+                   // the block mapping gives)
   float c;       // scale * log2(e)
   // query-block mode: blocks [seg_start + t seg_len, ...) clipped to S, both
   // multiples of 32; per block the mean over its rows and the unit's heads
@@ -131,7 +131,12 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
   const int split = a.head_split;
   const int G = a.per_head ? 1 : a.G / split;  // query heads swept per unit
   int unit, tile;
-  xcd_map(blockIdx.x, a.B * n_heads_out * split, unit, tile);
+  // paired grids carry equal work per block: whole units per round of an
+  // XCD; otherwise longest tiles first
+  if constexpr (kPair)
+    xcd_map_units(blockIdx.x, a.B * n_heads_out * split, (a.n_tiles + 1) / 2, unit, tile);
+  else
+    xcd_map(blockIdx.x, a.B * n_heads_out * split, unit, tile);
   const int part = unit % split;
   unit /= split;
   const int b = unit / n_heads_out;
