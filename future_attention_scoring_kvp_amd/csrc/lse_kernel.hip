@@ -24,7 +24,10 @@
 //   * software pipeline inside each wave: the MFMAs of block p+1 are issued
 //     between the VALU operations of block p;
 //   * every workgroup of a (batch, KV head) walks the same key sequence
-//     (shared L2), and workgroups run longest first.
+//     (shared L2), and workgroups run longest first; in grids of one
+//     workgroup per CU whose tile pairs fill whole rounds of the CUs, each
+//     workgroup takes the tile of the longest rows and then the tile of the
+//     shortest, so every workgroup has the same work.
 // Sparse mode (the running top-k pattern of KVpop §3.2, whose per-query
 // log-normalisers the student returns): key j counts for query i iff j <= i
 // and (i - j < w or rank[j] <= cutoff[i]).  Each staged key block carries its

@@ -35,8 +35,15 @@
 //     fixed order and each key's mass is written once: no atomics, bitwise
 //     reproducible.
 // Blocks are mapped XCD-aware: all tiles of one (batch, KV head) run on the
-// same XCD and sweep the same Q rows in the same order (shared L2), longest
-// tiles first so the triangular work load balances.
+// same XCD and sweep the same Q rows at the same time (shared L2).
+// Grids of one workgroup per CU whose tile pairs fill whole rounds of the CUs
+// give each workgroup two tiles, m and n_tiles - 1 - m (a long and a short
+// band of the triangle: equal work for every workgroup, so no round waits on
+// the order in which the hardware hands out workgroups); the second tile
+// sweeps its query blocks upwards, which keeps the second tiles of all
+// workgroups on the same rows at the same time.  Such grids take whole units
+// per round of an XCD's CUs; other grids run single tiles, longest first, so
+// the triangular work load balances.
 #include <type_traits>
 
 #include "kvp_device.h"
