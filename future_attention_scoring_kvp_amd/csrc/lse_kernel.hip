@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
   }
   int rank_pref = 0;
 
-  // ---- staging: wave w copies key block 4 * st + w of stage st, in halves
+  // ---- staging: wave w copies key block kSlots * st + w of stage st, in halves
   constexpr int kHalf = C::kKSteps / 2;
   u32x4_t stage_regs[kHalf];
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase, head_bytes);

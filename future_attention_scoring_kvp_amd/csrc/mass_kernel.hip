@@ -272,7 +272,7 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
     const int p_full_lo = asc ? min(n_pairs, (qb_full - qb_lo) * G) : p_part;
     const int p_full_hi = asc ? n_pairs - p_part : max(0, min(n_pairs, (qb_hi - qb_full + 1) * G));
 
-    // ---- staging: this wave copies pair 4 * st + wave of stage st
+    // ---- staging: this wave copies pair kSlots * st + wave of stage st
     int ld_qb = qb_first + qb_step * (wave / G);
     int ld_g = wave % G;
     auto advance = [&](int& qb, int& g) __attribute__((always_inline)) {
