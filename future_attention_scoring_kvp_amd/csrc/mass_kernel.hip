@@ -197,6 +197,13 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
   // belongs to a block)
   const int q_first = kSeg ? max(tile_key0 + w, a.seg_start) : tile_key0 + w;
 
+  // The query blocks are swept from the last one down, except in the second
+  // tile of a paired workgroup, which sweeps them upwards from the first block
+  // it sees: the second tiles of all workgroups start at staggered times, and
+  // sweeping upwards puts all of them on the same query rows at the same time
+  // (shared L2), as the first tiles are while they sweep down.
+  const bool asc = kPair && rep == 1;
+
   // query-block mode: per-key running maxima of the blocks flushed so far
   // (block scores are >= 0), the lowest block flushed, and the key rows this
   // lane writes after a column reduction
@@ -220,6 +227,15 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
     buf_store_f32(rf, off0, fmax0);
     buf_store_f32(rf, off0 + 128u, fmax1);
   };
+  // upward sweep: a block's mean is parked in its future row until the
+  // running maximum can be taken from the last block down
+  auto write_raw = [&](int t, float v0, float v1) __attribute__((always_inline)) {
+    if (l32 & 1) return;
+    const __amdgpu_buffer_rsrc_t rf = make_rsrc(a.seg_future + (seg_row0 + t) * S, (uint32_t)S * 4u);
+    const uint32_t off0 = (uint32_t)(key0 + red_row) * 4u;
+    buf_store_f32(rf, off0, v0);
+    buf_store_f32(rf, off0 + 128u, v1);
+  };
   auto flush_seg = [&](int t) __attribute__((always_inline)) {
     const int i0 = a.seg_start + t * a.seg_len;
     const int rows = min(S, i0 + a.seg_len) - i0;
@@ -228,38 +244,35 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
     const float v1 = reduce_columns(acc1, l32) * inv;
     acc0 = f32x16_t{};
     acc1 = f32x16_t{};
-    fmax0 = fmaxf(fmax0, v0);
-    fmax1 = fmaxf(fmax1, v1);
-    write_seg(t, v0, v1);
-    seg_low = t;
+    if (asc) {
+      write_raw(t, v0, v1);
+    } else {
+      fmax0 = fmaxf(fmax0, v0);
+      fmax1 = fmaxf(fmax1, v1);
+      write_seg(t, v0, v1);
+    }
+    seg_low = min(seg_low, t);
   };
 
   if (q_first < S) {
     const int qb_hi = (S - 1) / kBlk;
     const int qb_lo = q_first / kBlk;
     const int n_pairs = (qb_hi - qb_lo + 1) * G;
-    // query-block mode: after the last pair of a block (its first query
-    // block, last head) or the last pair of the sweep, reduce and write
+    // Pair p is (query block qb_first + qb_step * (p / G), head p % G).
+    const int qb_step = asc ? 1 : -1;
+    const int qb_first = asc ? qb_lo : qb_hi;
+    // query-block mode: after the last pair of a block (its last head, and
+    // its first query block going down or its last going up) or the last
+    // pair of the sweep, reduce and write
     auto maybe_flush = [&](int p) __attribute__((always_inline)) {
       if constexpr (kSeg) {
         if (p >= n_pairs) return;
-        const int qrow = (qb_hi - p / G) * kBlk - a.seg_start;
-        if (p == n_pairs - 1 || (p % G == G - 1 && qrow % a.seg_len == 0))
-          flush_seg(qrow / a.seg_len);
+        const int qrow = (qb_first + qb_step * (p / G)) * kBlk - a.seg_start;
+        const bool edge = asc ? (qrow + kBlk) % a.seg_len == 0 : qrow % a.seg_len == 0;
+        if (p == n_pairs - 1 || (p % G == G - 1 && edge)) flush_seg(qrow / a.seg_len);
       }
     };
     const int n_stages = (n_pairs + C::kSlots - 1) / C::kSlots;
-    // Pair p is (query block qb_of(p), head p % G).  The query blocks are
-    // swept from the last one down, except in the second tile of a paired
-    // workgroup, which sweeps them upwards from the first block it sees: the
-    // second tiles of all workgroups start at staggered times, and sweeping
-    // upwards puts all of them on the same query rows at the same time
-    // (shared L2), as the first tiles are while they sweep down.  Query-block
-    // mode keeps both tiles descending: its future score is a running
-    // maximum over the blocks after the current one.
-    const bool asc = kPair && !kSeg && rep == 1;
-    const int qb_step = asc ? 1 : -1;
-    const int qb_first = asc ? qb_lo : qb_hi;
     // For this wave, pairs [p_vis_lo, p_vis_hi) see at least one query;
     // those in [p_full_lo, p_full_hi) see every key with every query (no
     // mask), the others need the mask.  A partial last block (rows >= S) is
@@ -436,6 +449,35 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
   }
 
   if constexpr (kSeg) {
+    if (asc && seg_low < a.n_seg) {
+      // upward sweep: wait for the parked block means, read them back (the
+      // stores have reached L2; this wave never read those lines before) and
+      // write block scores and running maxima from the last block down,
+      // sixteen blocks' loads in flight at a time
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      const uint32_t off0 = (uint32_t)(key0 + red_row) * 4u;
+      constexpr int kBatch = 16;
+      for (int t_hi = a.n_seg - 1; t_hi >= seg_low; t_hi -= kBatch) {
+        float p0[kBatch], p1[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int t = max(t_hi - u, seg_low);
+          const __amdgpu_buffer_rsrc_t rf =
+              make_rsrc(a.seg_future + (seg_row0 + t) * S, (uint32_t)S * 4u);
+          p0[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rf, off0, 0, 0));
+          p1[u] = __builtin_bit_cast(float,
+                                     __builtin_amdgcn_raw_buffer_load_b32(rf, off0 + 128u, 0, 0));
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int t = t_hi - u;
+          if (t < seg_low) break;
+          fmax0 = fmaxf(fmax0, p0[u]);
+          fmax1 = fmaxf(fmax1, p1[u]);
+          write_seg(t, p0[u], p1[u]);
+        }
+      }
+    }
     // blocks wholly before the first query the tile sees: no attention, and
     // the future score is the maximum of the later blocks
     for (int t = seg_low - 1; t >= 0; --t) write_seg(t, 0.f, 0.f);

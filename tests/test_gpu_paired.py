@@ -11,7 +11,8 @@ unit is checked through the w = 0 row-sum identity.  The query-block mode
 (Golden-Eviction scores) is checked on the same shapes, group and per head,
 against the oracle-checked masses: with blocks from row 0 the block means
 times their row and head counts add up to the mass, and the future score is
-the running maximum of the block scores from the end (exact)."""
+the running maximum of the block scores from the end (exact); the attribution
+to blocks is checked against the oracle's mass from the last blocks' rows."""
 import numpy as np
 import pytest
 import torch
@@ -59,6 +60,7 @@ def test_paired_tiles(S, w):
 
 
 def check_blocks(q, k, lse, S, w, G, mass_h, ph_h, li):
+    wl_kv = li.wl.Hkv
     L = 1024                      # blocks [0, 1024), ..., the last one partial
     n = kvp.block_count(S, 0, L)
     rows = np.array([min(S, (t + 1) * L) - t * L for t in range(n)], np.float64)
@@ -72,6 +74,19 @@ def check_blocks(q, k, lse, S, w, G, mass_h, ph_h, li):
         np.testing.assert_allclose(total, ref, rtol=2e-5, atol=1e-6)
         suffix = np.maximum.accumulate(blk[:, :, ::-1], axis=2)[:, :, ::-1]
         assert np.array_equal(fut, suffix), f"future scores S={S} per_head={per_head}"
+        # attribution to blocks: the block sums from block t on are the mass
+        # from rows >= t L only, which the oracle computes with row_lo
+        h = wl_kv - 1
+        for t in (n - 2, n - 1):
+            say(f"[paired] S={S} w={w}: oracle rows >= {t * L}, unit h={h}, per_head={per_head}")
+            ref_t = oracle.future_mass(li.q, li.k, w, b_only=0, h_only=h, row_lo=t * L,
+                                       want_per_head=per_head)
+            tail = (blk[0, :, t:].astype(np.float64) * (rows[t:] * heads)[None, :, None]).sum(axis=1)
+            if per_head:
+                assert_mass(tail[h * G:(h + 1) * G], ref_t["mass_heads"][0, h * G:(h + 1) * G],
+                            f"block sums from {t} per head")
+            else:
+                assert_mass(tail[h], ref_t["mass"][0, h], f"block sums from {t}")
 
 
 def test_paired_f32_inputs_match_bf16():
