@@ -115,3 +115,35 @@ def test_paired_f32_inputs_match_bf16():
                           out["f32"], out["bf16"]):
         # the same instructions on the same bf16 operands: bit for bit
         assert torch.equal(a, b), f"{what}: fp32 path differs from the bf16 path"
+
+
+def test_paired_units_not_a_multiple_of_8():
+    """12 KV heads: the paired grids (mass: 12 units x 64 pairs, three full
+    rounds; LSE: 12 x 256 pairs) fall back to unit-major order over the whole
+    grid instead of per XCD.  The oracle computes the tail rows of one unit
+    (exact masses for the keys they cover) and sampled LSE rows of every head;
+    every unit is checked through the w = 0 row-sum identity."""
+    S, w = 65536, 256
+    wl = kvp_inputs.workload(4).with_(Hq=48, Hkv=12, S=S, window=w, seed=1212)
+    say(f"[paired] 48/12 heads S={S}: generating inputs")
+    li = kvp_inputs.make_layer(wl)
+    q, k = to_dev(li.q), to_dev(li.k)
+    say(f"[paired] 48/12 heads S={S}: GPU path")
+    lse = kvp.lse_fwd(q, k)
+    mass = kvp.future_mass(q, k, lse, w)
+    total0 = kvp.future_mass(q, k, lse, 0).double().sum(dim=2)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(total0.cpu().numpy(), wl.G * S, rtol=1e-4)
+    lse_h, mass_h = lse.cpu().numpy(), mass.cpu().numpy()
+    rng = np.random.default_rng(5)
+    rows = np.stack([np.zeros(64, np.int64), rng.integers(0, wl.Hq, 64), rng.integers(0, S, 64)], 1)
+    rows[:4, 2] = S - 1 - np.arange(4)
+    say(f"[paired] 48/12 heads S={S}: oracle LSE rows")
+    ref_rows = oracle.lse_rows(li.q, li.k, rows)
+    assert np.abs(lse_h[0, rows[:, 1], rows[:, 2]] - ref_rows).max() <= 1e-4
+    h, row_lo = 11, S - 1024
+    say(f"[paired] 48/12 heads S={S}: oracle tail rows >= {row_lo} of h={h}")
+    ref = oracle.future_mass(li.q, li.k, w, b_only=0, h_only=h, row_lo=row_lo)
+    g0 = h * wl.G
+    assert_lse(lse_h[0, g0:g0 + wl.G, row_lo:], ref["lse"][0, g0:g0 + wl.G, row_lo:], "48/12 tail")
+    assert_mass(mass_h[0, h, row_lo - w:], ref["mass"][0, h, row_lo - w:], "48/12 tail")
