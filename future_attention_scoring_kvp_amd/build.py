@@ -1,6 +1,7 @@
 """Build libkvp.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree."""
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -41,18 +42,20 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link libkvp.so next to this file."""
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every source for gfx950 and link libkvp.so next to this file.
+    The translation units compile concurrently (``jobs`` processes, default
+    one per source up to the CPU count, at most 16)."""
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="kvp_build_") as tmp:
-        objs = []
-        for src in SOURCES:
-            obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
-            lang = ["-x", "hip"]
-            out = _run([cc, *lang, *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
-            if verbose and out.strip():
-                print(out)
-            objs.append(obj)
+        objs = [os.path.join(tmp, os.path.splitext(src)[0] + ".o") for src in SOURCES]
+        cmds = [[cc, "-x", "hip", *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+                for src, obj in zip(SOURCES, objs)]
+        n = jobs or max(1, min(len(cmds), os.cpu_count() or 1, 16))
+        with concurrent.futures.ThreadPoolExecutor(max_workers=n) as pool:
+            for out in pool.map(_run, cmds):
+                if verbose and out.strip():
+                    print(out)
         tmp_lib = os.path.join(tmp, "libkvp.so")
         _run([cc, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp_lib])
         shutil.copyfile(tmp_lib, LIB_PATH + ".tmp")
