@@ -25,13 +25,14 @@ from parity import assert_lse, assert_mass, say, to_dev
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("S,w", [
-    (32000, 77),    # 63 key tiles of 512: tile 31 sweeps alone; S % 512 = 256
-    (32749, 300),   # 64 key tiles, the last one partial; S % 32 = 13
+@pytest.mark.parametrize("S,w,D", [
+    (32000, 77, 128),    # 63 key tiles of 512: tile 31 sweeps alone; S % 512 = 256
+    (32749, 300, 128),   # 64 key tiles, the last one partial; S % 32 = 13
+    (32749, 300, 64),    # the same at d = 64 (four 16-wide slices per operand)
 ])
-def test_paired_tiles(S, w):
-    wl = kvp_inputs.workload(4).with_(S=S, window=w, seed=4242 + S)
-    say(f"[paired] S={S} w={w}: generating inputs")
+def test_paired_tiles(S, w, D):
+    wl = kvp_inputs.workload(4).with_(S=S, D=D, window=w, seed=4242 + S + D)
+    say(f"[paired] S={S} w={w} D={D}: generating inputs")
     li = kvp_inputs.make_layer(wl)
     q, k = to_dev(li.q), to_dev(li.k)
     say(f"[paired] S={S} w={w}: GPU path")
