@@ -20,7 +20,7 @@ import torch
 import future_attention_scoring_kvp_amd as kvp
 import kvp_inputs
 import oracle
-from parity import assert_lse, assert_mass, say, to_dev
+from parity import assert_keep, assert_lse, assert_mass, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -148,3 +148,45 @@ def test_paired_units_not_a_multiple_of_8():
     g0 = h * wl.G
     assert_lse(lse_h[0, g0:g0 + wl.G, row_lo:], ref["lse"][0, g0:g0 + wl.G, row_lo:], "48/12 tail")
     assert_mass(mass_h[0, h, row_lo - w:], ref["mass"][0, h, row_lo - w:], "48/12 tail")
+
+
+@pytest.mark.parametrize("family", range(6))
+def test_paired_random_shapes(family):
+    """One seeded case per family of shapes whose one-tile 8-wave grids reach
+    512 blocks with tile pairs filling whole rounds (the paired paths), with
+    random window, sinks, budget, head dimension and query blocks; everything
+    against the oracle in full: LSE, group and per-head masses, keep-sets,
+    block and future scores."""
+    B, Hkv, G, lo, hi = [(2, 64, 1, 1537, 2048), (1, 64, 1, 3585, 4096), (2, 32, 2, 3585, 4096),
+                         (1, 32, 2, 7681, 8192), (4, 32, 1, 1537, 2048),
+                         (1, 16, 8, 1537, 2048)][family]
+    rng = np.random.default_rng(900 + family)
+    D = int(rng.choice([64, 128]))
+    S = int(rng.integers(lo, hi + 1))
+    w = int(rng.integers(0, S // 3))
+    s = int(rng.integers(0, 8))
+    k = int(rng.integers(0, S + 5))
+    L = int(rng.choice([32, 64, 128, 256]))
+    start = int(rng.integers(0, S // 32)) * 32
+    wl = kvp_inputs.workload(2).with_(B=B, Hq=Hkv * G, Hkv=Hkv, S=S, D=D, window=w, n_sink=s,
+                                      top_k=k, seed=20000 + family)
+    say(f"[paired] random family {family}: B={B} Hq={Hkv * G} Hkv={Hkv} S={S} D={D} w={w} "
+        f"s={s} k={k} blocks {start}+{L}")
+    li = kvp_inputs.make_layer(wl)
+    q, kk = to_dev(li.q), to_dev(li.k)
+    lse = kvp.lse_fwd(q, kk)
+    mass = kvp.future_mass(q, kk, lse, w)
+    ph = kvp.future_mass_per_head(q, kk, lse, w)
+    keep = kvp.select_topk(mass, w, s, k)
+    blk, fut = kvp.block_future_scores(q, kk, lse, start, L, window=w)
+    torch.cuda.synchronize()
+    ref = oracle.future_mass(li.q, li.k, w, want_per_head=True)
+    what = f"random family {family}"
+    assert_lse(lse.cpu().numpy(), ref["lse"], what)
+    assert_mass(mass.cpu().numpy(), ref["mass"], what)
+    assert_mass(ph.cpu().numpy(), ref["mass_heads"], what + " per head")
+    assert_keep(keep.cpu().numpy(), ref["mass"], w, s, k, oracle.select(ref["mass"], w, s, k),
+                what)
+    rb = oracle.block_scores(li.q, li.k, w, start, L)
+    assert_mass(blk.cpu().numpy(), rb["block"], what + " block")
+    assert_mass(fut.cpu().numpy(), rb["future"], what + " future")
