@@ -27,6 +27,7 @@ def priorities(rng, B, Hkv, S):
     (1, 8, 1, 2100, 128, 512, 4, 1024, "bf16"),    # many blocks outside every window
     (1, 1, 1, 256, 64, 16, 4, 32, "f32"),          # fp32 inputs rounded on load
     (1, 4, 2, 200, 128, 8, 2, 10_000, "bf16"),     # full budget: the dense LSE
+    (1, 32, 8, 8100, 128, 512, 4, 2000, "bf16"),   # one-per-CU grid with paired tiles
 ])
 def test_sparse_lse_matches_oracle(B, Hq, Hkv, S, D, w, s, k, dtype):
     wl = kvp_inputs.workload(2).with_(B=B, Hq=Hq, Hkv=Hkv, S=S, D=D, dtype=dtype, seed=900 + S)
