@@ -6,9 +6,10 @@
 //
 // Work decomposition (queries stationary, keys streamed):
 //   * one workgroup = 8 waves (one per CU; 4 waves, two per CU, for grids
-//     too small to give every CU two); each wave owns 64 consecutive query
-//     positions of one query head (two 32-column MFMA blocks kept as bf16 B
-//     operands in registers); the waves cover (position block, head) pairs
+//     too small to give every CU two); each wave owns 96 consecutive query
+//     positions of one query head (three 32-column MFMA blocks kept as bf16 B
+//     operands in registers; two blocks, 64 positions, in the sparse pass and
+//     for fp32 input); the waves cover (position block, head) pairs
 //     of one GQA group, heads fastest, so the group's shared keys are staged
 //     once for all of them;
 //   * keys are streamed in blocks of 32 from position 0 upwards, one block
@@ -18,9 +19,9 @@
 //     16-wide slice of d, 1 KB with lane l's 16 bytes at 16 l), copied from
 //     HBM through VGPRs in two halves, so every operand read is one
 //     contiguous ds_read_b128;
-//   * per key block and wave: 16 MFMA 32x32x16 give a 32-key x 64-query
-//     tile; each lane (one query column per 32-query half) adds exp2(c*s - u)
-//     of its 16 values into one running sum per half;
+//   * per key block and wave: 24 MFMA 32x32x16 give a 32-key x 96-query
+//     tile; each lane (one query column per 32-query block) adds
+//     exp2(c*s - u) of its 16 values into one running sum per block;
 //   * software pipeline inside each wave: the MFMAs of block p+1 are issued
 //     between the VALU operations of block p;
 //   * every workgroup of a (batch, KV head) walks the same key sequence
@@ -48,19 +49,27 @@
 namespace kvp {
 namespace {
 
-template <int D, int W>
+template <int D, int W, int NB>
 struct LseCfg {
   static constexpr int kWaves = W;
   static constexpr int kThreads = kWaves * kWave;
-  static constexpr int kQueriesPerWave = 64;
+  static constexpr int kQueryBlocks = NB;        // 32-column query blocks per wave
+  static constexpr int kQueriesPerWave = 32 * NB;
   static constexpr int kKSteps = D / 16;          // 16-wide slices of d
   static constexpr int kFragBytes = kWave * 16;   // one A operand (1 KB)
   static constexpr int kSlotBytes = kKSteps * kFragBytes;
   static constexpr int kSlots = kWaves;           // wave w stages slot w
   static constexpr int kStageBytes = kSlots * kSlotBytes;
-  static constexpr int kMfmaPerBlock = 2 * kKSteps;
-  static constexpr int kValuPerBlock = 3 * 32;    // fma + exp + add per value
+  static constexpr int kMfmaPerBlock = NB * kKSteps;
 };
+
+// 32-query blocks per wave: three for the dense pass on bf16 input (every
+// staged key block then feeds 24 MFMAs per wave), two for the sparse pass and
+// for fp32 input, whose extra registers would spill.
+template <typename T, bool kSp>
+constexpr int lse_query_blocks() {
+  return (kSp || std::is_same<T, float>::value) ? 2 : 3;
+}
 
 struct LseArgs {
   const void* q;
@@ -80,11 +89,11 @@ struct LseArgs {
 
 template <bool kSp>
 struct LTile {
-  f32x16_t s0, s1;  // logits: 32 keys (rows) x query half 0 / 1 (columns)
+  f32x16_t s0, s1, s2;  // logits: 32 keys (rows) x query block 0 / 1 / 2 (columns)
 };
 template <>
 struct LTile<true> {
-  f32x16_t s0, s1;
+  f32x16_t s0, s1, s2;  // (s2 unused: the sparse pass keeps two query blocks)
   // ranks of this lane's 16 key rows (sparse mode), as fp32 bit patterns
   // (exact: ranks lie in [-1, S) and S <= 2^22)
   u32x4_t rk0, rk1, rk2, rk3;
@@ -96,7 +105,8 @@ struct LTile<true> {
 
 template <int D, typename T, int W, bool kSp, bool kPair>
 __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
-  using C = LseCfg<D, W>;
+  constexpr int NB = lse_query_blocks<T, kSp>();
+  using C = LseCfg<D, W, NB>;
   using Tile = LTile<kSp>;
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[C::kStageBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[C::kStageBytes];
@@ -157,12 +167,12 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
   const T* __restrict__ qrow = static_cast<const T*>(a.q) + (size_t)(b * a.Hq + h * G + g) * S * D;
   const uint32_t head_bytes = (uint32_t)S * D * sizeof(T);
 
-  // Stationary queries: B operands of the two 32-column blocks.
-  u32x4_t qf[2][C::kKSteps];
+  // Stationary queries: B operands of the NB 32-column blocks.
+  u32x4_t qf[NB][C::kKSteps];
   {
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(qrow, active ? head_bytes : 0u);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
       for (int ks = 0; ks < C::kKSteps; ++ks)  // rows >= S (or no pair) read 0
         qf[cb][ks] = buf_load8(qr, (uint32_t)(p0 + 32 * cb + l32) * D + 16 * ks + 8 * h32,
@@ -173,10 +183,11 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
   }
 
   const float c = a.c;
-  float u0 = 0.f, u1 = 0.f;      // per-row shifts (log2 units)
-  float sum0 = 0.f, sum1 = 0.f;  // running sums of exp2(c*s - u)
+  float u0 = 0.f, u1 = 0.f, u2 = 0.f;        // per-row shifts (log2 units)
+  float sum0 = 0.f, sum1 = 0.f, sum2 = 0.f;  // running sums of exp2(c*s - u)
   const int iq0 = p0 + l32;
   const int iq1 = iq0 + 32;
+  const int iq2 = iq0 + 64;
 
   // sparse mode: the cutoffs of this lane's two query columns, and the
   // leading key blocks that lie outside every query's window (the rank test
@@ -233,6 +244,7 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
       const u32x4_t ak = *reinterpret_cast<const u32x4_t*>(src + ks * C::kFragBytes);
       t.s0 = mfma_32x32x16(ak, qf[0][ks], ks ? t.s0 : f32x16_t{});
       t.s1 = mfma_32x32x16(ak, qf[1][ks], ks ? t.s1 : f32x16_t{});
+      if constexpr (NB == 3) t.s2 = mfma_32x32x16(ak, qf[2][ks], ks ? t.s2 : f32x16_t{});
     }
     if constexpr (kSp) {
       // ranks of rows 8 g + 4 h32 + (0..3): the rows of values 4 g .. 4 g + 3
@@ -246,14 +258,16 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
     }
   };
   auto exp_full = [&](const Tile& t) __attribute__((always_inline)) {
-    float t0 = 0.f, t1 = 0.f;
+    float t0 = 0.f, t1 = 0.f, t2 = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       t0 += fast_exp2(__builtin_fmaf(t.s0[v], c, -u0));
       t1 += fast_exp2(__builtin_fmaf(t.s1[v], c, -u1));
+      if constexpr (NB == 3) t2 += fast_exp2(__builtin_fmaf(t.s2[v], c, -u2));
     }
     sum0 += t0;
     sum1 += t1;
+    if constexpr (NB == 3) sum2 += t2;
   };
   // sparse mode, blocks outside every window: a key counts iff its rank is
   // at most the query's cutoff.  The 0/1 weight is one clamped subtract,
@@ -306,7 +320,8 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
     // i.e. iff the constant 8 (v / 4) + v % 4 <= lim
     const int lim0 = min(iq0, S - 1) - kb * kBlk - 4 * h32;
     const int lim1 = min(iq1, S - 1) - kb * kBlk - 4 * h32;
-    float t0 = 0.f, t1 = 0.f;
+    const int lim2 = min(iq2, S - 1) - kb * kBlk - 4 * h32;
+    float t0 = 0.f, t1 = 0.f, t2 = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int r = 8 * (v >> 2) + (v & 3);
@@ -314,23 +329,31 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
       const float x1 = __builtin_fmaf(t.s1[v], c, -u1);
       t0 += fast_exp2(r <= lim0 ? x0 : -__builtin_inff());
       t1 += fast_exp2(r <= lim1 ? x1 : -__builtin_inff());
+      if constexpr (NB == 3) {
+        const float x2 = __builtin_fmaf(t.s2[v], c, -u2);
+        t2 += fast_exp2(r <= lim2 ? x2 : -__builtin_inff());
+      }
     }
     sum0 += t0;
     sum1 += t1;
+    if constexpr (NB == 3) sum2 += t2;
   };
   // Shifts from the first key block (key 0 is valid for every row).
   auto set_shift = [&](const Tile& t) __attribute__((always_inline)) {
-    float m0 = -__builtin_inff(), m1 = -__builtin_inff();
+    float m0 = -__builtin_inff(), m1 = -__builtin_inff(), m2 = -__builtin_inff();
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int j = mfma_row(v, lane);
       if (j <= iq0 && j < S) m0 = fmaxf(m0, t.s0[v]);
       if (j <= iq1 && j < S) m1 = fmaxf(m1, t.s1[v]);
+      if constexpr (NB == 3)
+        if (j <= iq2 && j < S) m2 = fmaxf(m2, t.s2[v]);
     }
     m0 = fmaxf(m0, __shfl_xor(m0, 32));
     m1 = fmaxf(m1, __shfl_xor(m1, 32));
     u0 = m0 * c;
     u1 = m1 * c;
+    if constexpr (NB == 3) u2 = fmaxf(m2, __shfl_xor(m2, 32)) * c;
   };
   // Exponentials of block kb (in cur) and MFMAs of block kb + 1 (into nxt).
   auto step = [&](Tile& cur, Tile& nxt, int kb, const unsigned char* nk, const int* nr, int nslot)
@@ -341,8 +364,8 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
     // VALU and transcendental (exp2) operations per MFMA: per value an fma
     // and an add (dense) or a clamped subtract and two fma (rank test), and
     // one exp2
-    constexpr int kValuPerMfma = (kSp ? 3 : 2) * 32 / C::kMfmaPerBlock;
-    constexpr int kTransPerMfma = 32 / C::kMfmaPerBlock;
+    constexpr int kValuPerMfma = (kSp ? 3 : 2) * 16 * NB / C::kMfmaPerBlock;
+    constexpr int kTransPerMfma = 16 * NB / C::kMfmaPerBlock;
     if (m_ok && fast) {
       mfma_block(nxt, nk, nr, nslot);
       if constexpr (kSp)
@@ -355,7 +378,8 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
         __builtin_amdgcn_sched_group_barrier(0x400, kTransPerMfma, 0);
-        if ((m & 1) == 1 && m < 2 * C::kKSteps - 2)
+        // one operand read per key slice, i.e. after every NB-th MFMA
+        if (m % NB == NB - 1 && m < NB * C::kKSteps - NB)
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         if (kSp && m == C::kKSteps - 1)  // the next block's four rank reads
           __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -428,6 +452,7 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
   // Combine the two half-columns (lanes l and l^32 hold the same query).
   sum0 += __shfl_xor(sum0, 32);
   sum1 += __shfl_xor(sum1, 32);
+  if constexpr (NB == 3) sum2 += __shfl_xor(sum2, 32);
   if (active && lane < 32) {
     float* out = a.lse + (size_t)(b * a.Hq + h * G + g) * S;
     const float l0 = (u0 + __log2f(sum0)) * kLn2;
@@ -440,6 +465,11 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
     const bool ok1 = sum1 < __builtin_inff() && l1 == l1 && (!kSp || sum1 >= lo);
     if (iq0 < S) out[iq0] = ok0 ? l0 : __builtin_inff();
     if (iq1 < S) out[iq1] = ok1 ? l1 : __builtin_inff();
+    if constexpr (NB == 3) {
+      const float l2 = (u2 + __log2f(sum2)) * kLn2;
+      const bool ok2 = sum2 < __builtin_inff() && l2 == l2;
+      if (iq2 < S) out[iq2] = ok2 ? l2 : __builtin_inff();
+    }
   }
   }  // tiles of the workgroup
 }
@@ -517,7 +547,7 @@ struct SparseIn {
 template <int D, typename T, int W, bool kSp>
 hipError_t launch_lse_w(const void* q, const void* k, const Shape& sh, float scale, float* lse,
                         const SparseIn& sp, hipStream_t stream) {
-  using C = LseCfg<D, W>;
+  using C = LseCfg<D, W, lse_query_blocks<T, kSp>()>;
   LseArgs a;
   a.rank = sp.rank;
   a.cutoff = sp.cutoff;
@@ -569,7 +599,8 @@ hipError_t launch_lse_w(const void* q, const void* k, const Shape& sh, float sca
 template <int D, typename T, bool kSp>
 hipError_t launch_lse_t(const void* q, const void* k, const Shape& sh, float scale, float* lse,
                         const SparseIn& sp, hipStream_t stream) {
-  const int64_t n_pb = (sh.S + LseCfg<D, 8>::kQueriesPerWave - 1) / LseCfg<D, 8>::kQueriesPerWave;
+  constexpr int kQ = LseCfg<D, 8, lse_query_blocks<T, kSp>()>::kQueriesPerWave;
+  const int64_t n_pb = (sh.S + kQ - 1) / kQ;
   const int64_t blocks8 = (n_pb * sh.G + 7) / 8 * sh.B * sh.Hkv;
   if (blocks8 >= 2 * kNumCUs) return launch_lse_w<D, T, 8, kSp>(q, k, sh, scale, lse, sp, stream);
   return launch_lse_w<D, T, 4, kSp>(q, k, sh, scale, lse, sp, stream);
