@@ -20,7 +20,9 @@
 //     HBM through VGPRs in two halves, so every operand read is one
 //     contiguous ds_read_b128;
 //   * per key block and wave: 24 MFMA 32x32x16 give a 32-key x 96-query
-//     tile; each lane (one query column per 32-query block) adds
+//     tile (16 MFMA and 64 queries for fp32 input, the sparse pass and
+//     grids too short to fill the CUs); each lane (one query column per
+//     32-query block) adds
 //     exp2(c*s - u) of its 16 values into one running sum per block;
 //   * software pipeline inside each wave: the MFMAs of block p+1 are issued
 //     between the VALU operations of block p;
@@ -63,9 +65,11 @@ struct LseCfg {
   static constexpr int kMfmaPerBlock = NB * kKSteps;
 };
 
-// 32-query blocks per wave: three for the dense pass on bf16 input (every
-// staged key block then feeds 24 MFMAs per wave), two for the sparse pass and
-// for fp32 input, whose extra registers would spill.
+// Most 32-query blocks per wave: three for the dense pass on bf16 input
+// (every staged key block then feeds 24 MFMAs per wave), two for the sparse
+// pass and for fp32 input, whose extra registers would spill.  Grids too
+// small for two 8-wave workgroups per CU at three blocks run two blocks per
+// wave instead, so that short sequences still spread over every CU.
 template <typename T, bool kSp>
 constexpr int lse_query_blocks() {
   return (kSp || std::is_same<T, float>::value) ? 2 : 3;
@@ -103,9 +107,9 @@ struct LTile<true> {
   }
 };
 
-template <int D, typename T, int W, bool kSp, bool kPair>
+template <int D, typename T, int W, bool kSp, bool kPair, int NB>
 __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
-  constexpr int NB = lse_query_blocks<T, kSp>();
+  static_assert(NB >= 2 && NB <= lse_query_blocks<T, kSp>(), "query blocks per wave");
   using C = LseCfg<D, W, NB>;
   using Tile = LTile<kSp>;
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[C::kStageBytes];
@@ -544,10 +548,10 @@ struct SparseIn {
   int window;
 };
 
-template <int D, typename T, int W, bool kSp>
+template <int D, typename T, int W, bool kSp, int NB>
 hipError_t launch_lse_w(const void* q, const void* k, const Shape& sh, float scale, float* lse,
                         const SparseIn& sp, hipStream_t stream) {
-  using C = LseCfg<D, W, lse_query_blocks<T, kSp>()>;
+  using C = LseCfg<D, W, NB>;
   LseArgs a;
   a.rank = sp.rank;
   a.cutoff = sp.cutoff;
@@ -576,13 +580,13 @@ hipError_t launch_lse_w(const void* q, const void* k, const Shape& sh, float sca
   const int64_t blocks = units * (pair ? (a.n_wg + 1) / 2 : a.n_wg);
   if constexpr (W == 8) {
     if (pair)
-      hipLaunchKernelGGL((lse_kernel<D, T, W, kSp, true>), dim3((unsigned)blocks),
+      hipLaunchKernelGGL((lse_kernel<D, T, W, kSp, true, NB>), dim3((unsigned)blocks),
                          dim3(C::kThreads), 0, stream, a);
     else
-      hipLaunchKernelGGL((lse_kernel<D, T, W, kSp, false>), dim3((unsigned)blocks),
+      hipLaunchKernelGGL((lse_kernel<D, T, W, kSp, false, NB>), dim3((unsigned)blocks),
                          dim3(C::kThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((lse_kernel<D, T, W, kSp, false>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((lse_kernel<D, T, W, kSp, false, NB>), dim3((unsigned)blocks),
                        dim3(C::kThreads), 0, stream, a);
   }
   hipError_t err = hipGetLastError();
@@ -595,15 +599,24 @@ hipError_t launch_lse_w(const void* q, const void* k, const Shape& sh, float sca
 }
 
 // 8-wave workgroups (one per CU) when the grid holds at least two per CU,
-// else 4-wave workgroups (two per CU).
+// else 4-wave workgroups (two per CU) with two query blocks per wave.  Three
+// query blocks per wave only where they still give such a grid.  The number
+// of blocks per wave does not change the result: every row sums the same key
+// blocks in the same order.
 template <int D, typename T, bool kSp>
 hipError_t launch_lse_t(const void* q, const void* k, const Shape& sh, float scale, float* lse,
                         const SparseIn& sp, hipStream_t stream) {
-  constexpr int kQ = LseCfg<D, 8, lse_query_blocks<T, kSp>()>::kQueriesPerWave;
-  const int64_t n_pb = (sh.S + kQ - 1) / kQ;
-  const int64_t blocks8 = (n_pb * sh.G + 7) / 8 * sh.B * sh.Hkv;
-  if (blocks8 >= 2 * kNumCUs) return launch_lse_w<D, T, 8, kSp>(q, k, sh, scale, lse, sp, stream);
-  return launch_lse_w<D, T, 4, kSp>(q, k, sh, scale, lse, sp, stream);
+  auto blocks8 = [&](int queries_per_wave) {
+    const int64_t n_pb = (sh.S + queries_per_wave - 1) / queries_per_wave;
+    return (n_pb * sh.G + 7) / 8 * sh.B * sh.Hkv;
+  };
+  if constexpr (lse_query_blocks<T, kSp>() == 3) {
+    if (blocks8(LseCfg<D, 8, 3>::kQueriesPerWave) >= 2 * kNumCUs)
+      return launch_lse_w<D, T, 8, kSp, 3>(q, k, sh, scale, lse, sp, stream);
+  }
+  if (blocks8(LseCfg<D, 8, 2>::kQueriesPerWave) >= 2 * kNumCUs)
+    return launch_lse_w<D, T, 8, kSp, 2>(q, k, sh, scale, lse, sp, stream);
+  return launch_lse_w<D, T, 4, kSp, 2>(q, k, sh, scale, lse, sp, stream);
 }
 
 }  // namespace
