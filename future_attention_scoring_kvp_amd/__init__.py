@@ -39,9 +39,9 @@ from typing import Optional
 
 import torch
 
-__all__ = ["lse_fwd", "lse_sparse", "future_mass", "future_mass_per_head", "target_scores", "select_topk",
-           "keep_count", "running_cutoff", "block_count", "block_future_scores", "soft_topk", "soft_topk_backward",
-           "KvpError", "library_path", "load_library", "AGG_LOG_MEAN",
+__all__ = ["lse_fwd", "lse_sparse", "future_mass", "future_mass_per_head", "target_scores",
+           "select_topk", "select_workspace_bytes", "keep_count", "running_cutoff", "block_count",
+           "block_future_scores", "soft_topk", "soft_topk_backward", "KvpError", "library_path", "load_library", "AGG_LOG_MEAN",
            "AGG_MEAN_LOG", "AGG_MAX_LOG"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -91,7 +91,10 @@ def load_library():
             lib.kvp_keep_count.restype = i64
             lib.kvp_keep_count.argtypes = [i64, i64, i64, i64]
             lib.kvp_select_topk.restype = ctypes.c_int
-            lib.kvp_select_topk.argtypes = [vp, _Dims, i32, i32, i32, vp, vp]
+            lib.kvp_select_topk.argtypes = [vp, _Dims, i32, i32, i32, vp, vp, ctypes.c_size_t,
+                                            vp]
+            lib.kvp_select_workspace_bytes.restype = ctypes.c_size_t
+            lib.kvp_select_workspace_bytes.argtypes = [_Dims, i32]
             lib.kvp_block_count.restype = i64
             lib.kvp_block_count.argtypes = [i64, i64, i64]
             lib.kvp_block_future_scores.restype = ctypes.c_int
@@ -285,10 +288,20 @@ def target_scores(mass: torch.Tensor, n_kv_heads: int, window: int, *, per_head:
     return out
 
 
+def select_workspace_bytes(rows: int, seq_len: int, top_k: int = 0) -> int:
+    """Bytes of device workspace select_topk needs for ``rows`` rows of
+    ``seq_len`` scores (0 for rows of at most 32768)."""
+    return int(load_library().kvp_select_workspace_bytes(_Dims(rows, 1, 1, seq_len, 128),
+                                                         int(top_k)))
+
+
 def select_topk(mass: torch.Tensor, window: int, n_sink: int, top_k: int,
-                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
     """Keep-set per KV head, int32 [..., n_keep] ascending.  ``mass`` is
-    [B, Hkv, S] (any leading dims are flattened into rows)."""
+    [B, Hkv, S] (any leading dims are flattened into rows).  ``workspace`` (a
+    uint8 GPU tensor of select_workspace_bytes bytes, 256-byte aligned) is
+    allocated when needed and not given."""
     lib = load_library()
     _require_device(mass)
     if mass.dtype != torch.float32 or mass.dim() < 1:
@@ -305,8 +318,16 @@ def select_topk(mass: torch.Tensor, window: int, n_sink: int, top_k: int,
     if out.dtype != torch.int32 or tuple(out.shape) != shape:
         raise KvpError(f"keep out must be int32 {shape}")
     d = _Dims(rows, 1, 1, S, 128)
+    need = int(lib.kvp_select_workspace_bytes(d, int(top_k)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=mass.device)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _require_device(workspace)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     _check(lib.kvp_select_topk(mass.data_ptr(), d, int(window), int(n_sink), int(top_k),
-                               out.data_ptr(), _stream_ptr(stream)), "kvp_select_topk")
+                               out.data_ptr(), ws_ptr, ws_bytes, _stream_ptr(stream)),
+           "kvp_select_topk")
     return out
 
 

@@ -41,8 +41,15 @@ hipError_t launch_block_scores(const void* q, const void* k, const float* lse, i
 hipError_t launch_target(const float* mass, int per_head, const Shape& sh, int window,
                          int normalize, int agg, float eps, int query, int decay_step,
                          const float* log_gamma, float* score, hipStream_t stream);
+// Keep-set of `rows` rows of S scores.  Rows longer than 32768 are split
+// over several workgroups with their state in `workspace`, of
+// select_workspace_bytes(rows, S) bytes (0: no workspace is read); its
+// blocks number select_split_blocks(rows, S) per launch.
+size_t select_workspace_bytes(int64_t rows, int S);
+int64_t select_split_blocks(int64_t rows, int S);
 hipError_t launch_select(const float* mass, int64_t rows, int S, int window, int n_sink,
-                         int top_k, int64_t n_keep, int32_t* keep, hipStream_t stream);
+                         int top_k, int64_t n_keep, int32_t* keep, void* workspace,
+                         hipStream_t stream);
 
 // Running top-k cutoff: rank [rows, S] and cutoff [rows, S] (int32) from
 // scores [rows, S]; workspace of cutoff_workspace_bytes(rows, S, n_sink).

@@ -7,30 +7,40 @@
 // (e.g. the log targets, which are negative).  Ranking: score descending,
 // equal scores by ascending index.
 //
-// One workgroup per (batch, KV head) row, in two steps:
-//   1. radix select, most significant byte first, on an order-preserving
-//      32-bit key of each fp32 score (any sign; see score_key): four passes of a
-//      256-bin LDS histogram over the candidates that match the bytes fixed
-//      so far give the k-th largest value T exactly and the number r of
-//      copies of T that belong to the top-k (the r lowest-indexed ones);
+// Both paths work in two steps:
+//   1. radix select, most significant digit first, on an order-preserving
+//      32-bit key of each fp32 score (any sign; see score_key): histograms of
+//      the candidates that match the digits fixed so far give the k-th
+//      largest value T exactly and the number r of copies of T that belong to
+//      the top-k (the r lowest-indexed ones);
 //   2. ordered emission: position j is kept iff it is a sink or in the
 //      window, or its key is above T, or it is among the first r copies of T;
 //      its output slot is the number of kept positions before it, so the
 //      output is ascending with no sort.
-// Rows of up to 32768 scores (select_reg_kernel, 1024 threads): each thread
-// holds KPT consecutive keys in registers, so the row is read from memory
-// once; the passes histogram from registers into per-wave LDS copies, and
-// one block-wide scan of (kept, tie) counts places every kept position.
-// Longer rows (select_kernel, 256 threads) re-read the row from memory per
-// pass and emit in chunks of 256 positions with a ballot scan per chunk.
+// Rows of up to 32768 scores (select_reg_kernel, one 1024-thread workgroup
+// per row): each thread holds KPT consecutive keys in registers, so the row
+// is read from memory once; four 8-bit passes histogram from registers into
+// per-wave LDS copies, and one block-wide scan of (kept, tie) counts places
+// every kept position.
+// Longer rows are split into chunks of 4096 or more positions, one 256-thread
+// workgroup per (row, chunk), with the per-chunk integer state in a caller
+// workspace (deterministic: integer counts, fixed reduction order):
+//   sel_hist_kernel     per chunk, a 2048-bin histogram of key bits 31..21;
+//   sel_bin_kernel      per row, the bin b1 of the k-th largest key (suffix
+//                       scan over the summed chunk histograms), the count of
+//                       keys above b1 per chunk and each chunk's offset into
+//                       the candidate list (the keys in bin b1);
+//   sel_compact_kernel  per chunk, its keys in bin b1 into its segment of the
+//                       candidate list;
+//   sel_finish_kernel   per row, two more radix passes (bits 20..10, 9..0)
+//                       over the candidates give T and r; per chunk, the kept
+//                       and tie counts before it;
+//   sel_emit_kernel     per chunk, flags, a block scan and the stores.
 #include "kvp_device.h"
 #include "kvp_launch.h"
 
 namespace kvp {
 namespace {
-
-constexpr int kSelThreads = 256;
-constexpr int kSelWaves = kSelThreads / kWave;
 
 struct SelArgs {
   const float* mass;
@@ -47,107 +57,6 @@ __device__ __forceinline__ uint32_t score_key(float m) {
   if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-
-// Exclusive prefix (over the workgroup, in thread order) of a 0/1 flag, and
-// the chunk total.  Uses wave ballots and a 4-entry LDS table.
-__device__ __forceinline__ int block_prefix(bool flag, int* wave_tot, int& total) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const uint64_t bal = __ballot(flag);
-  const int in_wave = __popcll(bal & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-  if (lane == 0) wave_tot[wave] = __popcll(bal);
-  __syncthreads();
-  int before = 0;
-  total = 0;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
-    const int t = wave_tot[w];
-    if (w < wave) before += t;
-    total += t;
-  }
-  __syncthreads();
-  return before + in_wave;
-}
-
-__global__ __launch_bounds__(kSelThreads) void select_kernel(SelArgs a) {
-  __shared__ int hist[256];
-  __shared__ int wave_tot[kSelWaves];
-  __shared__ uint32_t sel_digit;
-  __shared__ int sel_above;
-
-  const int tid = threadIdx.x;
-  const int S = a.S;
-  const float* __restrict__ m = a.mass + (size_t)blockIdx.x * S;
-  int32_t* __restrict__ out = a.keep + (size_t)blockIdx.x * a.n_keep;
-
-  const int e_lo = a.n_sink;                 // eligible range [e_lo, e_hi)
-  const int e_hi = S - a.window;             // may be <= e_lo (empty)
-  const int n_elig = e_hi > e_lo ? e_hi - e_lo : 0;
-  const int kk = a.top_k < n_elig ? a.top_k : n_elig;
-  const bool take_all = kk == n_elig;
-
-  // --- 1. threshold T and tie count r (only when 0 < kk < n_elig)
-  uint32_t prefix = 0, pmask = 0;
-  int r = kk;
-  if (!take_all && kk > 0) {
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      hist[tid] = 0;
-      __syncthreads();
-      for (int j = e_lo + tid; j < e_hi; j += kSelThreads) {
-        const uint32_t u = score_key(m[j]);
-        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
-      }
-      __syncthreads();
-      if (tid == 0) {
-        int above = 0;
-        int d = 255;
-        for (; d > 0; --d) {
-          if (above + hist[d] >= r) break;
-          above += hist[d];
-        }
-        sel_digit = (uint32_t)d;
-        sel_above = above;
-      }
-      __syncthreads();
-      prefix |= sel_digit << shift;
-      pmask |= 255u << shift;
-      r -= sel_above;
-      __syncthreads();
-    }
-  }
-  const uint32_t T = prefix;
-
-  // --- 2. ordered emission
-  int written = 0;
-  int ties_seen = 0;
-  for (int base = 0; base < S; base += kSelThreads) {
-    const int j = base + tid;
-    bool kept = false, is_tie = false;
-    if (j < S) {
-      if (j < a.n_sink || j >= e_hi) {
-        kept = true;  // sink or protected window
-      } else if (kk > 0) {
-        if (take_all) {
-          kept = true;
-        } else {
-          const uint32_t u = score_key(m[j]);
-          kept = u > T;
-          is_tie = u == T;
-        }
-      }
-    }
-    int n_ties = 0;
-    const int tie_rank = ties_seen + block_prefix(is_tie, wave_tot, n_ties);
-    if (is_tie && tie_rank < r) kept = true;
-    ties_seen += n_ties;
-    int n_kept = 0;
-    const int slot = written + block_prefix(kept, wave_tot, n_kept);
-    if (kept && slot < a.n_keep) out[slot] = j;
-    written += n_kept;
-  }
-}
-
 
 // ---- rows of up to kRegThreads * KPT scores: keys held in registers
 
@@ -366,29 +275,500 @@ __global__ __launch_bounds__(kRegThreads) void select_reg_kernel(SelArgs a, bool
   for (int i = tid; i < n_out; i += kRegThreads) out[i] = out_lds[i];
 }
 
+
+// ---- rows split over several workgroups (state in the caller's workspace)
+
+constexpr int kMbThreads = 256;
+constexpr int kMbWaves = kMbThreads / kWave;
+constexpr int kSubLen = 4 * kMbThreads;     // positions per sub-chunk (one float4 per thread)
+constexpr int kBins1 = 2048;                // digit 1: key bits 31..21
+constexpr int kBins2 = 2048;                // digit 2: key bits 20..10
+constexpr int kBins3 = 1024;                // digit 3: key bits 9..0
+constexpr int kFinThreads = 1024;
+constexpr int kFinWaves = kFinThreads / kWave;
+constexpr int kCandLds = 32768;             // candidates held in LDS by sel_finish_kernel
+constexpr int kStateInts = 8;               // per row: b1, k1, n_cand, T, r
+
+// Selection of a row: 0 = no eligible token is taken (k = 0 or none
+// eligible), 1 = every eligible token is taken, 2 = a real top-k.
+enum { kTakeNone = 0, kTakeAll = 1, kSelect = 2 };
+
+struct MbArgs {
+  const float* mass;
+  int32_t* keep;
+  int S, window, n_sink, kk, mode;
+  int nc, C;            // chunks per row, chunk length (a multiple of kSubLen)
+  int64_t n_keep;
+  bool vec4;            // rows are 16-byte aligned (S % 4 == 0)
+  int32_t* hist;        // [rows][nc][kBins1]
+  int32_t* chunk;       // [rows][nc][4]: keys above bin b1, candidate offset, kept base, tie base
+  int32_t* state;       // [rows][kStateInts]
+  uint32_t* cand;       // [rows][S] candidate keys, chunk segments in chunk order
+};
+
+// Four consecutive scores at position p of a row (p % 4 == 0); positions at
+// or past S read 0 and are never eligible.
+__device__ __forceinline__ void load4(const float* __restrict__ m, int p, int S, bool vec4,
+                                      float v[4]) {
+  if (vec4 && p + 3 < S) {
+    const float4 x = *reinterpret_cast<const float4*>(m + p);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = p + q < S ? m[p + q] : 0.f;
+  }
+}
+
+// Positions kept whatever the scores (sinks and window) in [0, p), p <= S.
+__device__ __forceinline__ int forced_before(int p, int S, int w, int s) {
+  const int sp = min(s, S);
+  const int wl = max(sp, S - w);  // first window position that is not a sink
+  return min(p, sp) + max(0, p - wl);
+}
+
+__global__ __launch_bounds__(kMbThreads) void sel_hist_kernel(MbArgs a) {
+  __shared__ int h[kMbWaves][kBins1];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int row = blockIdx.x / a.nc, c = blockIdx.x - row * a.nc;
+  for (int i = tid; i < kMbWaves * kBins1; i += kMbThreads) (&h[0][0])[i] = 0;
+  __syncthreads();
+  const float* __restrict__ m = a.mass + (size_t)row * a.S;
+  const int e_lo = a.n_sink, e_hi = a.S - a.window;
+  const int p_end = min(a.S, (c + 1) * a.C);
+  for (int p = c * a.C + 4 * tid; p < p_end; p += kSubLen) {
+    float v[4];
+    load4(m, p, a.S, a.vec4, v);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (p + q >= e_lo && p + q < e_hi) atomicAdd(&h[wave][score_key(v[q]) >> 21], 1);
+  }
+  __syncthreads();
+  int32_t* out = a.hist + ((size_t)row * a.nc + c) * kBins1;
+  for (int b = tid; b < kBins1; b += kMbThreads) out[b] = h[0][b] + h[1][b] + h[2][b] + h[3][b];
+}
+
+// Inclusive suffix sum over the threads of a block (thread t gets the sum of
+// `v` over threads >= t); `tot` is LDS scratch of one int per wave.
+template <int kWaves>
+__device__ __forceinline__ int block_suffix(int v, int* tot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_down(x, off);
+    if (lane + off < kWave) x += o;
+  }
+  if (lane == 0) tot[wave] = x;
+  __syncthreads();
+  int later = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w)
+    if (w > wave) later += tot[w];
+  __syncthreads();
+  return x + later;
+}
+
+// Digit search over per-thread bin counts: thread t owns bins [kPer t,
+// kPer t + kPer).  Finds the digit d with (count above d) < r <= (count at or
+// above d) and writes d and the count above it to *dig / *above.  r >= 1 and
+// the total is >= r, so exactly one thread finds it.
+template <int kWaves, int kPer>
+__device__ __forceinline__ void find_digit(const int (&c)[kPer], int r, int* tot, int* dig,
+                                           int* above) {
+  int own = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) own += c[i];
+  const int suf = block_suffix<kWaves>(own, tot);
+  const int ab = suf - own;  // in bins above this thread's
+  if (ab < r && r <= suf) {
+    int acc = ab, d = kPer * (int)threadIdx.x + kPer - 1;
+#pragma unroll
+    for (int i = kPer - 1; i > 0; --i) {
+      if (acc + c[i] >= r) break;
+      acc += c[i];
+      --d;
+    }
+    *dig = d;
+    *above = acc;
+  }
+}
+
+// Per row: the bin of the k-th largest key, the keys above that bin per chunk
+// and the candidate offsets.  One 256-thread workgroup per row.
+__global__ __launch_bounds__(kMbThreads) void sel_bin_kernel(MbArgs a) {
+  constexpr int kPer = kBins1 / kMbThreads;  // 8 bins per thread
+  __shared__ int tot[kMbWaves];
+  __shared__ int s_b1, s_above;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x;
+  const int32_t* hist = a.hist + (size_t)row * a.nc * kBins1;
+  if (tid == 0) {  // found by exactly one thread below; set for safety
+    s_b1 = 0;
+    s_above = 0;
+  }
+  int c8[kPer] = {};
+  for (int c = 0; c < a.nc; ++c) {
+    const int4* p = reinterpret_cast<const int4*>(hist + (size_t)c * kBins1 + kPer * tid);
+    const int4 x = p[0], y = p[1];
+    c8[0] += x.x; c8[1] += x.y; c8[2] += x.z; c8[3] += x.w;
+    c8[4] += y.x; c8[5] += y.y; c8[6] += y.z; c8[7] += y.w;
+  }
+  find_digit<kMbWaves, kPer>(c8, a.kk, tot, &s_b1, &s_above);
+  __syncthreads();
+  const int b1 = s_b1 & (kBins1 - 1);
+  int32_t* st = a.state + (size_t)row * kStateInts;
+  int32_t* ch = a.chunk + (size_t)row * a.nc * 4;
+  // keys above b1 in each chunk: one wave per chunk, lanes over the bins
+  for (int c = wave; c < a.nc; c += kMbWaves) {
+    const int32_t* hc = hist + (size_t)c * kBins1;
+    int t = 0;
+    for (int b = b1 + 1 + lane; b < kBins1; b += kWave) t += hc[b];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off);
+    if (lane == 0) ch[4 * c] = t;
+  }
+  // candidate offsets: exclusive prefix over chunks of the count in bin b1
+  if (wave == 0) {
+    int base = 0;
+    for (int c0 = 0; c0 < a.nc; c0 += kWave) {
+      const int c = c0 + lane;
+      const int v = c < a.nc ? hist[(size_t)c * kBins1 + b1] : 0;
+      int x = v;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(x, off);
+        if (lane >= off) x += o;
+      }
+      if (c < a.nc) ch[4 * c + 1] = base + x - v;
+      base += __shfl(x, kWave - 1);
+    }
+    if (lane == 0) {
+      st[0] = b1;
+      st[1] = a.kk - s_above;  // rank of T among the candidates (1-based)
+      st[2] = base;            // candidates
+    }
+  }
+}
+
+// Per chunk: its keys in bin b1 go to its segment of the candidate list (in
+// any order inside the segment).
+__global__ __launch_bounds__(kMbThreads) void sel_compact_kernel(MbArgs a) {
+  __shared__ int n;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int row = blockIdx.x / a.nc, c = blockIdx.x - row * a.nc;
+  if (tid == 0) n = 0;
+  __syncthreads();
+  const uint32_t b1 = (uint32_t)a.state[(size_t)row * kStateInts] & (kBins1 - 1);
+  uint32_t* out = a.cand + (size_t)row * a.S + a.chunk[((size_t)row * a.nc + c) * 4 + 1];
+  const float* __restrict__ m = a.mass + (size_t)row * a.S;
+  const int e_lo = a.n_sink, e_hi = a.S - a.window;
+  const int p_end = min(a.S, (c + 1) * a.C);
+  // every lane of the block runs the same trip count (ballots below)
+  for (int p0 = c * a.C; p0 < p_end; p0 += kSubLen) {
+    const int p = p0 + 4 * tid;
+    float v[4];
+    load4(m, p, a.S, a.vec4, v);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t u = score_key(v[q]);
+      const bool is_c = p + q >= e_lo && p + q < e_hi && (u >> 21) == b1;
+      const uint64_t bal = __ballot(is_c);
+      if (bal == 0) continue;
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&n, __popcll(bal));
+      base = __shfl(base, 0);
+      if (is_c) out[base + __popcll(bal & ((1ull << lane) - 1ull))] = u;
+    }
+  }
+}
+
+// Per row: T and r from the candidates, then the kept / tie bases of every
+// chunk.  One 1024-thread workgroup per row.
+__global__ __launch_bounds__(kFinThreads) void sel_finish_kernel(MbArgs a) {
+  __shared__ uint32_t keys[kCandLds];
+  __shared__ int h[kBins2];
+  __shared__ int tot[kFinWaves];
+  __shared__ int s_d, s_above;
+  __shared__ int s_gt[kWave], s_eq[kWave];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x;
+  int32_t* st = a.state + (size_t)row * kStateInts;
+  const uint32_t b1 = (uint32_t)st[0] & (kBins1 - 1);
+  int r = st[1];
+  const int n = min(st[2], a.S);
+  const uint32_t* gk = a.cand + (size_t)row * a.S;
+  const bool in_lds = n <= kCandLds;
+  if (in_lds)
+    for (int i = tid; i < n; i += kFinThreads) keys[i] = gk[i];
+  const uint32_t* src = in_lds ? keys : gk;
+
+  // digit 2 (bits 20..10) over all candidates, then digit 3 (bits 9..0) over
+  // those that match it
+  uint32_t prefix = b1 << 21;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = pass == 0 ? 10 : 0;
+    const uint32_t pmask = pass == 0 ? 0xFFE00000u : 0xFFFFFC00u;
+    const int nb = pass == 0 ? kBins2 : kBins3;
+    for (int i = tid; i < kBins2; i += kFinThreads) h[i] = 0;
+    if (tid == 0) {  // found by exactly one thread below; set for safety
+      s_d = 0;
+      s_above = 0;
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += kFinThreads) {
+      const uint32_t u = src[i];
+      if ((u & pmask) == prefix) atomicAdd(&h[(u >> shift) & (uint32_t)(nb - 1)], 1);
+    }
+    __syncthreads();
+    if (pass == 0) {
+      int c2[2] = {h[2 * tid], h[2 * tid + 1]};
+      find_digit<kFinWaves, 2>(c2, r, tot, &s_d, &s_above);
+    } else {
+      int c1[1] = {h[tid]};
+      find_digit<kFinWaves, 1>(c1, r, tot, &s_d, &s_above);
+    }
+    __syncthreads();
+    prefix |= (uint32_t)s_d << shift;
+    r -= s_above;
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+
+  // per chunk: candidates above T and equal to T, one wave per chunk over its
+  // segment; then the exclusive prefixes over chunks
+  int32_t* ch = a.chunk + (size_t)row * a.nc * 4;
+  const int S = a.S, w = a.window, s = a.n_sink;
+  int fa_base = 0, tie_base = 0;
+  for (int c0 = 0; c0 < a.nc; c0 += kWave) {
+    const int nch = min(kWave, a.nc - c0);
+    for (int cc = wave; cc < nch; cc += kFinWaves) {
+      const int c = c0 + cc;
+      const int lo = max(0, min(ch[4 * c + 1], n));
+      const int hi = c + 1 < a.nc ? max(lo, min(ch[4 * c + 5], n)) : n;
+      int gt = 0, eq = 0;
+      for (int i = lo + lane; i < hi; i += kWave) {
+        const uint32_t u = src[i];
+        gt += u > T;
+        eq += u == T;
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        gt += __shfl_xor(gt, off);
+        eq += __shfl_xor(eq, off);
+      }
+      if (lane == 0) {
+        s_gt[cc] = gt;
+        s_eq[cc] = eq;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int c = c0 + lane;
+      int fa = 0, eq = 0;
+      if (lane < nch) {
+        const int p_lo = c * a.C, p_hi = min(S, (c + 1) * a.C);
+        fa = forced_before(p_hi, S, w, s) - forced_before(p_lo, S, w, s) + ch[4 * c] + s_gt[lane];
+        eq = s_eq[lane];
+      }
+      int xf = fa, xe = eq;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int of = __shfl_up(xf, off), oe = __shfl_up(xe, off);
+        if (lane >= off) {
+          xf += of;
+          xe += oe;
+        }
+      }
+      if (lane < nch) {
+        ch[4 * c + 2] = fa_base + xf - fa;
+        ch[4 * c + 3] = tie_base + xe - eq;
+      }
+      fa_base += __shfl(xf, kWave - 1);
+      tie_base += __shfl(xe, kWave - 1);
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    st[3] = (int32_t)T;
+    st[4] = r;
+  }
+}
+
+// Per chunk: keep flags, a block scan in position order and the stores.
+__global__ __launch_bounds__(kMbThreads) void sel_emit_kernel(MbArgs a) {
+  __shared__ uint32_t tot[kMbWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x / a.nc, c = blockIdx.x - row * a.nc;
+  const int S = a.S;
+  const int e_lo = a.n_sink, e_hi = S - a.window;
+  const float* __restrict__ m = a.mass + (size_t)row * S;
+  int32_t* __restrict__ out = a.keep + (size_t)row * a.n_keep;
+  uint32_t T = 0;
+  int r = 0, fa_before, tie_before = 0;
+  if (a.mode == kSelect) {
+    const int32_t* st = a.state + (size_t)row * kStateInts;
+    const int32_t* ch = a.chunk + ((size_t)row * a.nc + c) * 4;
+    T = (uint32_t)st[3];
+    r = st[4];
+    fa_before = ch[2];
+    tie_before = ch[3];
+  } else if (a.mode == kTakeAll) {
+    fa_before = c * a.C;
+  } else {
+    fa_before = forced_before(c * a.C, S, a.window, a.n_sink);
+  }
+  const int p_end = min(S, (c + 1) * a.C);
+  for (int p0 = c * a.C; p0 < p_end; p0 += kSubLen) {
+    const int p = p0 + 4 * tid;
+    bool fa[4], tie[4];
+    if (a.mode == kSelect) {
+      float v[4];
+      load4(m, p, S, a.vec4, v);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = p + q;
+        const bool elig = j >= e_lo && j < e_hi;
+        const uint32_t u = score_key(v[q]);
+        fa[q] = j < S && (!elig || u > T);
+        tie[q] = elig && u == T;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = p + q;
+        fa[q] = j < S && (a.mode == kTakeAll || j < e_lo || j >= e_hi);
+        tie[q] = false;
+      }
+    }
+    // (forced-or-above << 16 | ties) of this thread's four positions; the
+    // sub-chunk totals are at most 1024, so the tie half never carries
+    const uint32_t mine = ((uint32_t)(fa[0] + fa[1] + fa[2] + fa[3]) << 16) |
+                          (uint32_t)(tie[0] + tie[1] + tie[2] + tie[3]);
+    uint32_t x = mine;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const uint32_t o = __shfl_up(x, off);
+      if (lane >= off) x += o;
+    }
+    if (lane == kWave - 1) tot[wave] = x;
+    __syncthreads();
+    uint32_t before = x - mine, all = 0;
+#pragma unroll
+    for (int wv = 0; wv < kMbWaves; ++wv) {
+      const uint32_t t = tot[wv];
+      if (wv < wave) before += t;
+      all += t;
+    }
+    __syncthreads();
+    int fb = fa_before + (int)(before >> 16);
+    int tb = tie_before + (int)(before & 0xFFFFu);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (fa[q] || (tie[q] && tb < r)) {
+        const int slot = fb + min(tb, r);
+        if (slot < a.n_keep) out[slot] = p + q;
+      }
+      fb += fa[q];
+      tb += tie[q];
+    }
+    fa_before += (int)(all >> 16);
+    tie_before += (int)(all & 0xFFFFu);
+  }
+}
+
+// Chunking of the split path: chunk length a multiple of kSubLen, at least
+// 4096, aiming at about 1024 workgroups per launch and at most kMaxChunks
+// chunks per row (the per-row kernels then read at most 2 MB of histograms).
+constexpr int kMaxChunks = 256;
+constexpr int kMinChunk = 4 * kSubLen;
+
+void mb_plan(int64_t rows, int S, int& nc, int& C) {
+  int64_t want = (1024 + rows - 1) / rows;
+  const int64_t most = (S + kMinChunk - 1) / kMinChunk;
+  if (want > most) want = most;
+  if (want > kMaxChunks) want = kMaxChunks;
+  if (want < 1) want = 1;
+  int64_t len = (S + want - 1) / want;
+  len = (len + kMinChunk - 1) / kMinChunk * kMinChunk;
+  C = (int)len;
+  nc = (int)((S + len - 1) / len);
+  if (nc < 1) nc = 1;
+}
+
+// Rows longer than the register kernel holds take the split path.
+bool use_split(int64_t, int S) { return S > 32768; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
 }  // namespace
 
+int64_t select_split_blocks(int64_t rows, int S) {
+  if (rows <= 0 || S <= 0 || !use_split(rows, S)) return 0;
+  int nc, C;
+  mb_plan(rows, S, nc, C);
+  return rows * nc;
+}
+
+size_t select_workspace_bytes(int64_t rows, int S) {
+  if (rows <= 0 || S <= 0 || !use_split(rows, S)) return 0;
+  int nc, C;
+  mb_plan(rows, S, nc, C);
+  return align256((size_t)rows * nc * kBins1 * 4) + align256((size_t)rows * nc * 16) +
+         align256((size_t)rows * kStateInts * 4) + align256((size_t)rows * S * 4);
+}
+
 hipError_t launch_select(const float* mass, int64_t rows, int S, int window, int n_sink,
-                         int top_k, int64_t n_keep, int32_t* keep, hipStream_t stream) {
-  SelArgs a;
+                         int top_k, int64_t n_keep, int32_t* keep, void* workspace,
+                         hipStream_t stream) {
+  // 16-byte loads when every row starts 16-byte aligned
+  const bool vec4 = S % 4 == 0 && reinterpret_cast<uintptr_t>(mass) % 16 == 0;
+  if (!use_split(rows, S)) {
+    SelArgs a;
+    a.mass = mass;
+    a.keep = keep;
+    a.S = S;
+    a.window = window;
+    a.n_sink = n_sink;
+    a.top_k = top_k;
+    a.n_keep = n_keep;
+    const dim3 grid((unsigned)rows), reg_block(kRegThreads);
+    if (S <= kRegThreads * 8)
+      hipLaunchKernelGGL(select_reg_kernel<8>, grid, reg_block, 0, stream, a, vec4);
+    else if (S <= kRegThreads * 16)
+      hipLaunchKernelGGL(select_reg_kernel<16>, grid, reg_block, 0, stream, a, vec4);
+    else
+      hipLaunchKernelGGL(select_reg_kernel<32>, grid, reg_block, 0, stream, a, vec4);
+    return hipGetLastError();
+  }
+  MbArgs a;
   a.mass = mass;
   a.keep = keep;
   a.S = S;
   a.window = window;
   a.n_sink = n_sink;
-  a.top_k = top_k;
+  const int e_hi = S - window;
+  const int n_elig = e_hi > n_sink ? e_hi - n_sink : 0;
+  a.kk = top_k < n_elig ? top_k : n_elig;
+  a.mode = a.kk == 0 ? kTakeNone : (a.kk == n_elig ? kTakeAll : kSelect);
+  mb_plan(rows, S, a.nc, a.C);
   a.n_keep = n_keep;
-  // 16-byte loads when every row starts 16-byte aligned
-  const bool vec4 = S % 4 == 0 && reinterpret_cast<uintptr_t>(mass) % 16 == 0;
-  const dim3 grid((unsigned)rows), reg_block(kRegThreads);
-  if (S <= kRegThreads * 8)
-    hipLaunchKernelGGL(select_reg_kernel<8>, grid, reg_block, 0, stream, a, vec4);
-  else if (S <= kRegThreads * 16)
-    hipLaunchKernelGGL(select_reg_kernel<16>, grid, reg_block, 0, stream, a, vec4);
-  else if (S <= kRegThreads * 32)
-    hipLaunchKernelGGL(select_reg_kernel<32>, grid, reg_block, 0, stream, a, vec4);
-  else
-    hipLaunchKernelGGL(select_kernel, grid, dim3(kSelThreads), 0, stream, a);
+  a.vec4 = vec4;
+  char* ws = static_cast<char*>(workspace);
+  a.hist = reinterpret_cast<int32_t*>(ws);
+  ws += align256((size_t)rows * a.nc * kBins1 * 4);
+  a.chunk = reinterpret_cast<int32_t*>(ws);
+  ws += align256((size_t)rows * a.nc * 16);
+  a.state = reinterpret_cast<int32_t*>(ws);
+  ws += align256((size_t)rows * kStateInts * 4);
+  a.cand = reinterpret_cast<uint32_t*>(ws);
+  const dim3 chunks((unsigned)(rows * a.nc)), per_row((unsigned)rows);
+  if (a.mode == kSelect) {
+    hipLaunchKernelGGL(sel_hist_kernel, chunks, dim3(kMbThreads), 0, stream, a);
+    hipLaunchKernelGGL(sel_bin_kernel, per_row, dim3(kMbThreads), 0, stream, a);
+    hipLaunchKernelGGL(sel_compact_kernel, chunks, dim3(kMbThreads), 0, stream, a);
+    hipLaunchKernelGGL(sel_finish_kernel, per_row, dim3(kFinThreads), 0, stream, a);
+  }
+  hipLaunchKernelGGL(sel_emit_kernel, chunks, dim3(kMbThreads), 0, stream, a);
   return hipGetLastError();
 }
 

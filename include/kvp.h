@@ -67,7 +67,7 @@
  *     call enqueues nothing.  No function prints, throws or aborts, and all
  *     are thread-safe (no global state).
  *   - Sizes: batch >= 0 and 0 <= seq_len <= 2^22 (0 = empty input: nothing
- *     to do, KVP_OK; longer sequences give KVP_ERR_UNSUPPORTED);
+ *     to do, KVP_OK; longer sequences give KVP_EUNSUPPORTED);
  *     n_q_heads, n_kv_heads >= 1 and n_q_heads % n_kv_heads == 0; head_dim
  *     in {64, 128}.  Pointers must be 16-byte aligned.
  */
@@ -85,13 +85,13 @@ extern "C" {
 
 typedef enum {
   KVP_OK = 0,
-  KVP_ERR_INVALID = 1,      /* null/misaligned pointer, negative size, Hq % Hkv != 0, ... */
-  KVP_ERR_UNSUPPORTED = 2,  /* head_dim not in {64, 128}, unknown dtype, size beyond limits */
-  KVP_ERR_WORKSPACE = 3,    /* workspace too small */
-  KVP_ERR_HIP = 4           /* a kernel launch failed (hipGetLastError) */
-} kvp_status;
+  KVP_EINVAL = 1,        /* null/misaligned pointer, negative size, Hq % Hkv != 0, ... */
+  KVP_EUNSUPPORTED = 2,  /* head_dim not in {64, 128}, unknown dtype, size beyond limits */
+  KVP_EWORKSPACE = 3,    /* workspace too small */
+  KVP_EHIP = 4           /* a kernel launch failed (hipGetLastError) */
+} kvp_status_t;
 
-typedef enum { KVP_BF16 = 0, KVP_F32 = 1 } kvp_dtype;
+typedef enum { KVP_BF16 = 0, KVP_F32 = 1 } kvp_dtype_t;
 
 typedef struct {
   int32_t batch;       /* B  */
@@ -99,7 +99,7 @@ typedef struct {
   int32_t n_kv_heads;  /* Hkv */
   int32_t seq_len;     /* S  */
   int32_t head_dim;    /* d  */
-} kvp_dims;
+} kvp_dims_t;
 
 /* Stage 1 — causal log-sum-exp.
  *   lse[b, g, i] = ln sum_{j <= i} exp(scale * <q[b,g,i], k[b, g/G, j]>)
@@ -111,8 +111,8 @@ typedef struct {
  *   lse   : device fp32 [B, Hq, S], written entirely.
  * Rows whose logits span more than the fp32 exponent range are recomputed by
  * an exact per-row fallback, so every finite input yields a finite LSE. */
-kvp_status kvp_lse_fwd(const void* q, const void* k, kvp_dtype dtype, kvp_dims dims,
-                       float scale, float* lse, hipStream_t stream);
+kvp_status_t kvp_lse_fwd(const void* q, const void* k, kvp_dtype_t dtype, kvp_dims_t dims,
+                         float scale, float* lse, hipStream_t stream);
 
 /* Stage 1, sparse — the log-normaliser of the running top-k sparse attention
  * ([KVpop] §3.2: the student's sparse attention keeps, at query q, the sink
@@ -128,9 +128,9 @@ kvp_status kvp_lse_fwd(const void* q, const void* k, kvp_dtype dtype, kvp_dims d
  *                  (window 0, no sinks and no budget).
  * The same MFMA pass as kvp_lse_fwd with the pattern tested per (query, key)
  * pair; rows whose sum leaves the fp32 range are recomputed exactly. */
-kvp_status kvp_lse_sparse(const void* q, const void* k, kvp_dtype dtype, kvp_dims dims, float scale,
-                          const int32_t* rank, const int32_t* cutoff, int32_t window, float* lse,
-                          hipStream_t stream);
+kvp_status_t kvp_lse_sparse(const void* q, const void* k, kvp_dtype_t dtype, kvp_dims_t dims,
+                            float scale, const int32_t* rank, const int32_t* cutoff, int32_t window,
+                            float* lse, hipStream_t stream);
 
 /* Stage 2 — transposed future-attention-mass pass.
  *   mass[b, h, j] = sum_{g : g/G = h} sum_{i = j + window}^{S-1}
@@ -148,9 +148,9 @@ kvp_status kvp_lse_sparse(const void* q, const void* k, kvp_dtype dtype, kvp_dim
  * GPU (short sequences), each group's heads are split over two workgroups
  * that add into the output after a zero fill: two terms, so the sum does not
  * depend on their order.  Either way the result is bitwise reproducible. */
-kvp_status kvp_future_mass(const void* q, const void* k, const float* lse, kvp_dtype dtype,
-                           kvp_dims dims, float scale, int32_t window, float* mass,
-                           hipStream_t stream);
+kvp_status_t kvp_future_mass(const void* q, const void* k, const float* lse, kvp_dtype_t dtype,
+                             kvp_dims_t dims, float scale, int32_t window, float* mass,
+                             hipStream_t stream);
 
 /* Stage 2, per query head.
  *   mass[b, g, j] = sum_{i = j + window}^{S-1} exp(scale * <q[b,g,i], k[b,g/G,j]> - lse[b,g,i])
@@ -158,9 +158,9 @@ kvp_status kvp_future_mass(const void* q, const void* k, const float* lse, kvp_d
  * un-normalised per-head mass m^(h,g) of [KVpop] §3.1 Eq. 2 / App. B.1, the
  * input of the per-head aggregation of Eq. 3.  Arguments as kvp_future_mass
  * except mass: device fp32 [B, Hq, S], written entirely. */
-kvp_status kvp_future_mass_per_head(const void* q, const void* k, const float* lse,
-                                    kvp_dtype dtype, kvp_dims dims, float scale, int32_t window,
-                                    float* mass, hipStream_t stream);
+kvp_status_t kvp_future_mass_per_head(const void* q, const void* k, const float* lse,
+                                      kvp_dtype_t dtype, kvp_dims_t dims, float scale,
+                                      int32_t window, float* mass, hipStream_t stream);
 
 /* Aggregation of the per-head log masses over the query heads of a group
  * ([KVpop] §3.1 Eq. 3 leaves Agg open; App. B.1 uses the log of the mean). */
@@ -168,7 +168,7 @@ typedef enum {
   KVP_AGG_LOG_MEAN = 0,  /* log(eps + (1/G) sum_g m_g)      App. B.1            */
   KVP_AGG_MEAN_LOG = 1,  /* (1/G) sum_g log(eps + m_g)      Eq. 3, Agg = mean   */
   KVP_AGG_MAX_LOG = 2    /* max_g log(eps + m_g)            Eq. 3, Agg = max    */
-} kvp_agg;
+} kvp_agg_t;
 
 /* KVpop target scores ([KVpop] §3.1 Eq. 2-3, App. B.1-B.3), one per key:
  *   m_g[t]  = mass[b, g, t] / N_t (per_head = 1) or the group sum / G
@@ -186,10 +186,10 @@ typedef enum {
  *   score     : device fp32 [B, Hkv, S], written entirely.
  *   dims      : head_dim is not read.
  * Natural logs in fp32.  The scores can be passed to kvp_select_topk. */
-kvp_status kvp_target_scores(const float* mass, int32_t per_head, kvp_dims dims, int32_t window,
-                             int32_t normalize, kvp_agg agg, float eps, int32_t query,
-                             int32_t decay_step, const float* log_gamma, float* score,
-                             hipStream_t stream);
+kvp_status_t kvp_target_scores(const float* mass, int32_t per_head, kvp_dims_t dims, int32_t window,
+                               int32_t normalize, kvp_agg_t agg, float eps, int32_t query,
+                               int32_t decay_step, const float* log_gamma, float* score,
+                               hipStream_t stream);
 
 /* Size of every KV head's keep-set ([KVpop] §3 Eq. 1, budget B = s + w + k,
  * clipped to the sequence):
@@ -209,12 +209,28 @@ int64_t kvp_keep_count(int64_t seq_len, int64_t window, int64_t n_sink, int64_t 
  * fp32 scores of either sign, e.g. kvp_target_scores; -0 equals +0, -inf is
  * allowed, NaN gives an unspecified keep-set.  Selection compares exactly,
  * through an order-preserving integer key of every fp32 value.
- *   mass : device fp32 [B, Hkv, S] scores (the batch dimension may also
- *          stack layers: any number of independent [Hkv, S] rows).
- *   keep : device int32 [B, Hkv, kvp_keep_count(S, window, n_sink, top_k)].
- *   dims : only batch, n_kv_heads and seq_len are read. */
-kvp_status kvp_select_topk(const float* mass, kvp_dims dims, int32_t window, int32_t n_sink,
-                           int32_t top_k, int32_t* keep, hipStream_t stream);
+ *   mass      : device fp32 [B, Hkv, S] scores (the batch dimension may also
+ *               stack layers: any number of independent [Hkv, S] rows).
+ *   keep      : device int32 [B, Hkv, kvp_keep_count(S, window, n_sink, top_k)].
+ *   workspace : device scratch of at least kvp_select_workspace_bytes(dims,
+ *               top_k) bytes, 256-byte aligned, owned by the caller (NULL
+ *               allowed when that is 0); contents on entry and exit are
+ *               unspecified.  KVP_EWORKSPACE if workspace_bytes is smaller.
+ *   dims      : only batch, n_kv_heads and seq_len are read.
+ * Rows of up to 32768 scores run one workgroup per row with no workspace;
+ * longer rows are split over many workgroups (chunks of >= 4096 scores)
+ * whose histograms, candidate keys and per-chunk counts live in the
+ * workspace.  Integer counts only, so the result is exact and reproducible. */
+kvp_status_t kvp_select_topk(const float* mass, kvp_dims_t dims, int32_t window, int32_t n_sink,
+                             int32_t top_k, int32_t* keep, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* Bytes of device workspace kvp_select_topk needs for `dims` (batch,
+ * n_kv_heads and seq_len are read) and `top_k`: 0 for rows of at most 32768
+ * scores; otherwise, with R = batch * n_kv_heads rows split into c chunks
+ * each, about R * (8 KiB * c + 4 * seq_len) (histograms and candidate keys).
+ * Pure host function; 0 for invalid arguments. */
+size_t kvp_select_workspace_bytes(kvp_dims_t dims, int32_t top_k);
 
 /* Number of query blocks [block_start + t * block_len, block_start + (t+1) *
  * block_len) that intersect [0, seq_len): ceil((S - block_start) / block_len),
@@ -238,16 +254,17 @@ int64_t kvp_block_count(int64_t seq_len, int64_t block_start, int64_t block_len)
  *   q, k, lse : as kvp_future_mass (lse from kvp_lse_fwd).
  *   window    : >= 0 (0 in [FKV]; a query counts for a key iff i >= j + window).
  *   block_start, block_len : >= 0 and >= 1; multiples of 32 (else
- *               KVP_ERR_UNSUPPORTED).
+ *               KVP_EUNSUPPORTED).
  *   block_scores  : device fp32 [B, U, n_blocks, S] or NULL (not written).
  *   future_scores : device fp32 [B, U, n_blocks, S], written entirely;
  *                   U = Hkv (per_head = 0) or Hq (per_head = 1).
  * The same transposed pass as kvp_future_mass with the column sums flushed at
  * every block boundary: no S x S map, no atomics, bitwise reproducible. */
-kvp_status kvp_block_future_scores(const void* q, const void* k, const float* lse,
-                                   kvp_dtype dtype, kvp_dims dims, float scale, int32_t window,
-                                   int32_t per_head, int32_t block_start, int32_t block_len,
-                                   float* block_scores, float* future_scores, hipStream_t stream);
+kvp_status_t kvp_block_future_scores(const void* q, const void* k, const float* lse,
+                                     kvp_dtype_t dtype, kvp_dims_t dims, float scale,
+                                     int32_t window, int32_t per_head, int32_t block_start,
+                                     int32_t block_len, float* block_scores, float* future_scores,
+                                     hipStream_t stream);
 
 /* LKV Soft-TopK forward ([LKV] §3.2 "The Differentiable Soft-TopK Operator",
  * App. A.1).  Per row r of n scores x, with z = x / tau:
@@ -266,21 +283,21 @@ kvp_status kvp_block_future_scores(const void* q, const void* k, const float* ls
  * and confirm it, and form the sums and y, in fp64; longer rows find it by
  * bisection on the scores' bit patterns (at most 32 fp64 reductions).  x
  * must be finite. */
-kvp_status kvp_soft_topk_fwd(const float* x, int64_t rows, int32_t n, const float* k, float tau,
-                             float* y, float* lam, hipStream_t stream);
+kvp_status_t kvp_soft_topk_fwd(const float* x, int64_t rows, int32_t n, const float* k, float tau,
+                               float* y, float* lam, hipStream_t stream);
 
 /* Soft-TopK backward ([LKV] App. A.2): with f'(u) = e^{-|u|}/2, u_i = z_i - lam,
  * A = sum_i dy_i f'(u_i), B = sum_i f'(u_i):
  *   dx[r,j] = f'(u_j) (dy[r,j] - A / B) / tau,   dk[r] = A / B.
  *   x, lam : as passed to / returned by kvp_soft_topk_fwd;  dy : device fp32
  *   [rows, n];  dx : device fp32 [rows, n];  dk : device fp32 [rows] or NULL. */
-kvp_status kvp_soft_topk_bwd(const float* x, const float* lam, const float* dy, int64_t rows,
-                             int32_t n, float tau, float* dx, float* dk, hipStream_t stream);
+kvp_status_t kvp_soft_topk_bwd(const float* x, const float* lam, const float* dy, int64_t rows,
+                               int32_t n, float tau, float* dx, float* dk, hipStream_t stream);
 
 /* Bytes of device workspace kvp_running_cutoff needs for `dims` (batch,
  * n_kv_heads and seq_len are read) and `n_sink`: 20 * B * Hkv * (S - min(s, S)).
  * Pure host function; 0 for invalid arguments. */
-size_t kvp_running_cutoff_workspace_bytes(kvp_dims dims, int32_t n_sink);
+size_t kvp_running_cutoff_workspace_bytes(kvp_dims_t dims, int32_t n_sink);
 
 /* Running top-k cutoff ([KVpop] §3.2 "Efficient Target Implementation", the
  * paragraphs on running top-k sparse attention and on its kernel; Appendix I).
@@ -304,16 +321,16 @@ size_t kvp_running_cutoff_workspace_bytes(kvp_dims dims, int32_t n_sink);
  *               kvp_running_cutoff_workspace_bytes(dims, n_sink) bytes, 4-byte
  *               aligned, owned by the caller (NULL allowed when that is 0);
  *               its contents on entry and exit are unspecified.
- *               KVP_ERR_WORKSPACE if workspace_bytes is smaller.
+ *               KVP_EWORKSPACE if workspace_bytes is smaller.
  *   dims      : only batch, n_kv_heads and seq_len are read.
  * Results are exact (integer ranks); two kernels: a per-row stable radix
  * sort, then a per-row sweep over q whose cutoff only moves down. */
-kvp_status kvp_running_cutoff(const float* score, kvp_dims dims, int32_t window, int32_t n_sink,
-                              int32_t top_k, int32_t* rank, int32_t* cutoff, void* workspace,
-                              size_t workspace_bytes, hipStream_t stream);
+kvp_status_t kvp_running_cutoff(const float* score, kvp_dims_t dims, int32_t window, int32_t n_sink,
+                                int32_t top_k, int32_t* rank, int32_t* cutoff, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
 
 /* Static string for a status code. */
-const char* kvp_status_string(kvp_status status);
+const char* kvp_status_string(kvp_status_t status);
 
 /* Library ABI version (incremented on any signature change). */
 int32_t kvp_abi_version(void);

@@ -36,7 +36,7 @@ def test_header_declares_the_three_stages():
               "kvp_status_string", "kvp_abi_version", "kvp_future_mass_per_head",
               "kvp_target_scores", "kvp_running_cutoff", "kvp_running_cutoff_workspace_bytes",
               "kvp_block_count", "kvp_block_future_scores", "kvp_soft_topk_fwd",
-              "kvp_soft_topk_bwd", "kvp_lse_sparse"):
+              "kvp_soft_topk_bwd", "kvp_lse_sparse", "kvp_select_workspace_bytes"):
         assert n in names
 
 
@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.kvp_abi_version() == 6
+    assert lib.kvp_abi_version() == 7
     for code in range(5):
         assert lib.kvp_status_string(code)
     assert lib.kvp_status_string(99) == b"unknown status"
@@ -96,19 +96,47 @@ def test_empty_inputs_are_noops(lib):
     assert lse_call(lib, q=None, k=None, out=None, d=dims(B=0)) == OK
     assert lse_call(lib, d=dims(S=0)) == OK
     assert mass_call(lib, d=dims(S=0)) == OK
-    assert lib.kvp_select_topk(None, dims(B=0), 4, 4, 8, None, None) == OK
-    assert lib.kvp_select_topk(None, dims(S=0), 4, 4, 8, None, None) == OK
+    assert lib.kvp_select_topk(None, dims(B=0), 4, 4, 8, None, None, 0, None) == OK
+    assert lib.kvp_select_topk(None, dims(S=0), 4, 4, 8, None, None, 0, None) == OK
 
 
 def test_select_validation(lib):
-    sel = lib.kvp_select_topk
-    assert sel(None, dims(), 4, 4, 8, FAKE, None) == INVALID
-    assert sel(FAKE, dims(), 4, 4, 8, None, None) == INVALID
-    assert sel(FAKE, dims(), -1, 4, 8, FAKE, None) == INVALID
-    assert sel(FAKE, dims(), 4, -1, 8, FAKE, None) == INVALID
-    assert sel(FAKE, dims(), 4, 4, -8, FAKE, None) == INVALID
-    assert sel(FAKE + 1, dims(), 4, 4, 8, FAKE, None) == INVALID
-    assert sel(FAKE, dims(Hkv=0), 4, 4, 8, FAKE, None) == INVALID
+    def sel(mass, d, w, s, k, keep, ws=None, ws_bytes=0):
+        return lib.kvp_select_topk(mass, d, w, s, k, keep, ws, ws_bytes, None)
+    assert sel(None, dims(), 4, 4, 8, FAKE) == INVALID
+    assert sel(FAKE, dims(), 4, 4, 8, None) == INVALID
+    assert sel(FAKE, dims(), -1, 4, 8, FAKE) == INVALID
+    assert sel(FAKE, dims(), 4, -1, 8, FAKE) == INVALID
+    assert sel(FAKE, dims(), 4, 4, -8, FAKE) == INVALID
+    assert sel(FAKE + 1, dims(), 4, 4, 8, FAKE) == INVALID
+    assert sel(FAKE, dims(Hkv=0), 4, 4, 8, FAKE) == INVALID
+    assert sel(FAKE, dims(S=(1 << 22) + 1), 4, 4, 8, FAKE) == UNSUPPORTED
+    # rows longer than 32768 need the workspace
+    long_d = dims(B=1, Hkv=8, S=131072)
+    need = lib.kvp_select_workspace_bytes(long_d, 2048)
+    assert need > 0
+    assert sel(FAKE, long_d, 1024, 4, 2048, FAKE) == WORKSPACE
+    assert sel(FAKE, long_d, 1024, 4, 2048, FAKE, None, need - 1) == WORKSPACE
+    assert sel(FAKE, long_d, 1024, 4, 2048, FAKE, None, need) == INVALID      # null workspace
+    assert sel(FAKE, long_d, 1024, 4, 2048, FAKE, FAKE + 16, need) == INVALID  # not 256-aligned
+
+
+def test_select_workspace_bytes(lib):
+    ws = lib.kvp_select_workspace_bytes
+    # rows of up to 32768 scores need none
+    for S in (0, 1, 256, 4096, 32768):
+        assert ws(dims(B=36, Hkv=8, S=S), 16384) == 0
+    assert ws(dims(S=-1), 8) == 0 and ws(dims(), -1) == 0 and ws(dims(Hkv=0), 8) == 0
+    assert ws(dims(S=(1 << 22) + 1), 8) == 0
+    # longer rows: histograms (8 KiB per chunk of >= 4096 scores) and a
+    # candidate key per score, per row; it grows with the rows
+    for rows, S in ((1, 32769), (8, 131072), (3, 1 << 20), (1, 1 << 22)):
+        n = ws(dims(B=rows, Hkv=1, S=S), 1)
+        assert n % 256 == 0
+        assert n >= rows * 4 * S
+        assert n <= rows * (4 * S + 8192 * 256 + 4096) + 4 * 256
+    assert ws(dims(B=2, Hkv=8, S=131072), 1) > ws(dims(B=1, Hkv=8, S=131072), 1)
+    assert kvp.select_workspace_bytes(8, 131072, 2048) == ws(dims(B=8, Hkv=1, S=131072), 2048)
 
 
 def test_keep_count_matches_oracle(lib, orc):
