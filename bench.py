@@ -16,6 +16,11 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
                launch over its average launch time, measured with HIP events
                on the stream it runs on, against the bf16 dense MFMA peak
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
+               (with the parity of the GPU's layer 0 on that sample: LSE and
+               mass errors, keep-set status)
+  mfma_probe   the sustained bf16 matrix-core rate of this GPU (a pure-MFMA
+               kernel) and its core clock under that load; roofline also
+               states the mass kernel against that measured peak
   next_rows    after the timed steps: the per-head mass pass, the KVpop target
                epilogue, the running top-k cutoff and the Golden-Eviction
                block / future scores on the same layers
@@ -24,6 +29,8 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
   hash to the value recorded there
 
     python bench.py [--steps K] [--warmup W] [--workload N] [--no-cpu-baseline]
+                    [--batch B] [--hq H] [--hkv H] [--seq S] [--dim D]
+                    [--window W] [--sinks N] [--topk K] [--seed N]
     python bench.py --copy-probe BYTES   # plain copy kernel, for counter scaling
 """
 from __future__ import annotations
@@ -99,13 +106,17 @@ def copy_probe(nbytes: int, reps: int) -> None:
     print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}))
 
 
-def cpu_baseline(wl, li0, n_heads: int, max_pairs: float = 4.5e9) -> dict:
+def cpu_baseline(wl, li0, n_heads: int, gpu=None, max_pairs: float = 4.5e9) -> dict:
     """The CPU oracle (dense fp64 softmax rows + explicit column sums), as it
     stands, on whole (batch 0, KV head) units 0 .. n_heads-1 of layer 0: the
     query rows of their G query heads from row_lo on, row_lo = 0 unless that
     would exceed max_pairs future-mass pairs (long sequences: the last rows,
     each computed in full).  Returns the future-mass pairs per second the
-    sample covers (its LSE work included in the time)."""
+    sample covers (its LSE work included in the time).  With ``gpu`` = the
+    GPU's layer-0 (lse [B,Hq,S], mass [B,Hkv,S], keep [B,Hkv,n]) as numpy
+    arrays, also the parity of the sample: LSE of its rows, masses of the keys
+    its rows complete, and (whole units only) the keep-sets."""
+    import numpy as np
     import oracle
     S, w, G = wl.S, wl.window, wl.G
     n_heads = max(1, min(n_heads, wl.Hkv))
@@ -126,16 +137,115 @@ def cpu_baseline(wl, li0, n_heads: int, max_pairs: float = 4.5e9) -> dict:
                 hi = mid
         row_lo = hi
     threads = oracle.default_threads()
+    refs = []
     t0 = time.perf_counter()
     for h in range(n_heads):
-        oracle.future_mass(li0.q, li0.k, w, b_only=0, h_only=h, row_lo=row_lo, nthreads=threads)
+        refs.append(oracle.future_mass(li0.q, li0.k, w, b_only=0, h_only=h, row_lo=row_lo,
+                                       nthreads=threads))
     dt = time.perf_counter() - t0
     pairs = pairs_from(row_lo)
     rows = "all" if row_lo == 0 else f"the last {S - row_lo} of"
-    return {"value": pairs / dt / 1e9, "unit": "G query-key pairs/s", "cores": threads,
-            "kind": "oracle", "seconds": round(dt, 3),
-            "sample": (f"layer 0, batch 0, KV heads 0..{n_heads - 1} ({n_heads * G} query heads), "
-                       f"{rows} {S} query rows: {pairs} future-mass pairs, LSE included")}
+    out = {"value": pairs / dt / 1e9, "unit": "G query-key pairs/s", "cores": threads,
+           "kind": "oracle", "seconds": round(dt, 3),
+           "sample": (f"layer 0, batch 0, KV heads 0..{n_heads - 1} ({n_heads * G} query heads), "
+                      f"{rows} {S} query rows: {pairs} future-mass pairs, LSE included")}
+    if gpu is not None:
+        lse_g, mass_g, keep_g = gpu
+        lse_err, rel_err, n_bad, statuses = 0.0, 0.0, 0, []
+        key_lo = max(0, row_lo - w)  # keys whose every future row is in the sample
+        for h, ref in enumerate(refs):
+            g0 = h * G
+            d = np.abs(lse_g[0, g0:g0 + G, row_lo:] - ref["lse"][0, g0:g0 + G, row_lo:])
+            lse_err = max(lse_err, float(d.max()))
+            o = ref["mass"][0, h, key_lo:]
+            g = mass_g[0, h, key_lo:].astype(np.float64)
+            n_bad += int((np.abs(g - o) > 1e-5 + 2e-3 * np.abs(o)).sum())
+            nz = o > 0
+            if nz.any():
+                rel_err = max(rel_err, float((np.abs(g[nz] - o[nz]) / o[nz]).max()))
+            if row_lo == 0:
+                m = ref["mass"][:, h:h + 1]
+                exact = oracle.select(m, w, wl.n_sink, wl.top_k)[0, 0]
+                statuses.append(keep_status(keep_g[0, h], m[0, 0], S, w, wl.n_sink, wl.top_k,
+                                            exact))
+        out["parity"] = {
+            "lse_max_abs_err": lse_err, "lse_tol": 1e-4,
+            "mass_max_rel_err": rel_err, "mass_violations": n_bad,
+            "mass_tol": "1e-5 + 2e-3 |oracle|", "mass_keys": f"{key_lo}..{S - 1}",
+            "keep": statuses if statuses else "not compared (partial unit)",
+            "ok": lse_err <= 1e-4 and n_bad == 0 and all(x != "differs" for x in statuses)}
+    return out
+
+
+def mfma_probe(torch, blocks: int = 256, iters: int = 20000, reps: int = 5) -> dict:
+    """The matrix-core probe (libkvp_probe.so): best rate of `reps` launches
+    of back-to-back bf16 MFMAs on every CU, and the mean core clock of its
+    workgroups (core-clock counter over the constant-rate counter)."""
+    import ctypes
+    import future_attention_scoring_kvp_amd as kvp
+    path = os.path.join(os.path.dirname(kvp.library_path()), "libkvp_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.kvp_probe_mfma_bf16.restype = ctypes.c_int
+    lib.kvp_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+    lib.kvp_probe_flops.restype = ctypes.c_double
+    lib.kvp_probe_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.kvp_probe_wall_clock_khz.restype = ctypes.c_int
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    stamps = torch.zeros(blocks * 4, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+    best_ms, clocks = None, []
+    for r in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rc = lib.kvp_probe_mfma_bf16(blocks, iters, sink.data_ptr(), stamps.data_ptr(),
+                                     int(stream.cuda_stream))
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if rc != 0:
+            raise RuntimeError(f"mfma probe failed ({rc})")
+        if r == 0:
+            continue  # warm-up
+        ms = e0.elapsed_time(e1)
+        best_ms = ms if best_ms is None else min(best_ms, ms)
+        st = stamps.view(blocks, 4).cpu().double()
+        clocks.append(((st[:, 1] - st[:, 0]) / (st[:, 3] - st[:, 2])).mean().item())
+    khz = lib.kvp_probe_wall_clock_khz()
+    tflops = lib.kvp_probe_flops(blocks, iters) / (best_ms * 1e-3) / 1e12
+    ghz = sum(clocks) / len(clocks) * khz * 1e3 / 1e9 if khz > 0 else None
+    log(f"bench: MFMA probe {tflops:.1f} TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of the "
+        f"datasheet peak), core clock {ghz:.3f} GHz" if ghz else
+        f"bench: MFMA probe {tflops:.1f} TFLOP/s")
+    return {"tflops": round(tflops, 2), "clock_ghz": round(ghz, 3) if ghz else None,
+            "frac_of_datasheet": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "kernel": f"{blocks} workgroups x 8 waves x {16 * iters} v_mfma_f32_32x32x16_bf16, "
+                      f"register operands; best of {reps}"}
+
+
+def keep_status(keep, mass, S, w, s, k, exact) -> str:
+    """'exact' when the GPU keep-set equals the oracle's; 'tie-band' when it
+    differs only among tokens whose oracle masses lie within the mass
+    tolerance of the k-th one (and the k-th and (k+1)-th are that close);
+    'differs' otherwise."""
+    import numpy as np
+    if np.array_equal(keep, exact):
+        return "exact"
+    tol = lambda v: 1e-5 + 2e-3 * abs(v)  # noqa: E731
+    elig = np.arange(s, S - w) if S - w > s else np.arange(0)
+    kk = min(k, len(elig))
+    if kk in (0, len(elig)) or len(keep) != len(exact):
+        return "differs"
+    order = elig[np.lexsort((elig, -mass[elig]))]
+    vk, vk1 = mass[order[kk - 1]], mass[order[kk]]
+    if vk - vk1 > tol(vk):
+        return "differs"
+    fixed = set(range(min(s, S))) | set(range(max(0, S - w), S))
+    chosen = set(keep.tolist()) - fixed
+    if not fixed <= set(keep.tolist()) or not chosen <= set(elig.tolist()):
+        return "differs"
+    above = set(elig[mass[elig] > vk + tol(vk)].tolist())
+    below = set(elig[mass[elig] < vk - tol(vk)].tolist())
+    return "tie-band" if above <= chosen and not (below & chosen) else "differs"
 
 
 def next_rows(kvp, torch, wl, L, q_all, k_all, lse_all, stream) -> dict:
@@ -248,6 +358,14 @@ def main() -> int:
     ap.add_argument("--cpu-heads", type=int, default=2,
                     help="whole KV heads of layer 0 in the oracle sample")
     ap.add_argument("--no-extras", action="store_true", help="skip the next_rows timings")
+    ap.add_argument("--no-probe", action="store_true", help="skip the MFMA peak probe")
+    for name, field, what in (("batch", "B", "batch"), ("hq", "Hq", "query heads"),
+                              ("hkv", "Hkv", "KV heads"), ("seq", "S", "sequence length"),
+                              ("dim", "D", "head dimension"), ("window", "window", "window w"),
+                              ("sinks", "n_sink", "sink tokens s"), ("topk", "top_k", "budget k"),
+                              ("seed", "seed", "base seed of the input generator")):
+        ap.add_argument(f"--{name}", dest=f"ov_{field}", type=int, default=None,
+                        help=f"override the workload's {what}")
     ap.add_argument("--sha", action="store_true", help="print the mass kernel sources' sha256")
     ap.add_argument("--copy-probe", type=int, default=0)
     ap.add_argument("--copy-reps", type=int, default=5)
@@ -255,8 +373,8 @@ def main() -> int:
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the path has no multi-GPU mode "
-              "(each (layer, batch, KV head) unit is independent; see the sharding notes)",
-              file=sys.stderr)
+              "(each (layer, batch, KV head) unit is independent and would shard with no "
+              "exchange)", file=sys.stderr)
         return 2
 
     if args.sha:
@@ -272,6 +390,9 @@ def main() -> int:
 
     kvp.load_library()  # fails loudly if the HIP library is not built
     wl = kvp_inputs.workload(args.workload)
+    overrides = {k[3:]: v for k, v in vars(args).items() if k.startswith("ov_") and v is not None}
+    if overrides:
+        wl = wl.with_(**overrides)
     L = args.layers or wl.layers
     B, Hq, Hkv, S, D, G = wl.B, wl.Hq, wl.Hkv, wl.S, wl.D, wl.G
     w, s, k = wl.window, wl.n_sink, wl.top_k
@@ -297,6 +418,8 @@ def main() -> int:
     mass_all = torch.empty((L, B, Hkv, S), dtype=torch.float32, device=dev)
     n_keep = kvp.keep_count(S, w, s, k)
     keep_all = torch.empty((L * B, Hkv, n_keep), dtype=torch.int32, device=dev)
+    sel_ws_bytes = kvp.select_workspace_bytes(L * B * Hkv, S, k)
+    sel_ws = torch.empty(sel_ws_bytes, dtype=torch.uint8, device=dev) if sel_ws_bytes else None
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -311,7 +434,7 @@ def main() -> int:
             kvp.future_mass(q_all[l], k_all[l], lse_all[l], w, out=mass_all[l])
             if events is not None:
                 events[l][2].record(stream)
-        kvp.select_topk(mass_all.view(L * B, Hkv, S), w, s, k, out=keep_all)
+        kvp.select_topk(mass_all.view(L * B, Hkv, S), w, s, k, out=keep_all, workspace=sel_ws)
         if events is not None:
             events[L][0].record(stream)
 
@@ -369,7 +492,8 @@ def main() -> int:
         "data": "synthetic (seeded N(0,1) Q/K with the workload's heavy-hitter recipe)",
         "config": {"workload": wl.name, "layers": L, "batch": B, "n_q_heads": Hq,
                    "n_kv_heads": Hkv, "seq_len": S, "head_dim": D, "window": w,
-                   "n_sink": s, "top_k": k, "parallelism": "none (1 GPU)"},
+                   "n_sink": s, "top_k": k, "seed": wl.layer_seed(0),
+                   "overrides": overrides or None, "parallelism": "none (1 GPU)"},
         "stages_ms": {"lse_per_layer": round(lse_launch_ms, 4),
                       "mass_per_layer": round(mass_launch_ms, 4),
                       "select_all_layers": round(sel_launch_ms, 4)},
@@ -381,11 +505,19 @@ def main() -> int:
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(wl.name)},
     }
+    if not args.no_probe:
+        probe = mfma_probe(torch)
+        out["mfma_probe"] = probe
+        out["roofline"]["measured_peak"] = probe["tflops"]
+        out["roofline"]["frac_measured_peak"] = round(achieved / probe["tflops"], 4)
     if not args.no_extras:
         out["next_rows"] = next_rows(kvp, torch, wl, L, q_all, k_all, lse_all, stream)
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(wl, li0, args.cpu_heads)
+        gpu0 = (lse_all[0].cpu().numpy(), mass_all[0].cpu().numpy(),
+                keep_all[:B].cpu().numpy())
+        out["cpu_baseline"] = cpu_baseline(wl, li0, args.cpu_heads, gpu=gpu0)
+        log(f"bench: parity of layer 0 on the oracle's sample: {out['cpu_baseline']['parity']}")
     print(json.dumps(out), flush=True)
     return 0
 
