@@ -40,8 +40,9 @@ from typing import Optional
 import torch
 
 __all__ = ["lse_fwd", "lse_sparse", "future_mass", "future_mass_per_head", "target_scores",
-           "select_topk", "select_workspace_bytes", "keep_count", "running_cutoff", "block_count",
-           "block_future_scores", "soft_topk", "soft_topk_backward", "KvpError", "library_path", "load_library", "AGG_LOG_MEAN",
+           "select_topk", "select_topk_noalloc", "select_workspace_bytes", "keep_count",
+           "running_cutoff", "block_count", "block_future_scores", "soft_topk",
+           "soft_topk_backward", "KvpError", "library_path", "load_library", "AGG_LOG_MEAN",
            "AGG_MEAN_LOG", "AGG_MAX_LOG"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -93,6 +94,8 @@ def load_library():
             lib.kvp_select_topk.restype = ctypes.c_int
             lib.kvp_select_topk.argtypes = [vp, _Dims, i32, i32, i32, vp, vp, ctypes.c_size_t,
                                             vp]
+            lib.kvp_select_topk_noalloc.restype = ctypes.c_int
+            lib.kvp_select_topk_noalloc.argtypes = [vp, _Dims, i32, i32, i32, vp, vp]
             lib.kvp_select_workspace_bytes.restype = ctypes.c_size_t
             lib.kvp_select_workspace_bytes.argtypes = [_Dims, i32]
             lib.kvp_block_count.restype = i64
@@ -328,6 +331,27 @@ def select_topk(mass: torch.Tensor, window: int, n_sink: int, top_k: int,
     _check(lib.kvp_select_topk(mass.data_ptr(), d, int(window), int(n_sink), int(top_k),
                                out.data_ptr(), ws_ptr, ws_bytes, _stream_ptr(stream)),
            "kvp_select_topk")
+    return out
+
+
+def select_topk_noalloc(mass: torch.Tensor, window: int, n_sink: int, top_k: int,
+                        out: torch.Tensor, stream=None) -> torch.Tensor:
+    """select_topk for callers that cannot allocate (e.g. under graph
+    capture): ``out`` must be given; the split path's state lives in the
+    library's own 32 MiB array per GPU, so calls that overlap on one GPU
+    race."""
+    lib = load_library()
+    _require_device(mass, out)
+    if mass.dtype != torch.float32 or mass.dim() < 1:
+        raise KvpError("mass must be fp32 [..., S]")
+    S = mass.shape[-1]
+    rows = mass.numel() // S if S else 0
+    shape = (*mass.shape[:-1], keep_count(S, window, n_sink, top_k))
+    if out.dtype != torch.int32 or tuple(out.shape) != shape:
+        raise KvpError(f"keep out must be int32 {shape}")
+    _check(lib.kvp_select_topk_noalloc(mass.data_ptr(), _Dims(rows, 1, 1, S, 128), int(window),
+                                       int(n_sink), int(top_k), out.data_ptr(),
+                                       _stream_ptr(stream)), "kvp_select_topk_noalloc")
     return out
 
 

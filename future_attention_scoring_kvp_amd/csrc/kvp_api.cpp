@@ -196,6 +196,33 @@ kvp_status_t kvp_select_topk(const float* mass, kvp_dims_t dims, int32_t window,
   return from_hip(kvp::launch_select(mass, rows, S, w, s, top_k, n_keep, keep, workspace, stream));
 }
 
+kvp_status_t kvp_select_topk_noalloc(const float* mass, kvp_dims_t dims, int32_t window,
+                                     int32_t n_sink, int32_t top_k, int32_t* keep,
+                                     hipStream_t stream) {
+  if (dims.batch < 0 || dims.seq_len < 0 || dims.n_kv_heads < 1) return KVP_EINVAL;
+  if (window < 0 || n_sink < 0 || top_k < 0) return KVP_EINVAL;
+  if (dims.seq_len > kMaxSeq) return KVP_EUNSUPPORTED;
+  const int64_t rows = int64_t(dims.batch) * dims.n_kv_heads;
+  if (rows > kMaxBlocks || kvp::select_split_blocks(rows, dims.seq_len) > kMaxBlocks)
+    return KVP_EUNSUPPORTED;
+  const int64_t n_keep = kvp_keep_count(dims.seq_len, window, n_sink, top_k);
+  if (rows == 0 || dims.seq_len == 0) return KVP_OK;
+  if (!mass || !keep || !aligned(mass, 4) || !aligned(keep, 4)) return KVP_EINVAL;
+  const size_t need = kvp::select_workspace_bytes(rows, dims.seq_len);
+  static_assert(kvp::kSelectScratchBytes == KVP_SELECT_NOALLOC_MAX_WORKSPACE,
+                "the header states the size of the library's own workspace");
+  if (need > kvp::kSelectScratchBytes) return KVP_EWORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = kvp::select_scratch(&ws);
+    if (e != hipSuccess) return KVP_EHIP;
+  }
+  const int S = dims.seq_len;
+  const int w = window > S ? S : window;
+  const int s = n_sink > S ? S : n_sink;
+  return from_hip(kvp::launch_select(mass, rows, S, w, s, top_k, n_keep, keep, ws, stream));
+}
+
 int64_t kvp_block_count(int64_t seq_len, int64_t block_start, int64_t block_len) {
   if (seq_len < 0 || block_start < 0 || block_len < 1) return -1;
   return seq_len > block_start ? (seq_len - block_start + block_len - 1) / block_len : 0;

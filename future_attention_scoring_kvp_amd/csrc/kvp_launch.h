@@ -50,6 +50,11 @@ int64_t select_split_blocks(int64_t rows, int S);
 hipError_t launch_select(const float* mass, int64_t rows, int S, int window, int n_sink,
                          int top_k, int64_t n_keep, int32_t* keep, void* workspace,
                          hipStream_t stream);
+// The library's own fixed workspace for the selection (a device array of
+// kSelectScratchBytes per GPU): its device address on the current device,
+// looked up once per device.  Calls that use it on one GPU share it.
+constexpr size_t kSelectScratchBytes = size_t(32) << 20;
+hipError_t select_scratch(void** ptr);
 
 // Running top-k cutoff: rank [rows, S] and cutoff [rows, S] (int32) from
 // scores [rows, S]; workspace of cutoff_workspace_bytes(rows, S, n_sink).

@@ -36,6 +36,8 @@
 //                       over the candidates give T and r; per chunk, the kept
 //                       and tie counts before it;
 //   sel_emit_kernel     per chunk, flags, a block scan and the stores.
+#include <mutex>
+
 #include "kvp_device.h"
 #include "kvp_launch.h"
 
@@ -770,6 +772,38 @@ hipError_t launch_select(const float* mass, int64_t rows, int S, int window, int
   }
   hipLaunchKernelGGL(sel_emit_kernel, chunks, dim3(kMbThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+// ---- the same selection for callers that cannot allocate: the split path's
+// state in a fixed device array of this library (one copy per GPU)
+
+namespace {
+
+__device__ __align__(256) unsigned char scratch[kSelectScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+hipError_t select_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    // the device address of this GPU's copy of the array; the name itself is
+    // only a host-side stand-in and must never reach a kernel
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace kvp

@@ -65,7 +65,8 @@
  *     even) as they are loaded, so both dtypes run the same bf16 arithmetic.
  *   - Validation is synchronous and happens before any launch; a rejected
  *     call enqueues nothing.  No function prints, throws or aborts, and all
- *     are thread-safe (no global state).
+ *     are thread-safe; only kvp_select_topk_noalloc keeps state (its
+ *     per-GPU device array, see there).
  *   - Sizes: batch >= 0 and 0 <= seq_len <= 2^22 (0 = empty input: nothing
  *     to do, KVP_OK; longer sequences give KVP_EUNSUPPORTED);
  *     n_q_heads, n_kv_heads >= 1 and n_q_heads % n_kv_heads == 0; head_dim
@@ -224,6 +225,26 @@ int64_t kvp_keep_count(int64_t seq_len, int64_t window, int64_t n_sink, int64_t 
 kvp_status_t kvp_select_topk(const float* mass, kvp_dims_t dims, int32_t window, int32_t n_sink,
                              int32_t top_k, int32_t* keep, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
+
+/* kvp_select_topk for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments and results without the workspace, which instead is a
+ * fixed device array inside the library of KVP_SELECT_NOALLOC_MAX_WORKSPACE
+ * bytes (32 MiB), one copy per GPU, held until the process ends.  The call
+ * allocates nothing (no hipMalloc / hipFree, no allocating library routine);
+ * its first call on a GPU looks up that GPU's copy once.
+ *   KVP_EWORKSPACE if kvp_select_workspace_bytes(dims, top_k) exceeds
+ *   KVP_SELECT_NOALLOC_MAX_WORKSPACE (e.g. more than about 8M scores in all
+ *   in rows longer than 32768); nothing is launched then.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on the same GPU (different streams or host threads without ordering)
+ * race and give undefined keep-sets.  Calls ordered on one stream are safe:
+ * no part of the array needs to start at zero, every region is written before
+ * it is read in each call. */
+#define KVP_SELECT_NOALLOC_MAX_WORKSPACE ((size_t)32 << 20)
+kvp_status_t kvp_select_topk_noalloc(const float* mass, kvp_dims_t dims, int32_t window,
+                                     int32_t n_sink, int32_t top_k, int32_t* keep,
+                                     hipStream_t stream);
 
 /* Bytes of device workspace kvp_select_topk needs for `dims` (batch,
  * n_kv_heads and seq_len are read) and `top_k`: 0 for rows of at most 32768

@@ -121,6 +121,21 @@ def test_select_validation(lib):
     assert sel(FAKE, long_d, 1024, 4, 2048, FAKE, FAKE + 16, need) == INVALID  # not 256-aligned
 
 
+def test_select_noalloc_validation(lib):
+    def sel(mass, d, w, s, k, keep):
+        return lib.kvp_select_topk_noalloc(mass, d, w, s, k, keep, None)
+    assert sel(None, dims(), 4, 4, 8, FAKE) == INVALID
+    assert sel(FAKE, dims(), 4, 4, 8, None) == INVALID
+    assert sel(FAKE, dims(), -1, 4, 8, FAKE) == INVALID
+    assert sel(FAKE + 2, dims(), 4, 4, 8, FAKE) == INVALID
+    assert sel(None, dims(B=0), 4, 4, 8, None) == OK
+    assert sel(FAKE, dims(S=(1 << 22) + 1), 4, 4, 8, FAKE) == UNSUPPORTED
+    # more than the library's own 32 MiB array holds: rejected before any launch
+    big = dims(B=4, Hkv=1, S=1 << 22)
+    assert lib.kvp_select_workspace_bytes(big, 10) > 32 << 20
+    assert sel(FAKE, big, 16, 4, 10, FAKE) == WORKSPACE
+
+
 def test_select_workspace_bytes(lib):
     ws = lib.kvp_select_workspace_bytes
     # rows of up to 32768 scores need none
