@@ -314,6 +314,32 @@ def _target_scores(mass, window, n_kv_heads, per_head, group_size, normalize, ag
     return r
 
 
+def static_priority(score: np.ndarray, decay_step: int, log_gamma: np.ndarray) -> np.ndarray:
+    """Static token priorities of KVpop's running top-k (§3.2 "Running top-k
+    sparse attention"; App. B.3 "Temporal Decay and Static Priorities"), fp64
+    [B, Hkv, S].
+
+    App. B.3 decays a token's score at query q by floor((q - t) / n) steps of
+    log gamma_h.  Writing floor((q - t) / n) = floor(q / n) - floor(t / n) -
+    [q mod n < t mod n], the part floor(q / n) log gamma_h is the same for
+    every token at a given q, so the decayed order at q is the order of
+
+        pi[t] = r[t] - floor(t / n) * log gamma_h,
+
+    up to the last term, which is at most one decay step (|log gamma_h|) and
+    vanishes for n = 1 and at every query with q mod n = n - 1.  The pages say
+    only that the query-dependent part is shared up to the decay-step
+    discretization; this is the reading taken.
+
+    score: [B, Hkv, S] undecayed scores r (e.g. target_scores with query < 0);
+    log_gamma: [Hkv] values of log gamma_h; decay_step: n >= 1."""
+    r = np.asarray(score, dtype=np.float64)
+    B, H, S = r.shape
+    lg = np.asarray(log_gamma, dtype=np.float64).reshape(1, H, 1)
+    steps = (np.arange(S) // int(decay_step)).astype(np.float64)
+    return r - steps * lg
+
+
 def _laplace_cdf(z):
     return np.where(z >= 0, 1.0 - 0.5 * np.exp(-np.abs(z)), 0.5 * np.exp(-np.abs(z)))
 
