@@ -1,9 +1,14 @@
 """GPU parity at the full sizes of the three large workloads, in the launch
-configuration the benchmark times.  The oracle is run on what it finishes in
-seconds: one whole (batch, KV head) unit where affordable, otherwise the tail
-rows of a unit (exact masses for the keys they cover), LSE of sampled rows of
-every head, and properties that hold at any size (w = 0 total mass G*S, zero
-mass inside the window, exact selection on the GPU's own masses)."""
+configuration the benchmark times.  The oracle runs one whole (batch, KV
+head) unit of the 16K and 32K shapes here; for the 128K shape a whole KV head
+is compared with oracle values stored by a committed script (minutes of CPU
+work), and the tail rows of another head with the oracle run here.  Also: LSE
+of sampled rows of every head, and properties that hold at any size (w = 0
+total mass G*S, zero mass inside the window, exact selection on the GPU's own
+masses)."""
+import hashlib
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -14,6 +19,8 @@ import oracle
 from parity import assert_keep, assert_lse, assert_mass, say, to_dev
 
 pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
 def gpu_path(q, k, w, s, kk):
@@ -89,20 +96,46 @@ def test_workload4_qwen3_layer(layer, h):
 
 
 def test_workload5_llama70b_128k():
+    """Whole KV head 3 (its 8 query heads, every one of the 131072 query rows
+    and keys) against the oracle's fp64 values stored by
+    tests/golden/make_config5_head.py; the tail rows of a second head against
+    the oracle run here."""
     wl = kvp_inputs.workload(5)
     say("[workload] llama70b_128k: generating inputs")
     li = kvp_inputs.make_layer(wl)
+    gold = np.load(os.path.join(GOLDEN, "config5_head3.npz"), allow_pickle=False)
+    h = int(gold["head"])
+    g0 = h * wl.G
+    qh = np.ascontiguousarray(li.q[0, g0:g0 + wl.G])
+    kh = np.ascontiguousarray(li.k[0, h])
+    assert hashlib.sha256(qh.tobytes()).hexdigest() == str(gold["q_sha256"]) and \
+        hashlib.sha256(kh.tobytes()).hexdigest() == str(gold["k_sha256"]), \
+        "inputs differ from those of the stored oracle values"
     q, k = to_dev(li.q), to_dev(li.k)
     say("[workload] llama70b_128k: GPU path")
     lse, mass, keep = gpu_path(q, k, wl.window, wl.n_sink, wl.top_k)
     common_properties(li, lse, mass, keep, q, k, "llama70b_128k")
     S, w = wl.S, wl.window
+    say(f"[workload] llama70b_128k: whole head {h} against the stored oracle values")
+    assert_lse(lse.cpu().numpy()[0, g0:g0 + wl.G], gold["lse"].astype(np.float64),
+               "llama70b_128k head LSE")
+    ref_mass = gold["mass"]
+    assert ref_mass.shape == (S,)
+    got = mass.cpu().numpy()[0, h].astype(np.float64)
+    nz = ref_mass > 0
+    say(f"[workload] llama70b_128k head {h}: max rel mass err "
+        f"{(np.abs(got[nz] - ref_mass[nz]) / ref_mass[nz]).max():.2e}, keep-set "
+        f"{'identical' if np.array_equal(keep.cpu().numpy()[0, h], gold['keep']) else 'differs'}")
+    assert_mass(mass.cpu().numpy()[0, h], ref_mass, "llama70b_128k head mass")
+    assert_keep(keep.cpu().numpy()[:, h:h + 1], ref_mass.reshape(1, 1, S), w, wl.n_sink,
+                wl.top_k, gold["keep"].reshape(1, 1, -1), "llama70b_128k head keep-set")
+
     row_lo = S - 1536
-    h = 3
-    say(f"[workload] llama70b_128k: oracle tail rows >= {row_lo} of h={h}")
-    ref = oracle.future_mass(li.q, li.k, w, b_only=0, h_only=h, row_lo=row_lo)
-    g0 = h * wl.G
-    assert_lse(lse.cpu().numpy()[0, g0:g0 + wl.G, row_lo:], ref["lse"][0, g0:g0 + wl.G, row_lo:],
+    h2 = 6
+    say(f"[workload] llama70b_128k: oracle tail rows >= {row_lo} of h={h2}")
+    ref = oracle.future_mass(li.q, li.k, w, b_only=0, h_only=h2, row_lo=row_lo)
+    g2 = h2 * wl.G
+    assert_lse(lse.cpu().numpy()[0, g2:g2 + wl.G, row_lo:], ref["lse"][0, g2:g2 + wl.G, row_lo:],
                "llama70b_128k tail")
     lo = row_lo - w   # masses of keys >= row_lo - w are complete
-    assert_mass(mass.cpu().numpy()[0, h, lo:], ref["mass"][0, h, lo:], "llama70b_128k tail")
+    assert_mass(mass.cpu().numpy()[0, h2, lo:], ref["mass"][0, h2, lo:], "llama70b_128k tail")
