@@ -22,7 +22,8 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
                kernel) and its core clock under that load; roofline also
                states the mass kernel against that measured peak
   next_rows    after the timed steps: the per-head mass pass, the KVpop target
-               epilogue, the running top-k cutoff and the Golden-Eviction
+               epilogue, its static priorities, the running top-k cutoff over
+               them, the sparse LSE, the Soft-TopK and the Golden-Eviction
                block / future scores on the same layers
   roofline.traffic is the HBM bytes per mass-kernel launch from the committed
   counter summary (profiles/), reported only while the kernel sources still
@@ -296,11 +297,18 @@ def next_rows(kvp, torch, wl, L, q_all, k_all, lse_all, stream) -> dict:
         blk_ms = timed(blocks_all, 1) / L
     blk_pairs = B * Hq * (S * (S + 1) // 2 - b_start * (b_start + 1) // 2) if nb > 0 else 0
     rows = L * B * Hkv
+    # static priorities of the decayed target (App. B.3 leaves gamma_h and n open:
+    # n = 64 and gamma_h from 0.90 to 0.99 over the KV heads), the running
+    # cutoff's input
+    n_decay = 64
+    lg = torch.log(torch.linspace(0.90, 0.99, Hkv, dtype=torch.float32, device=dev))
+    pri = torch.empty_like(score)
+    pri_ms = timed(lambda: kvp.static_priority(score, n_decay, lg, out=pri), 10)
     ws = torch.empty(max(1, 20 * rows * (S - min(s, S))), dtype=torch.uint8, device=dev)
-    cut_ms = timed(lambda: kvp.running_cutoff(score, w, s, k, workspace=ws), 3)
+    cut_ms = timed(lambda: kvp.running_cutoff(pri, w, s, k, workspace=ws), 3)
     # the sparse normaliser of KVpop's student on layer 0, with the running
     # cutoff of its own target scores (window, sinks, budget of the workload)
-    rk_all, ct_all = kvp.running_cutoff(score, w, s, k, workspace=ws)
+    rk_all, ct_all = kvp.running_cutoff(pri, w, s, k, workspace=ws)
     sp_out = torch.empty_like(lse_all[0])
     sp_ms = timed(lambda: kvp.lse_sparse(q_all[0], k_all[0], rk_all[:B], ct_all[:B], w,
                                          out=sp_out), 3)
@@ -317,6 +325,7 @@ def next_rows(kvp, torch, wl, L, q_all, k_all, lse_all, stream) -> dict:
     st_dy = torch.ones_like(st_in)
     st_bwd_ms = timed(lambda: kvp.soft_topk_backward(st_in, st_out["lam"], st_dy, 1.0), 3)
     log(f"bench: per-head mass {ph_ms:.3f} ms/layer, target {tgt_ms:.4f} ms, "
+        f"static priority {pri_ms:.4f} ms, "
         f"running cutoff {cut_ms:.3f} ms ({rows} rows), sparse LSE {sp_ms:.3f} ms/layer, "
         f"soft top-k {st_fwd_ms:.3f} + "
         f"{st_bwd_ms:.3f} ms, block scores {blk_ms:.3f} ms/layer")
@@ -329,7 +338,11 @@ def next_rows(kvp, torch, wl, L, q_all, k_all, lse_all, stream) -> dict:
                           "gbs": round(tgt_bytes / (tgt_ms * 1e-3) / 1e9, 1),
                           "frac_hbm": round(tgt_bytes / (tgt_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                           "agg": "mean of logs, count-normalised, eps 1e-6"},
+        "static_priority": {"ms_all_layers": round(pri_ms, 4), "decay_step": n_decay,
+                            "gamma": "0.90..0.99 over the KV heads",
+                            "gbs": round(8 * rows * S / (pri_ms * 1e-3) / 1e9, 1)},
         "running_cutoff": {"ms_all_layers": round(cut_ms, 4), "rows": rows, "keys_per_row": S,
+                           "input": "static priorities of the decayed targets",
                            "mkeys_per_s": round(rows * S / (cut_ms * 1e-3) / 1e6, 1)},
         "lse_sparse": {"ms_per_layer": round(sp_ms, 4),
                        "gpairs_per_s": round(lse_pairs / (sp_ms * 1e-3) / 1e9, 3),

@@ -40,7 +40,7 @@ from typing import Optional
 import torch
 
 __all__ = ["lse_fwd", "lse_sparse", "future_mass", "future_mass_per_head", "target_scores",
-           "select_topk", "select_topk_noalloc", "select_workspace_bytes", "keep_count",
+           "static_priority", "select_topk", "select_topk_noalloc", "select_workspace_bytes", "keep_count",
            "running_cutoff", "block_count", "block_future_scores", "soft_topk",
            "soft_topk_backward", "KvpError", "library_path", "load_library", "AGG_LOG_MEAN",
            "AGG_MEAN_LOG", "AGG_MAX_LOG"]
@@ -89,6 +89,8 @@ def load_library():
             lib.kvp_target_scores.restype = ctypes.c_int
             lib.kvp_target_scores.argtypes = [vp, i32, _Dims, i32, i32, ctypes.c_int, f32, i32,
                                               i32, vp, vp, vp]
+            lib.kvp_static_priority.restype = ctypes.c_int
+            lib.kvp_static_priority.argtypes = [vp, _Dims, i32, vp, vp, vp]
             lib.kvp_keep_count.restype = i64
             lib.kvp_keep_count.argtypes = [i64, i64, i64, i64]
             lib.kvp_select_topk.restype = ctypes.c_int
@@ -288,6 +290,30 @@ def target_scores(mass: torch.Tensor, n_kv_heads: int, window: int, *, per_head:
                                  1 if normalize else 0, int(agg), float(eps), int(query),
                                  int(decay_step), lg_ptr, out.data_ptr(), _stream_ptr(stream)),
            "kvp_target_scores")
+    return out
+
+
+def static_priority(score: torch.Tensor, decay_step: int, log_gamma: torch.Tensor,
+                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Static priorities of the running top-k, fp32 [B, Hkv, S]:
+    score - floor(t / decay_step) * log_gamma[h] (KVpop §3.2 with App. B.3).
+    ``score`` fp32 [B, Hkv, S] undecayed; ``log_gamma`` fp32 [Hkv] on the GPU;
+    ``out`` may be ``score`` itself."""
+    lib = load_library()
+    _require_device(score, log_gamma)
+    if score.dtype != torch.float32 or score.dim() != 3:
+        raise KvpError("score must be fp32 [B, Hkv, S]")
+    B, H, S = score.shape
+    if log_gamma.dtype != torch.float32 or tuple(log_gamma.shape) != (H,):
+        raise KvpError("log_gamma must be fp32 [Hkv]")
+    if out is None:
+        out = torch.empty_like(score)
+    _require_device(out)
+    if out.dtype != torch.float32 or out.shape != score.shape:
+        raise KvpError("priority out must be fp32 like score")
+    _check(lib.kvp_static_priority(score.data_ptr(), _Dims(B, H, H, S, 128), int(decay_step),
+                                   log_gamma.data_ptr(), out.data_ptr(), _stream_ptr(stream)),
+           "kvp_static_priority")
     return out
 
 

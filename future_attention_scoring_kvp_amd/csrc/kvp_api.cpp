@@ -169,6 +169,26 @@ kvp_status_t kvp_target_scores(const float* mass, int32_t per_head, kvp_dims_t d
                                      query >= 0 ? decay_step : 1, log_gamma, score, stream));
 }
 
+kvp_status_t kvp_static_priority(const float* score, kvp_dims_t dims, int32_t decay_step,
+                                 const float* log_gamma, float* priority, hipStream_t stream) {
+  if (dims.batch < 0 || dims.seq_len < 0 || dims.n_kv_heads < 1 || decay_step < 1)
+    return KVP_EINVAL;
+  if (dims.seq_len > kMaxSeq) return KVP_EUNSUPPORTED;
+  if ((int64_t)dims.batch * dims.n_kv_heads * dims.seq_len > kMaxElems) return KVP_EUNSUPPORTED;
+  if (dims.batch == 0 || dims.seq_len == 0) return KVP_OK;
+  if (!score || !log_gamma || !priority || !aligned(score, 4) || !aligned(log_gamma, 4) ||
+      !aligned(priority, 4))
+    return KVP_EINVAL;
+  kvp::Shape sh;
+  sh.B = dims.batch;
+  sh.Hq = dims.n_kv_heads;
+  sh.Hkv = dims.n_kv_heads;
+  sh.S = dims.seq_len;
+  sh.D = dims.head_dim;
+  sh.G = 1;
+  return from_hip(kvp::launch_priority(score, sh, decay_step, log_gamma, priority, stream));
+}
+
 size_t kvp_select_workspace_bytes(kvp_dims_t dims, int32_t top_k) {
   if (dims.batch < 0 || dims.seq_len < 0 || dims.n_kv_heads < 1 || top_k < 0) return 0;
   if (dims.seq_len > kMaxSeq) return 0;

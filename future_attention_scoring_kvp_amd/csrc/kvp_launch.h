@@ -47,6 +47,9 @@ hipError_t launch_target(const float* mass, int per_head, const Shape& sh, int w
 // blocks number select_split_blocks(rows, S) per launch.
 size_t select_workspace_bytes(int64_t rows, int S);
 int64_t select_split_blocks(int64_t rows, int S);
+// Static priorities [B, Hkv, S] of the running top-k from undecayed scores.
+hipError_t launch_priority(const float* score, const Shape& sh, int decay_step,
+                           const float* log_gamma, float* priority, hipStream_t stream);
 hipError_t launch_select(const float* mass, int64_t rows, int S, int window, int n_sink,
                          int top_k, int64_t n_keep, int32_t* keep, void* workspace,
                          hipStream_t stream);

@@ -67,7 +67,31 @@ __global__ __launch_bounds__(256) void target_kernel(TargetArgs a) {
   a.score[idx] = r;
 }
 
+// Static priorities of the running top-k (KVpop §3.2 with App. B.3): the
+// decayed score at query q is r[t] + floor((q - t) / n) log gamma_h, whose
+// query-dependent part floor(q / n) log gamma_h is shared by every token up
+// to one decay step, so tokens are ranked once by
+//   pi[b, h, t] = r[b, h, t] - floor(t / n) * log gamma_h
+// (one fused multiply-add, correctly rounded; in place allowed).
+__global__ __launch_bounds__(256) void priority_kernel(const float* score, const float* log_gamma,
+                                                       float* pri, int64_t n, int Hkv, int S,
+                                                       int decay_step) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  const int t = (int)(idx % S);
+  const int h = (int)((idx / S) % Hkv);
+  pri[idx] = __builtin_fmaf(-(float)(t / decay_step), log_gamma[h], score[idx]);
+}
+
 }  // namespace
+
+hipError_t launch_priority(const float* score, const Shape& sh, int decay_step,
+                           const float* log_gamma, float* priority, hipStream_t stream) {
+  const int64_t n = (int64_t)sh.B * sh.Hkv * sh.S;
+  hipLaunchKernelGGL(priority_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                     score, log_gamma, priority, n, sh.Hkv, sh.S, decay_step);
+  return hipGetLastError();
+}
 
 hipError_t launch_target(const float* mass, int per_head, const Shape& sh, int window,
                          int normalize, int agg, float eps, int query, int decay_step,

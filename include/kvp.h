@@ -192,6 +192,25 @@ kvp_status_t kvp_target_scores(const float* mass, int32_t per_head, kvp_dims_t d
                                int32_t decay_step, const float* log_gamma, float* score,
                                hipStream_t stream);
 
+/* Static token priorities of the running top-k ([KVpop] §3.2 "Running top-k
+ * sparse attention": tokens are sorted once by a static priority because the
+ * query-dependent part of the decayed score is shared across eligible tokens
+ * up to the decay-step discretization; App. B.3 "Temporal Decay and Static
+ * Priorities"):
+ *   priority[b, h, t] = score[b, h, t] - floor(t / decay_step) * log_gamma[h]
+ * At query q, App. B.3's decayed score score[t] + floor((q - t) / n) log_gamma
+ * equals priority[t] + floor(q / n) log_gamma (shared by every token) plus at
+ * most one step |log_gamma| for tokens with t mod n > q mod n; the order is
+ * exact for n = 1 and at every q with q mod n = n - 1.  Pass the result to
+ * kvp_running_cutoff.
+ *   score     : device fp32 [B, Hkv, S] undecayed scores (e.g. kvp_target_scores
+ *               with query < 0); priority may alias it (computed in place).
+ *   log_gamma : device fp32 [Hkv], log(gamma_h) with gamma_h in (0, 1].
+ *   decay_step: n >= 1.   dims: batch, n_kv_heads and seq_len are read.
+ * One fp32 fused multiply-add per token (correctly rounded). */
+kvp_status_t kvp_static_priority(const float* score, kvp_dims_t dims, int32_t decay_step,
+                                 const float* log_gamma, float* priority, hipStream_t stream);
+
 /* Size of every KV head's keep-set ([KVpop] §3 Eq. 1, budget B = s + w + k,
  * clipped to the sequence):
  *   min(s, S) + |[max(s, S - w), S)| + min(k, max(0, S - w - s)).

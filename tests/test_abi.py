@@ -36,7 +36,8 @@ def test_header_declares_the_three_stages():
               "kvp_status_string", "kvp_abi_version", "kvp_future_mass_per_head",
               "kvp_target_scores", "kvp_running_cutoff", "kvp_running_cutoff_workspace_bytes",
               "kvp_block_count", "kvp_block_future_scores", "kvp_soft_topk_fwd",
-              "kvp_soft_topk_bwd", "kvp_lse_sparse", "kvp_select_workspace_bytes"):
+              "kvp_soft_topk_bwd", "kvp_lse_sparse", "kvp_select_workspace_bytes",
+              "kvp_static_priority"):
         assert n in names
 
 
@@ -289,3 +290,14 @@ def test_lse_sparse_validation(lib):
     assert f(FAKE, FAKE, 0, dims(D=96), 0.0, FAKE, FAKE, 4, FAKE, None) == UNSUPPORTED
     assert f(FAKE, FAKE, 7, dims(), 0.0, FAKE, FAKE, 4, FAKE, None) == UNSUPPORTED
     assert f(None, None, 0, dims(S=0), 0.0, None, None, 4, None, None) == OK
+
+
+def test_static_priority_validation(lib):
+    f = lib.kvp_static_priority
+    assert f(FAKE, dims(), 0, FAKE, FAKE, None) == INVALID      # decay step < 1
+    assert f(None, dims(), 4, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, dims(), 4, None, FAKE, None) == INVALID
+    assert f(FAKE, dims(), 4, FAKE, FAKE + 1, None) == INVALID
+    assert f(FAKE, dims(Hkv=0), 4, FAKE, FAKE, None) == INVALID
+    assert f(None, dims(B=0), 4, None, None, None) == OK
+    assert f(FAKE, dims(S=(1 << 22) + 1), 4, FAKE, FAKE, None) == UNSUPPORTED

@@ -98,3 +98,38 @@ def test_cutoff_stack_of_layers_random_rows():
     S = 32768
     sc = scores("logmass", 288, S, seed=9)
     check(sc, 512, 4, 16384)
+
+
+@pytest.mark.parametrize("n,kind", [(1, "logmass"), (16, "logmass"), (7, "ties")])
+def test_static_priority_then_cutoff(n, kind):
+    """Static priorities (KVpop §3.2 with App. B.3): every value against the
+    oracle's fp64 formula rounded once to fp32, then the running cutoff over
+    them bit-exact; with n = 1 the retained set at sampled queries equals a
+    direct top-k of the decayed scores r + (q - t) log gamma."""
+    rows, S, w, s, k = 6, 3001, 64, 4, 300
+    r = scores(kind, rows, S, seed=n)
+    lg = np.log(np.array([0.5, 0.7, 0.9, 0.97, 0.999, 1.0], dtype=np.float32)).astype(np.float32)
+    say(f"[priority] n={n} {kind}")
+    pri = kvp.static_priority(to_dev(r.reshape(1, rows, S)), n, to_dev(lg))
+    got = pri.cpu().numpy()[0]
+    ref = oracle.static_priority(r.astype(np.float64)[None], n, lg.astype(np.float64))[0]
+    ref32 = ref.astype(np.float32)
+    both_inf = np.isneginf(got) & np.isneginf(ref32)
+    ulp = np.spacing(np.abs(ref32)).astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        bad = ~both_inf & ~(np.abs(got.astype(np.float64) - ref) <= ulp)
+    assert not bad.any(), f"{int(bad.sum())} priorities off by more than one ulp"
+    rank, cut = check(got, w, s, k)
+    if n == 1:
+        for h in range(rows):
+            for q in (s + w + k - 1, 1000, S - 1):
+                elig = np.arange(s, q - w + 1)
+                dec = r[h].astype(np.float64) + (q - np.arange(S)) * float(lg[h])
+                order = sorted(elig.tolist(), key=lambda t: (-dec[t], t))[:k]
+                kept = elig[rank[h, elig] <= cut[h, q]]
+                # ties in the decayed scores may round differently in fp32: compare the sets
+                # only where the k-th and (k+1)-th decayed scores are apart
+                vk = dec[order[-1]]
+                rest = [dec[t] for t in elig.tolist() if t not in set(order)]
+                if not rest or vk - max(rest) > 1e-4 * (1 + abs(vk)):
+                    assert set(kept.tolist()) == set(order), (h, q)
