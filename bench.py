@@ -142,7 +142,7 @@ def cpu_baseline(wl, li0, n_heads: int, gpu=None, max_pairs: float = 4.5e9) -> d
     t0 = time.perf_counter()
     for h in range(n_heads):
         refs.append(oracle.future_mass(li0.q, li0.k, w, b_only=0, h_only=h, row_lo=row_lo,
-                                       nthreads=threads))
+                                       nthreads=threads, f32_exact=wl.dtype == "f32"))
     dt = time.perf_counter() - t0
     pairs = pairs_from(row_lo)
     rows = "all" if row_lo == 0 else f"the last {S - row_lo} of"

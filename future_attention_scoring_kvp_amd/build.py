@@ -18,8 +18,7 @@ LIB_PATH = os.path.join(HERE, "libkvp.so")
 PROBE_LIB_PATH = os.path.join(HERE, "libkvp_probe.so")
 
 SOURCES = ["kvp_api.cpp", "lse_kernel.hip", "mass_kernel.hip", "select_kernel.hip",
-           "target_kernel.hip", "cutoff_kernel.hip",
-           "softtopk_kernel.hip"]
+           "target_kernel.hip", "cutoff_kernel.hip", "softtopk_kernel.hip", "f32_kernel.hip"]
 PROBE_SOURCES = ["probe_kernel.hip"]
 ARCH = "gfx950"
 

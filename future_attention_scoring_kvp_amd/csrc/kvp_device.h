@@ -50,37 +50,16 @@ __device__ __forceinline__ void buf_store_f32(__amdgpu_buffer_rsrc_t r, uint32_t
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_offset, 0, 0);
 }
 
-// Eight elements at element offset `elem` of a buffer, as eight bf16 values
-// (16 bytes): bf16 is passed through, fp32 is rounded to nearest even.
+// Eight bf16 elements at element offset `elem` of a buffer (16 bytes).
 // Out-of-range reads give zeros.
 __device__ __forceinline__ u32x4_t buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t elem,
                                              const uint16_t*) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, elem * 2, 0, 0));
 }
-__device__ __forceinline__ u32x4_t buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t elem,
-                                             const float*) {
-  const f32x4_t lo =
-      __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, elem * 4, 0, 0));
-  const f32x4_t hi =
-      __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, elem * 4 + 16, 0, 0));
-  bf16x8_t v;
-  v[0] = (__bf16)lo[0]; v[1] = (__bf16)lo[1]; v[2] = (__bf16)lo[2]; v[3] = (__bf16)lo[3];
-  v[4] = (__bf16)hi[0]; v[5] = (__bf16)hi[1]; v[6] = (__bf16)hi[2]; v[7] = (__bf16)hi[3];
-  return __builtin_bit_cast(u32x4_t, v);
-}
 
-// Eight consecutive input elements as eight bf16 values (16 bytes).  bf16
-// input is passed through; fp32 input is rounded to nearest even.
+// Eight consecutive bf16 input elements (16 bytes).
 __device__ __forceinline__ u32x4_t load8(const uint16_t* __restrict__ p) {
   return *reinterpret_cast<const u32x4_t*>(p);
-}
-__device__ __forceinline__ u32x4_t load8(const float* __restrict__ p) {
-  const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(p);
-  const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(p + 4);
-  bf16x8_t r;
-  r[0] = (__bf16)lo[0]; r[1] = (__bf16)lo[1]; r[2] = (__bf16)lo[2]; r[3] = (__bf16)lo[3];
-  r[4] = (__bf16)hi[0]; r[5] = (__bf16)hi[1]; r[6] = (__bf16)hi[2]; r[7] = (__bf16)hi[3];
-  return __builtin_bit_cast(u32x4_t, r);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

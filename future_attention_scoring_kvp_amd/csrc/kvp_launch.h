@@ -12,7 +12,7 @@ struct Shape {
   int G;  // Hq / Hkv
 };
 
-// dtype: 0 = bf16, 1 = fp32 (rounded to bf16 on load).
+// dtype: 0 = bf16 (matrix cores), 1 = fp32 (exact fp32 path, launch_*_f32).
 hipError_t launch_lse(const void* q, const void* k, int dtype, const Shape& sh, float scale,
                       float* lse, hipStream_t stream);
 // LSE over the running top-k pattern: j counts for i iff j <= i and
@@ -35,6 +35,14 @@ struct SegOut {
 hipError_t launch_block_scores(const void* q, const void* k, const float* lse, int dtype,
                                const Shape& sh, float scale, int window, int per_head,
                                const SegOut& seg, hipStream_t stream);
+// fp32 inputs: the LSE (sparse when rank is not null) and the mass / block
+// scores computed in fp32 on the vector ALUs, with no rounding of the inputs.
+hipError_t launch_lse_f32(const void* q, const void* k, const Shape& sh, float scale,
+                          const int32_t* rank, const int32_t* cutoff, int window, float* lse,
+                          hipStream_t stream);
+hipError_t launch_mass_f32(const void* q, const void* k, const float* lse, const Shape& sh,
+                           float scale, int window, int per_head, float* mass, const SegOut& seg,
+                           hipStream_t stream);
 // Target scores [B, Hkv, S] from masses ([B, Hq, S] per head or [B, Hkv, S]
 // group sums); agg: 0 log of the mean, 1 mean of the logs, 2 max of the logs;
 // query < 0: no decay.

@@ -65,14 +65,14 @@ struct LseCfg {
   static constexpr int kMfmaPerBlock = NB * kKSteps;
 };
 
-// Most 32-query blocks per wave: three for the dense pass on bf16 input
-// (every staged key block then feeds 24 MFMAs per wave), two for the sparse
-// pass and for fp32 input, whose extra registers would spill.  Grids too
-// small for two 8-wave workgroups per CU at three blocks run two blocks per
-// wave instead, so that short sequences still spread over every CU.
+// Most 32-query blocks per wave: three for the dense pass (every staged key
+// block then feeds 24 MFMAs per wave), two for the sparse pass, whose rank
+// registers would otherwise spill.  Grids too small for two 8-wave workgroups
+// per CU at three blocks run two blocks per wave instead, so that short
+// sequences still spread over every CU.
 template <typename T, bool kSp>
 constexpr int lse_query_blocks() {
-  return (kSp || std::is_same<T, float>::value) ? 2 : 3;
+  return kSp ? 2 : 3;
 }
 
 struct LseArgs {
@@ -623,23 +623,19 @@ hipError_t launch_lse_t(const void* q, const void* k, const Shape& sh, float sca
 
 hipError_t launch_lse(const void* q, const void* k, int dtype, const Shape& sh, float scale,
                       float* lse, hipStream_t stream) {
+  if (dtype != 0) return launch_lse_f32(q, k, sh, scale, nullptr, nullptr, 0, lse, stream);
   const SparseIn none{nullptr, nullptr, 0};
-  if (sh.D == 128)
-    return dtype == 0 ? launch_lse_t<128, uint16_t, false>(q, k, sh, scale, lse, none, stream)
-                      : launch_lse_t<128, float, false>(q, k, sh, scale, lse, none, stream);
-  return dtype == 0 ? launch_lse_t<64, uint16_t, false>(q, k, sh, scale, lse, none, stream)
-                    : launch_lse_t<64, float, false>(q, k, sh, scale, lse, none, stream);
+  return sh.D == 128 ? launch_lse_t<128, uint16_t, false>(q, k, sh, scale, lse, none, stream)
+                     : launch_lse_t<64, uint16_t, false>(q, k, sh, scale, lse, none, stream);
 }
 
 hipError_t launch_lse_sparse(const void* q, const void* k, int dtype, const Shape& sh, float scale,
                              const int32_t* rank, const int32_t* cutoff, int window, float* lse,
                              hipStream_t stream) {
+  if (dtype != 0) return launch_lse_f32(q, k, sh, scale, rank, cutoff, window, lse, stream);
   const SparseIn sp{rank, cutoff, window};
-  if (sh.D == 128)
-    return dtype == 0 ? launch_lse_t<128, uint16_t, true>(q, k, sh, scale, lse, sp, stream)
-                      : launch_lse_t<128, float, true>(q, k, sh, scale, lse, sp, stream);
-  return dtype == 0 ? launch_lse_t<64, uint16_t, true>(q, k, sh, scale, lse, sp, stream)
-                    : launch_lse_t<64, float, true>(q, k, sh, scale, lse, sp, stream);
+  return sh.D == 128 ? launch_lse_t<128, uint16_t, true>(q, k, sh, scale, lse, sp, stream)
+                     : launch_lse_t<64, uint16_t, true>(q, k, sh, scale, lse, sp, stream);
 }
 
 }  // namespace kvp

@@ -600,30 +600,24 @@ hipError_t launch_mass_t(const void* q, const void* k, const float* lse, const S
 hipError_t launch_mass(const void* q, const void* k, const float* lse, int dtype, const Shape& sh,
                        float scale, int window, int per_head, float* mass, hipStream_t stream) {
   const SegOut none{0, 32, 0, nullptr, nullptr};
-  if (sh.D == 128)
-    return dtype == 0 ? launch_mass_t<128, uint16_t, false>(q, k, lse, sh, scale, window, per_head,
-                                                            mass, none, stream)
-                      : launch_mass_t<128, float, false>(q, k, lse, sh, scale, window, per_head,
-                                                         mass, none, stream);
-  return dtype == 0 ? launch_mass_t<64, uint16_t, false>(q, k, lse, sh, scale, window, per_head,
-                                                         mass, none, stream)
-                    : launch_mass_t<64, float, false>(q, k, lse, sh, scale, window, per_head, mass,
-                                                      none, stream);
+  if (dtype != 0)
+    return launch_mass_f32(q, k, lse, sh, scale, window, per_head, mass, none, stream);
+  return sh.D == 128 ? launch_mass_t<128, uint16_t, false>(q, k, lse, sh, scale, window, per_head,
+                                                           mass, none, stream)
+                     : launch_mass_t<64, uint16_t, false>(q, k, lse, sh, scale, window, per_head,
+                                                          mass, none, stream);
 }
 
 hipError_t launch_block_scores(const void* q, const void* k, const float* lse, int dtype,
                                const Shape& sh, float scale, int window, int per_head,
                                const SegOut& seg, hipStream_t stream) {
   if (seg.n == 0) return hipSuccess;
-  if (sh.D == 128)
-    return dtype == 0 ? launch_mass_t<128, uint16_t, true>(q, k, lse, sh, scale, window, per_head,
-                                                           nullptr, seg, stream)
-                      : launch_mass_t<128, float, true>(q, k, lse, sh, scale, window, per_head,
-                                                        nullptr, seg, stream);
-  return dtype == 0 ? launch_mass_t<64, uint16_t, true>(q, k, lse, sh, scale, window, per_head,
-                                                        nullptr, seg, stream)
-                    : launch_mass_t<64, float, true>(q, k, lse, sh, scale, window, per_head,
-                                                     nullptr, seg, stream);
+  if (dtype != 0)
+    return launch_mass_f32(q, k, lse, sh, scale, window, per_head, nullptr, seg, stream);
+  return sh.D == 128 ? launch_mass_t<128, uint16_t, true>(q, k, lse, sh, scale, window, per_head,
+                                                          nullptr, seg, stream)
+                     : launch_mass_t<64, uint16_t, true>(q, k, lse, sh, scale, window, per_head,
+                                                         nullptr, seg, stream);
 }
 
 }  // namespace kvp

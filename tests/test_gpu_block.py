@@ -42,7 +42,8 @@ def counts_of(S, start, L):
     (1, 4, 4, 257, 64, 5, 0, 32, False, "bf16"),      # d = 64, window, blocks from row 0
     (1, 8, 1, 2100, 128, 0, 1024, 256, False, "bf16"),  # first block after 1024 rows
     (1, 2, 1, 200, 128, 0, 0, 512, False, "bf16"),    # one block longer than S
-    (1, 1, 1, 256, 64, 0, 32, 32, False, "f32"),      # fp32 inputs rounded on load
+    (1, 1, 1, 256, 64, 0, 32, 32, False, "f32"),      # fp32 inputs, exact fp32 path
+    (2, 8, 2, 700, 128, 40, 64, 96, True, "f32"),
 ])
 def test_block_scores_match_oracle(B, Hq, Hkv, S, D, w, start, L, per_head, dtype):
     wl = kvp_inputs.workload(2).with_(B=B, Hq=Hq, Hkv=Hkv, S=S, D=D, dtype=dtype, seed=500 + S)
@@ -55,7 +56,8 @@ def test_block_scores_match_oracle(B, Hq, Hkv, S, D, w, start, L, per_head, dtyp
     _, fut_only = kvp.block_future_scores(q, k, lse, start, L, w, per_head=per_head,
                                           want_block=False)
     torch.cuda.synchronize()
-    ref = oracle.block_scores(li.q, li.k, w, start, L, per_head=per_head)
+    ref = oracle.block_scores(li.q, li.k, w, start, L, per_head=per_head,
+                              f32_exact=dtype == "f32")
     counts = counts_of(S, start, L)
     G = 1 if per_head else Hq // Hkv
     assert_blocks(blk.cpu().numpy(), ref["block"], counts, G, "block scores")

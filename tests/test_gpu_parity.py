@@ -26,7 +26,7 @@ def full_check(li, w, s, k, what, scale=0.0):
     say(f"[parity] {what}: B={li.wl.B} Hq={li.wl.Hq} Hkv={li.wl.Hkv} S={li.wl.S} D={li.wl.D} "
         f"{li.wl.dtype} w={w} s={s} k={k}")
     lse, mass, keep = run_gpu(li, w, s, k, scale)
-    ref = oracle.future_mass(li.q, li.k, w, scale=scale)
+    ref = oracle.future_mass(li.q, li.k, w, scale=scale, f32_exact=li.wl.dtype == "f32")
     assert_lse(lse, ref["lse"], what)
     assert_mass(mass, ref["mass"], what)
     exact = oracle.select(ref["mass"], w, s, k)
@@ -59,7 +59,7 @@ def test_workload2_gqa4k_full():
     (1, 4, 1, 300, 128, 400, 4, 8, "bf16"),       # w > S
     (1, 2, 1, 300, 128, 20, 4, 10000, "bf16"),    # k >= |eligible|
     (1, 2, 2, 513, 128, 1, 600, 8, "bf16"),       # sinks beyond S - w
-    (3, 6, 3, 257, 128, 5, 4, 30, "f32"),         # fp32 input, rounded on load
+    (3, 6, 3, 257, 128, 5, 4, 30, "f32"),         # fp32 input, exact fp32 path
     (1, 4, 2, 2048, 64, 64, 4, 256, "f32"),
 ])
 def test_edge_shapes(B, Hq, Hkv, S, D, w, s, k, dtype):

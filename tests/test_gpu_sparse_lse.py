@@ -25,7 +25,8 @@ def priorities(rng, B, Hkv, S):
     (2, 8, 2, 1000, 128, 64, 4, 100, "bf16"),
     (1, 4, 4, 257, 64, 0, 3, 40, "bf16"),          # no window
     (1, 8, 1, 2100, 128, 512, 4, 1024, "bf16"),    # many blocks outside every window
-    (1, 1, 1, 256, 64, 16, 4, 32, "f32"),          # fp32 inputs rounded on load
+    (1, 1, 1, 256, 64, 16, 4, 32, "f32"),          # fp32 inputs, exact fp32 path
+    (2, 8, 2, 1000, 128, 40, 4, 100, "f32"),
     (1, 4, 2, 200, 128, 8, 2, 10_000, "bf16"),     # full budget: the dense LSE
     (1, 32, 8, 8100, 128, 512, 4, 2000, "bf16"),   # one-per-CU grid with paired tiles
 ])
@@ -38,7 +39,8 @@ def test_sparse_lse_matches_oracle(B, Hq, Hkv, S, D, w, s, k, dtype):
     rank, cut = kvp.running_cutoff(to_dev(priorities(rng, B, Hkv, S)), w, s, k)
     lse = kvp.lse_sparse(q, kt, rank, cut, w)
     torch.cuda.synchronize()
-    ref = oracle.sparse_lse(li.q, li.k, w, rank.cpu().numpy(), cut.cpu().numpy())
+    ref = oracle.sparse_lse(li.q, li.k, w, rank.cpu().numpy(), cut.cpu().numpy(),
+                            f32_exact=dtype == "f32")
     got = lse.cpu().numpy().astype(np.float64)
     err = np.abs(got - ref)
     assert err.max() <= LSE_ATOL, f"max |d| {err.max():.3g} at {np.unravel_index(err.argmax(), err.shape)}"

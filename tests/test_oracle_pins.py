@@ -250,6 +250,32 @@ def test_f32_inputs_rounded_like_bf16(orc):
     assert not np.array_equal(a, c)
 
 
+def test_f32_exact_matrix_brute_force(orc):
+    """fp32 inputs used as given (not representable in bf16): LSE and mass
+    against the scipy matrix form on the same values widened to fp64."""
+    rng = np.random.default_rng(15)
+    for (B, Hq, Hkv, S, D, w) in ((1, 2, 1, 40, 64, 4), (2, 4, 2, 33, 128, 0)):
+        q = (rng.standard_normal((B, Hq, S, D)) * 1.3).astype(np.float32)
+        k = (rng.standard_normal((B, Hkv, S, D)) * 1.3).astype(np.float32)
+        out = orc.future_mass(q, k, w, f32_exact=True)
+        # brute_force widens bf16 bit patterns; give it the fp32 values directly
+        qd, kd = q.astype(np.float64), k.astype(np.float64)
+        G = Hq // Hkv
+        i_idx, j_idx = np.arange(S)[:, None], np.arange(S)[None, :]
+        for b in range(B):
+            for g in range(Hq):
+                L = np.where(j_idx <= i_idx, (qd[b, g] @ kd[b, g // G].T) / math.sqrt(D), -np.inf)
+                np.testing.assert_allclose(out["lse"][b, g], scipy.special.logsumexp(L, axis=1),
+                                           rtol=1e-12)
+        ref_mass = np.zeros((B, Hkv, S))
+        for b in range(B):
+            for g in range(Hq):
+                L = np.where(j_idx <= i_idx, (qd[b, g] @ kd[b, g // G].T) / math.sqrt(D), -np.inf)
+                P = scipy.special.softmax(L, axis=1)
+                ref_mass[b, g // G] += np.where(i_idx >= j_idx + w, P, 0.0).sum(axis=0)
+        np.testing.assert_allclose(out["mass"], ref_mass, rtol=1e-10, atol=1e-14)
+
+
 def test_bf16_rounding_matches_torch(orc):
     """The oracle's own round-to-nearest-even agrees with torch's fp32->bf16
     conversion on random values, exact ties and edge values."""
