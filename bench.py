@@ -33,6 +33,7 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
                     [--batch B] [--hq H] [--hkv H] [--seq S] [--dim D]
                     [--window W] [--sinks N] [--topk K] [--seed N]
     python bench.py --copy-probe BYTES   # plain copy kernel, for counter scaling
+    python bench.py --read-probe BYTES   # 16-byte buffer-load reads, for counter scaling
 """
 from __future__ import annotations
 
@@ -105,6 +106,31 @@ def copy_probe(nbytes: int, reps: int) -> None:
     torch.cuda.synchronize()
     log(f"copy probe: {reps} copies of {nbytes} bytes")
     print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}))
+
+
+def read_probe(nbytes: int, reps: int) -> None:
+    """The 16-byte buffer-load read probe (libkvp_probe.so) over `nbytes`
+    bytes, `reps` launches: the counter reading of a known read through the
+    kernels' own load instruction."""
+    import ctypes
+    import torch
+    import future_attention_scoring_kvp_amd as kvp
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(kvp.library_path()), "libkvp_probe.so"))
+    lib.kvp_probe_read16.restype = ctypes.c_int
+    lib.kvp_probe_read16.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    blocks = 4096
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        rc = lib.kvp_probe_read16(src.data_ptr(), nbytes, blocks, sink.data_ptr(),
+                                  int(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"read probe failed ({rc})")
+    torch.cuda.synchronize()
+    log(f"read probe: {reps} reads of {nbytes} bytes through 16-byte buffer loads")
+    print(json.dumps({"read_probe_bytes": nbytes, "reps": reps}))
 
 
 def cpu_baseline(wl, li0, n_heads: int, gpu=None, max_pairs: float = 4.5e9) -> dict:
@@ -382,6 +408,8 @@ def main() -> int:
     ap.add_argument("--sha", action="store_true", help="print the mass kernel sources' sha256")
     ap.add_argument("--copy-probe", type=int, default=0)
     ap.add_argument("--copy-reps", type=int, default=5)
+    ap.add_argument("--read-probe", type=int, default=0,
+                    help="read BYTES through 16-byte buffer loads (counter scaling)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -396,6 +424,9 @@ def main() -> int:
     import torch
     if args.copy_probe:
         copy_probe(args.copy_probe, args.copy_reps)
+        return 0
+    if args.read_probe:
+        read_probe(args.read_probe, args.copy_reps)
         return 0
 
     import future_attention_scoring_kvp_amd as kvp

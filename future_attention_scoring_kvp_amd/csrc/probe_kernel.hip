@@ -71,10 +71,36 @@ __global__ __launch_bounds__(kProbeThreads, 1) void mfma_probe_kernel(int iters,
   }
 }
 
+// Read probe: every thread reads 16-byte pieces through a buffer resource,
+// as the matrix-core kernels stage their operands (raw buffer loads of 16
+// bytes, consecutive lanes on consecutive pieces), and writes one word, so
+// the bytes the memory counters see can be compared with a known read.
+__global__ __launch_bounds__(256) void read16_probe_kernel(const unsigned char* src,
+                                                           uint32_t bytes, uint32_t* sink) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(src, bytes);
+  const uint32_t n16 = bytes / 16;
+  uint32_t x = 0;
+  for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < n16; i += gridDim.x * 256) {
+    const u32x4_t v =
+        __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, i * 16u, 0, 0));
+    x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  sink[blockIdx.x * 256 + threadIdx.x] = x;
+}
+
 }  // namespace
 }  // namespace kvp
 
 extern "C" {
+
+int kvp_probe_read16(const void* src, uint32_t bytes, int blocks, uint32_t* sink,
+                     hipStream_t stream) {
+  if (!src || !sink || blocks < 1 || bytes % 16 != 0) return 1;
+  hipLaunchKernelGGL(kvp::read16_probe_kernel, dim3(blocks), dim3(256), 0, stream,
+                     static_cast<const unsigned char*>(src), bytes, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
 
 int kvp_probe_mfma_bf16(int blocks, int iters, float* sink, long long* stamps,
                         hipStream_t stream) {

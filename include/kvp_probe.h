@@ -8,6 +8,8 @@
 #ifndef KVP_PROBE_H_
 #define KVP_PROBE_H_
 
+#include <stdint.h>
+
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
@@ -27,6 +29,14 @@ int kvp_probe_mfma_bf16(int blocks, int iters, float* sink, long long* stamps,
 
 /* Flops of one probe launch (2 per multiply-add). */
 double kvp_probe_flops(int blocks, int iters);
+
+/* Read probe for memory-counter scaling: `blocks` workgroups of 256 threads
+ * read the `bytes` bytes at `src` (device, a multiple of 16, below 4 GiB)
+ * through 16-byte raw buffer loads, consecutive lanes on consecutive 16-byte
+ * pieces, and write one uint32 per thread to `sink` (device, blocks * 256).
+ * Returns 0, 1 for invalid arguments, 4 if the launch failed. */
+int kvp_probe_read16(const void* src, uint32_t bytes, int blocks, uint32_t* sink,
+                     hipStream_t stream);
 
 /* Rate of the constant-rate counter in kHz (0 on error): core clock =
  * d(core counter) / d(constant counter) * rate. */
