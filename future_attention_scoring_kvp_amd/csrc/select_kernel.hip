@@ -25,11 +25,12 @@
 // Longer rows are split into chunks of 4096 or more positions, one 256-thread
 // workgroup per (row, chunk), with the per-chunk integer state in a caller
 // workspace (deterministic: integer counts, fixed reduction order):
-//   sel_hist_kernel     per chunk, a 2048-bin histogram of key bits 31..21;
-//   sel_bin_kernel      per row, the bin b1 of the k-th largest key (suffix
-//                       scan over the summed chunk histograms), the count of
-//                       keys above b1 per chunk and each chunk's offset into
-//                       the candidate list (the keys in bin b1);
+//   sel_hist_kernel     per chunk, a 2048-bin histogram of key bits 31..21,
+//                       stored as suffix counts (keys in that bin or above);
+//   sel_bin_kernel      per row, the bin b1 of the k-th largest key (from the
+//                       summed chunk suffix counts), the count of keys above
+//                       b1 per chunk and each chunk's offset into the
+//                       candidate list (the keys in bin b1);
 //   sel_compact_kernel  per chunk, its keys in bin b1 into its segment of the
 //                       candidate list;
 //   sel_finish_kernel   per row, two more radix passes (bits 20..10, 9..0)
@@ -290,6 +291,9 @@ constexpr int kFinThreads = 1024;
 constexpr int kFinWaves = kFinThreads / kWave;
 constexpr int kCandLds = 32768;             // candidates held in LDS by sel_finish_kernel
 constexpr int kStateInts = 8;               // per row: b1, k1, n_cand, T, r
+constexpr int kMaxChunks = 256;             // chunks per row: one thread each in sel_bin_kernel
+constexpr int kMinChunk = 4 * kSubLen;
+static_assert(kMaxChunks <= kMbThreads, "sel_bin_kernel gives every chunk a thread");
 
 // Selection of a row: 0 = no eligible token is taken (k = 0 or none
 // eligible), 1 = every eligible token is taken, 2 = a real top-k.
@@ -328,8 +332,41 @@ __device__ __forceinline__ int forced_before(int p, int S, int w, int s) {
   return min(p, sp) + max(0, p - wl);
 }
 
+// Sub-chunks whose loads are issued together before their keys are used.
+constexpr int kBatch = 4;
+
+// Exclusive prefix sum over the threads of a block and the block total;
+// `tot` is LDS scratch of one int per wave.
+template <int kWaves>
+__device__ __forceinline__ int block_prefix_excl(int v, int* tot, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(x, off);
+    if (lane >= off) x += o;
+  }
+  if (lane == kWave - 1) tot[wave] = x;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int t = tot[w];
+    if (w < wave) before += t;
+    total += t;
+  }
+  __syncthreads();
+  return before + x - v;
+}
+
+// Per chunk: the count of its eligible keys in each bin of key bits 31..21
+// and above, i.e. suf[b] = #{keys with bin >= b}, so that the per-row kernel
+// reads any bin's count and the count above it with two loads.
 __global__ __launch_bounds__(kMbThreads) void sel_hist_kernel(MbArgs a) {
+  constexpr int kPer = kBins1 / kMbThreads;  // 8 bins per thread
   __shared__ int h[kMbWaves][kBins1];
+  __shared__ int tot[kMbWaves];
   const int tid = threadIdx.x, wave = tid >> 6;
   const int row = blockIdx.x / a.nc, c = blockIdx.x - row * a.nc;
   for (int i = tid; i < kMbWaves * kBins1; i += kMbThreads) (&h[0][0])[i] = 0;
@@ -337,16 +374,38 @@ __global__ __launch_bounds__(kMbThreads) void sel_hist_kernel(MbArgs a) {
   const float* __restrict__ m = a.mass + (size_t)row * a.S;
   const int e_lo = a.n_sink, e_hi = a.S - a.window;
   const int p_end = min(a.S, (c + 1) * a.C);
-  for (int p = c * a.C + 4 * tid; p < p_end; p += kSubLen) {
-    float v[4];
-    load4(m, p, a.S, a.vec4, v);
+  for (int p0 = c * a.C + 4 * tid; p0 < p_end; p0 += kBatch * kSubLen) {
+    float v[kBatch][4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (p + q >= e_lo && p + q < e_hi) atomicAdd(&h[wave][score_key(v[q]) >> 21], 1);
+    for (int u = 0; u < kBatch; ++u) load4(m, p0 + u * kSubLen, a.S, a.vec4, v[u]);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int p = p0 + u * kSubLen + q;
+        if (p < p_end && p >= e_lo && p < e_hi) atomicAdd(&h[wave][score_key(v[u][q]) >> 21], 1);
+      }
   }
   __syncthreads();
-  int32_t* out = a.hist + ((size_t)row * a.nc + c) * kBins1;
-  for (int b = tid; b < kBins1; b += kMbThreads) out[b] = h[0][b] + h[1][b] + h[2][b] + h[3][b];
+  int cnt[kPer], own = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int b = kPer * tid + i;
+    cnt[i] = h[0][b] + h[1][b] + h[2][b] + h[3][b];
+    own += cnt[i];
+  }
+  int total;
+  const int excl = block_prefix_excl<kMbWaves>(own, tot, total);
+  int suf = total - excl;  // keys in bins >= kPer * tid
+  int out8[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    out8[i] = suf;
+    suf -= cnt[i];
+  }
+  int4* out = reinterpret_cast<int4*>(a.hist + ((size_t)row * a.nc + c) * kBins1 + kPer * tid);
+  out[0] = make_int4(out8[0], out8[1], out8[2], out8[3]);
+  out[1] = make_int4(out8[4], out8[5], out8[6], out8[7]);
 }
 
 // Inclusive suffix sum over the threads of a block (thread t gets the sum of
@@ -395,60 +454,63 @@ __device__ __forceinline__ void find_digit(const int (&c)[kPer], int r, int* tot
   }
 }
 
-// Per row: the bin of the k-th largest key, the keys above that bin per chunk
-// and the candidate offsets.  One 256-thread workgroup per row.
+// Per row: the bin b1 of the k-th largest key (the largest bin with at least
+// k keys at or above it), the keys above b1 in each chunk and each chunk's
+// offset into the candidate list.  One 256-thread workgroup per row.
 __global__ __launch_bounds__(kMbThreads) void sel_bin_kernel(MbArgs a) {
   constexpr int kPer = kBins1 / kMbThreads;  // 8 bins per thread
   __shared__ int tot[kMbWaves];
+  __shared__ int first[kMbThreads];
   __shared__ int s_b1, s_above;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int row = blockIdx.x;
   const int32_t* hist = a.hist + (size_t)row * a.nc * kBins1;
   if (tid == 0) {  // found by exactly one thread below; set for safety
     s_b1 = 0;
     s_above = 0;
   }
-  int c8[kPer] = {};
+  // suffix counts of the row: the sum of the chunks' suffix counts
+  int g[kPer] = {};
+#pragma unroll 8
   for (int c = 0; c < a.nc; ++c) {
     const int4* p = reinterpret_cast<const int4*>(hist + (size_t)c * kBins1 + kPer * tid);
     const int4 x = p[0], y = p[1];
-    c8[0] += x.x; c8[1] += x.y; c8[2] += x.z; c8[3] += x.w;
-    c8[4] += y.x; c8[5] += y.y; c8[6] += y.z; c8[7] += y.w;
+    g[0] += x.x; g[1] += x.y; g[2] += x.z; g[3] += x.w;
+    g[4] += y.x; g[5] += y.y; g[6] += y.z; g[7] += y.w;
   }
-  find_digit<kMbWaves, kPer>(c8, a.kk, tot, &s_b1, &s_above);
+  first[tid] = g[0];
+  __syncthreads();
+  const int next = tid + 1 < kMbThreads ? first[tid + 1] : 0;  // suffix count of bin kPer (tid + 1)
+  // bin b is b1 iff suf[b] >= k > suf[b + 1]: exactly one bin, since suf is
+  // non-increasing, suf[0] = eligible keys >= k and suf[2048] = 0 < k
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int nb = i + 1 < kPer ? g[i + 1] : next;
+    if (g[i] >= a.kk && nb < a.kk) {
+      s_b1 = kPer * tid + i;
+      s_above = nb;
+    }
+  }
   __syncthreads();
   const int b1 = s_b1 & (kBins1 - 1);
   int32_t* st = a.state + (size_t)row * kStateInts;
   int32_t* ch = a.chunk + (size_t)row * a.nc * 4;
-  // keys above b1 in each chunk: one wave per chunk, lanes over the bins
-  for (int c = wave; c < a.nc; c += kMbWaves) {
-    const int32_t* hc = hist + (size_t)c * kBins1;
-    int t = 0;
-    for (int b = b1 + 1 + lane; b < kBins1; b += kWave) t += hc[b];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off);
-    if (lane == 0) ch[4 * c] = t;
+  // per chunk (one thread each, at most kMbThreads chunks): keys above b1 and
+  // the candidates in b1, then the candidate offsets
+  int cand = 0;
+  if (tid < a.nc) {
+    const int32_t* hc = hist + (size_t)tid * kBins1;
+    const int above_c = b1 + 1 < kBins1 ? hc[b1 + 1] : 0;
+    cand = hc[b1] - above_c;
+    ch[4 * tid] = above_c;
   }
-  // candidate offsets: exclusive prefix over chunks of the count in bin b1
-  if (wave == 0) {
-    int base = 0;
-    for (int c0 = 0; c0 < a.nc; c0 += kWave) {
-      const int c = c0 + lane;
-      const int v = c < a.nc ? hist[(size_t)c * kBins1 + b1] : 0;
-      int x = v;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int o = __shfl_up(x, off);
-        if (lane >= off) x += o;
-      }
-      if (c < a.nc) ch[4 * c + 1] = base + x - v;
-      base += __shfl(x, kWave - 1);
-    }
-    if (lane == 0) {
-      st[0] = b1;
-      st[1] = a.kk - s_above;  // rank of T among the candidates (1-based)
-      st[2] = base;            // candidates
-    }
+  int n_cand;
+  const int off = block_prefix_excl<kMbWaves>(cand, tot, n_cand);
+  if (tid < a.nc) ch[4 * tid + 1] = off;
+  if (tid == 0) {
+    st[0] = b1;
+    st[1] = a.kk - s_above;  // rank of T among the candidates (1-based)
+    st[2] = n_cand;          // candidates
   }
 }
 
@@ -466,21 +528,24 @@ __global__ __launch_bounds__(kMbThreads) void sel_compact_kernel(MbArgs a) {
   const int e_lo = a.n_sink, e_hi = a.S - a.window;
   const int p_end = min(a.S, (c + 1) * a.C);
   // every lane of the block runs the same trip count (ballots below)
-  for (int p0 = c * a.C; p0 < p_end; p0 += kSubLen) {
-    const int p = p0 + 4 * tid;
-    float v[4];
-    load4(m, p, a.S, a.vec4, v);
+  for (int p0 = c * a.C; p0 < p_end; p0 += kBatch * kSubLen) {
+    float v[kBatch][4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t u = score_key(v[q]);
-      const bool is_c = p + q >= e_lo && p + q < e_hi && (u >> 21) == b1;
-      const uint64_t bal = __ballot(is_c);
-      if (bal == 0) continue;
-      int base = 0;
-      if (lane == 0) base = atomicAdd(&n, __popcll(bal));
-      base = __shfl(base, 0);
-      if (is_c) out[base + __popcll(bal & ((1ull << lane) - 1ull))] = u;
-    }
+    for (int u = 0; u < kBatch; ++u) load4(m, p0 + u * kSubLen + 4 * tid, a.S, a.vec4, v[u]);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int p = p0 + u * kSubLen + 4 * tid + q;
+        const uint32_t key = score_key(v[u][q]);
+        const bool is_c = p < p_end && p >= e_lo && p < e_hi && (key >> 21) == b1;
+        const uint64_t bal = __ballot(is_c);
+        if (bal == 0) continue;
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&n, __popcll(bal));
+        base = __shfl(base, 0);
+        if (is_c) out[base + __popcll(bal & ((1ull << lane) - 1ull))] = key;
+      }
   }
 }
 
@@ -620,19 +685,31 @@ __global__ __launch_bounds__(kMbThreads) void sel_emit_kernel(MbArgs a) {
     fa_before = forced_before(c * a.C, S, a.window, a.n_sink);
   }
   const int p_end = min(S, (c + 1) * a.C);
+  float vb[kBatch][4];
   for (int p0 = c * a.C; p0 < p_end; p0 += kSubLen) {
     const int p = p0 + 4 * tid;
+    // keys of the next kBatch sub-chunks, loaded together
+    const int u = ((p0 - c * a.C) / kSubLen) % kBatch;
+    if (a.mode == kSelect && u == 0) {
+#pragma unroll
+      for (int uu = 0; uu < kBatch; ++uu) load4(m, p + uu * kSubLen, S, a.vec4, vb[uu]);
+    }
     bool fa[4], tie[4];
     if (a.mode == kSelect) {
       float v[4];
-      load4(m, p, S, a.vec4, v);
+#pragma unroll
+      for (int uu = 0; uu < kBatch; ++uu)  // v = vb[u] with a constant index
+        if (uu == u) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = vb[uu][q];
+        }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int j = p + q;
         const bool elig = j >= e_lo && j < e_hi;
-        const uint32_t u = score_key(v[q]);
-        fa[q] = j < S && (!elig || u > T);
-        tie[q] = elig && u == T;
+        const uint32_t key = score_key(v[q]);
+        fa[q] = j < S && (!elig || key > T);
+        tie[q] = elig && key == T;
       }
     } else {
 #pragma unroll
@@ -681,8 +758,6 @@ __global__ __launch_bounds__(kMbThreads) void sel_emit_kernel(MbArgs a) {
 // Chunking of the split path: chunk length a multiple of kSubLen, at least
 // 4096, aiming at about 1024 workgroups per launch and at most kMaxChunks
 // chunks per row (the per-row kernels then read at most 2 MB of histograms).
-constexpr int kMaxChunks = 256;
-constexpr int kMinChunk = 4 * kSubLen;
 
 void mb_plan(int64_t rows, int S, int& nc, int& C) {
   int64_t want = (1024 + rows - 1) / rows;
