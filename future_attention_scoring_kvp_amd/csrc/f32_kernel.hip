@@ -13,10 +13,12 @@
 //   block mode:     the same sums per query block of the Golden-Eviction
 //                   scores, their means and suffix maxima (ForesightKV §3.2).
 //
-// One thread per query row (LSE) or per key (mass); tiles of 32 keys or
-// query rows are staged in LDS and shared by the 256 rows / keys of a
-// workgroup.  Dot products are fp32 fused multiply-adds in index order; the
-// LSE uses a running maximum, so no row overflows; the mass sums in fp64.
+// R consecutive lanes per query row (LSE) or per key (mass), R = 1 for large
+// problems and up to 16 for small ones; tiles of 32 KiB of key or query rows
+// are staged in LDS and shared by the workgroup.  Dot products are fp32 fused
+// multiply-adds (four partial sums); the LSE uses a running maximum, so no
+// row overflows; the mass sums in fp64; the lanes of a group merge their
+// partial results in a fixed order.
 // These passes are O(S^2 d) on the VALU: the exact path for fp32 callers,
 // not the fast one (bf16 inputs run on the matrix cores).
 #include "kvp_device.h"
@@ -26,7 +28,11 @@ namespace kvp {
 namespace {
 
 constexpr int kF32Threads = 256;
-constexpr int kF32Tile = 32;
+// rows per LDS tile: 32 KiB of fp32 rows (128 at d = 64, 64 at d = 128)
+template <int D>
+constexpr int f32_tile() {
+  return 32768 / (4 * D);
+}
 
 struct F32LseArgs {
   const float* q;
@@ -39,16 +45,50 @@ struct F32LseArgs {
   int window;
 };
 
-template <int D, bool kSp>
+// Dot product of a register row and an LDS row, with four partial sums for
+// instruction-level parallelism.
+template <int D>
+__device__ __forceinline__ float dot_f32(const float (&x)[D], const float* y) {
+  float p[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int e = 0; e < D; ++e) p[e & 3] = __builtin_fmaf(x[e], y[e], p[e & 3]);
+  return (p[0] + p[1]) + (p[2] + p[3]);
+}
+
+// Online log-sum-exp state (running maximum m, sum s relative to it).
+__device__ __forceinline__ void lse_add(float& m, float& s, float x) {
+  if (x > m) {
+    s = s * expf(m - x) + 1.f;
+    m = x;
+  } else {
+    s += expf(x - m);
+  }
+}
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  if (m2 > m) {
+    s = s * expf(m - m2) + s2;
+    m = m2;
+  } else if (s2 > 0.f) {
+    s += s2 * expf(m2 - m);
+  }
+}
+
+// R consecutive lanes share a query row (R = 1 for large problems, more for
+// small ones so that the grid fills the GPU); lane r of a group takes the keys
+// j = r (mod R), and the group merges its partial states in a fixed order.
+template <int D, bool kSp, int R>
 __global__ __launch_bounds__(kF32Threads) void f32_lse_kernel(F32LseArgs a) {
+  constexpr int kRows = kF32Threads / R;  // query rows per workgroup
+  constexpr int kF32Tile = f32_tile<D>();
   __shared__ float kt[kF32Tile][D];
   __shared__ int rt[kF32Tile];
   const int S = a.S;
-  const int per_head = (S + kF32Threads - 1) / kF32Threads;
+  const int per_head = (S + kRows - 1) / kRows;
   const int bg = blockIdx.x / per_head;  // b * Hq + g
-  const int i0 = (blockIdx.x - bg * per_head) * kF32Threads;
+  const int i0 = (blockIdx.x - bg * per_head) * kRows;
   const int b = bg / a.Hq, g = bg - b * a.Hq, h = g / a.G;
-  const int i = i0 + (int)threadIdx.x;
+  const int r = (int)threadIdx.x % R;
+  const int i = i0 + (int)threadIdx.x / R;
   const bool valid = i < S;
   const float* __restrict__ kb = a.k + (size_t)(b * a.Hkv + h) * S * D;
   float qv[D];
@@ -60,35 +100,40 @@ __global__ __launch_bounds__(kF32Threads) void f32_lse_kernel(F32LseArgs a) {
   int cut = 0;
   if (kSp && valid) cut = a.cutoff[(size_t)(b * a.Hkv + h) * S + i];
   float m = -__builtin_inff(), s = 0.f;
-  const int j_end = min(S, i0 + kF32Threads);  // keys any row of the block reaches
+  const int j_end = min(S, i0 + kRows);  // keys any row of the block reaches
   for (int j0 = 0; j0 < j_end; j0 += kF32Tile) {
     __syncthreads();
     for (int e = threadIdx.x; e < kF32Tile * D; e += kF32Threads) {
       const int jj = j0 + e / D;
       kt[e / D][e % D] = jj < S ? kb[(size_t)jj * D + e % D] : 0.f;
     }
-    if (kSp && threadIdx.x < kF32Tile) {
-      const int jj = j0 + (int)threadIdx.x;
-      rt[threadIdx.x] = jj < S ? a.rank[(size_t)(b * a.Hkv + h) * S + jj] : 0;
-    }
+    if (kSp)
+      for (int t = threadIdx.x; t < kF32Tile; t += kF32Threads) {
+        const int jj = j0 + t;
+        rt[t] = jj < S ? a.rank[(size_t)(b * a.Hkv + h) * S + jj] : 0;
+      }
     __syncthreads();
     if (!valid) continue;
-    const int jn = min(kF32Tile, i - j0 + 1);  // keys j0 .. min(i, j0 + 31)
-    for (int jj = 0; jj < jn; ++jj) {
+    const int jn = min(kF32Tile, i - j0 + 1);  // keys j0 .. min(i, j0 + kF32Tile - 1)
+    for (int jj = r; jj < jn; jj += R) {
       if (kSp && !(i - (j0 + jj) < a.window || rt[jj] <= cut)) continue;
-      float dot = 0.f;
-#pragma unroll
-      for (int e = 0; e < D; ++e) dot = __builtin_fmaf(qv[e], kt[jj][e], dot);
-      const float x = dot * a.scale;
-      if (x > m) {
-        s = s * expf(m - x) + 1.f;
-        m = x;
-      } else {
-        s += expf(x - m);
-      }
+      lse_add(m, s, dot_f32<D>(qv, kt[jj]) * a.scale);
     }
   }
-  if (valid) a.lse[(size_t)bg * S + i] = s > 0.f ? m + logf(s) : -__builtin_inff();
+#pragma unroll
+  for (int off = 1; off < R; off <<= 1) {
+    const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off);
+    // lanes merge in the same order on both sides of each exchange
+    if ((r & off) == 0)
+      lse_merge(m, s, m2, s2);
+    else {
+      float mm = m2, ss = s2;
+      lse_merge(mm, ss, m, s);
+      m = mm;
+      s = ss;
+    }
+  }
+  if (valid && r == 0) a.lse[(size_t)bg * S + i] = s > 0.f ? m + logf(s) : -__builtin_inff();
 }
 
 struct F32MassArgs {
@@ -105,20 +150,37 @@ struct F32MassArgs {
   float* seg_future;
 };
 
-template <int D, bool kSeg>
+// Sum of a double over the R lanes of a group, in a fixed order.
+template <int R>
+__device__ __forceinline__ double group_sum(double v) {
+#pragma unroll
+  for (int off = 1; off < R; off <<= 1) {
+    const double o = __shfl_xor(v, off);
+    v = ((threadIdx.x & off) == 0) ? v + o : o + v;
+  }
+  return v;
+}
+
+// R consecutive lanes share a key; lane r of a group takes the query rows
+// i = r (mod R) of every staged tile.
+template <int D, bool kSeg, int R>
 __global__ __launch_bounds__(kF32Threads) void f32_mass_kernel(F32MassArgs a) {
+  constexpr int kKeys = kF32Threads / R;  // keys per workgroup
+  // block mode: tiles of 32 rows, so that none straddles a block edge
+  constexpr int kF32Tile = kSeg ? 32 : f32_tile<D>();
   __shared__ float qt[kF32Tile][D];
   __shared__ float lt[kF32Tile];
   const int S = a.S, w = a.window;
   const int U = a.per_head ? a.Hq : a.Hkv;
-  const int per_unit = (S + kF32Threads - 1) / kF32Threads;
+  const int per_unit = (S + kKeys - 1) / kKeys;
   const int bu = blockIdx.x / per_unit;  // b * U + u
-  const int j0 = (blockIdx.x - bu * per_unit) * kF32Threads;
+  const int j0 = (blockIdx.x - bu * per_unit) * kKeys;
   const int b = bu / U, u = bu - b * U;
   const int h = a.per_head ? u / a.G : u;
   const int g_lo = a.per_head ? u : u * a.G;
   const int ng = a.per_head ? 1 : a.G;
-  const int j = j0 + (int)threadIdx.x;
+  const int r = (int)threadIdx.x % R;
+  const int j = j0 + (int)threadIdx.x / R;
   const bool valid = j < S;
   float kv[D];
   {
@@ -142,19 +204,16 @@ __global__ __launch_bounds__(kF32Threads) void f32_mass_kernel(F32MassArgs a) {
         const int ii = i0 + e / D;
         qt[e / D][e % D] = ii < S ? qb[(size_t)ii * D + e % D] : 0.f;
       }
-      if (threadIdx.x < kF32Tile) {
-        const int ii = i0 + (int)threadIdx.x;
-        lt[threadIdx.x] = ii < S ? a.lse[(size_t)(b * a.Hq + g) * S + ii] : 0.f;
+      for (int t = threadIdx.x; t < kF32Tile; t += kF32Threads) {
+        const int ii = i0 + t;
+        lt[t] = ii < S ? a.lse[(size_t)(b * a.Hq + g) * S + ii] : 0.f;
       }
       __syncthreads();
       if (!valid) continue;
-      for (int ii = 0; ii < kF32Tile; ++ii) {
+      for (int ii = r; ii < kF32Tile; ii += R) {
         const int i = i0 + ii;
         if (i >= S || i < j + w) continue;
-        float dot = 0.f;
-#pragma unroll
-        for (int e = 0; e < D; ++e) dot = __builtin_fmaf(qt[ii][e], kv[e], dot);
-        acc += (double)expf(dot * a.scale - lt[ii]);
+        acc += (double)expf(dot_f32<D>(kv, qt[ii]) * a.scale - lt[ii]);
       }
     }
     if constexpr (kSeg) {
@@ -162,9 +221,10 @@ __global__ __launch_bounds__(kF32Threads) void f32_mass_kernel(F32MassArgs a) {
       const int t = (i0 - a.seg_start) / a.seg_len;
       const int end = min(S, a.seg_start + (t + 1) * a.seg_len);
       if (i0 + kF32Tile >= end) {
-        if (valid) {
+        const double tot = group_sum<R>(acc);
+        if (valid && r == 0) {
           const int rows = end - (a.seg_start + t * a.seg_len);
-          const float mean = (float)(acc / ((double)rows * ng));
+          const float mean = (float)(tot / ((double)rows * ng));
           if (a.seg_block) a.seg_block[(seg_row0 + t) * S + j] = mean;
           a.seg_future[(seg_row0 + t) * S + j] = mean;  // turned into the suffix maximum below
         }
@@ -173,8 +233,8 @@ __global__ __launch_bounds__(kF32Threads) void f32_mass_kernel(F32MassArgs a) {
       }
     }
   }
-  if (!valid) return;
   if constexpr (kSeg) {
+    if (!valid || r != 0) return;
     // blocks before the first one swept: no query sees the key there; then
     // the suffix maximum from the last block down
     for (int t = 0; t < t_first; ++t) {
@@ -188,7 +248,35 @@ __global__ __launch_bounds__(kF32Threads) void f32_mass_kernel(F32MassArgs a) {
       *f = run;
     }
   } else {
-    a.mass[(size_t)bu * S + j] = (float)acc;
+    const double tot = group_sum<R>(acc);
+    if (valid && r == 0) a.mass[(size_t)bu * S + j] = (float)tot;
+  }
+}
+
+// Lanes per row / key: 1 when the problem already gives every CU several
+// workgroups, up to 16 for small ones.
+int lanes_for(int64_t rows) {
+  int R = 1;
+  while (R < 16 && rows * R < (int64_t)kNumCUs * kF32Threads * 2) R *= 2;
+  return R;
+}
+
+template <int D, bool kSp, int R>
+void lse_f32_launch(const F32LseArgs& a, hipStream_t stream) {
+  constexpr int kRows = kF32Threads / R;
+  const int64_t blocks = (int64_t)a.B * a.Hq * ((a.S + kRows - 1) / kRows);
+  hipLaunchKernelGGL((f32_lse_kernel<D, kSp, R>), dim3((unsigned)blocks), dim3(kF32Threads), 0,
+                     stream, a);
+}
+
+template <int D, bool kSp>
+void lse_f32_r(const F32LseArgs& a, int R, hipStream_t stream) {
+  switch (R) {
+    case 1: lse_f32_launch<D, kSp, 1>(a, stream); break;
+    case 2: lse_f32_launch<D, kSp, 2>(a, stream); break;
+    case 4: lse_f32_launch<D, kSp, 4>(a, stream); break;
+    case 8: lse_f32_launch<D, kSp, 8>(a, stream); break;
+    default: lse_f32_launch<D, kSp, 16>(a, stream); break;
   }
 }
 
@@ -208,14 +296,31 @@ hipError_t lse_f32_d(const void* q, const void* k, const Shape& sh, float scale,
   a.rank = rank;
   a.cutoff = cutoff;
   a.window = window;
-  const int64_t blocks = (int64_t)sh.B * sh.Hq * ((sh.S + kF32Threads - 1) / kF32Threads);
+  const int R = lanes_for((int64_t)sh.B * sh.Hq * sh.S);
   if (rank)
-    hipLaunchKernelGGL((f32_lse_kernel<D, true>), dim3((unsigned)blocks), dim3(kF32Threads), 0,
-                       stream, a);
+    lse_f32_r<D, true>(a, R, stream);
   else
-    hipLaunchKernelGGL((f32_lse_kernel<D, false>), dim3((unsigned)blocks), dim3(kF32Threads), 0,
-                       stream, a);
+    lse_f32_r<D, false>(a, R, stream);
   return hipGetLastError();
+}
+
+template <int D, bool kSeg, int R>
+void mass_f32_launch(const F32MassArgs& a, int64_t units, hipStream_t stream) {
+  constexpr int kKeys = kF32Threads / R;
+  const int64_t blocks = units * ((a.S + kKeys - 1) / kKeys);
+  hipLaunchKernelGGL((f32_mass_kernel<D, kSeg, R>), dim3((unsigned)blocks), dim3(kF32Threads), 0,
+                     stream, a);
+}
+
+template <int D, bool kSeg>
+void mass_f32_r(const F32MassArgs& a, int64_t units, int R, hipStream_t stream) {
+  switch (R) {
+    case 1: mass_f32_launch<D, kSeg, 1>(a, units, stream); break;
+    case 2: mass_f32_launch<D, kSeg, 2>(a, units, stream); break;
+    case 4: mass_f32_launch<D, kSeg, 4>(a, units, stream); break;
+    case 8: mass_f32_launch<D, kSeg, 8>(a, units, stream); break;
+    default: mass_f32_launch<D, kSeg, 16>(a, units, stream); break;
+  }
 }
 
 template <int D>
@@ -241,13 +346,11 @@ hipError_t mass_f32_d(const void* q, const void* k, const float* lse, const Shap
   a.seg_block = seg.block;
   a.seg_future = seg.future;
   const int64_t units = (int64_t)sh.B * (per_head ? sh.Hq : sh.Hkv);
-  const int64_t blocks = units * ((sh.S + kF32Threads - 1) / kF32Threads);
+  const int R = lanes_for(units * sh.S);
   if (seg.n > 0)
-    hipLaunchKernelGGL((f32_mass_kernel<D, true>), dim3((unsigned)blocks), dim3(kF32Threads), 0,
-                       stream, a);
+    mass_f32_r<D, true>(a, units, R, stream);
   else
-    hipLaunchKernelGGL((f32_mass_kernel<D, false>), dim3((unsigned)blocks), dim3(kF32Threads), 0,
-                       stream, a);
+    mass_f32_r<D, false>(a, units, R, stream);
   return hipGetLastError();
 }
 
