@@ -133,7 +133,8 @@ def read_probe(nbytes: int, reps: int) -> None:
     print(json.dumps({"read_probe_bytes": nbytes, "reps": reps}))
 
 
-def cpu_baseline(wl, li0, n_heads: int, gpu=None, max_pairs: float = 4.5e9) -> dict:
+def cpu_baseline(wl, li0, n_heads: int, gpu=None, max_pairs: float = 4.5e9,
+                 single_thread_pairs: float = 2e8) -> dict:
     """The CPU oracle (dense fp64 softmax rows + explicit column sums), as it
     stands, on whole (batch 0, KV head) units 0 .. n_heads-1 of layer 0: the
     query rows of their G query heads from row_lo on, row_lo = 0 unless that
@@ -142,7 +143,8 @@ def cpu_baseline(wl, li0, n_heads: int, gpu=None, max_pairs: float = 4.5e9) -> d
     sample covers (its LSE work included in the time).  With ``gpu`` = the
     GPU's layer-0 (lse [B,Hq,S], mass [B,Hkv,S], keep [B,Hkv,n]) as numpy
     arrays, also the parity of the sample: LSE of its rows, masses of the keys
-    its rows complete, and (whole units only) the keep-sets."""
+    its rows complete, and (whole units only) the keep-sets.  Samples of at
+    most single_thread_pairs pairs are timed on one thread as well."""
     import numpy as np
     import oracle
     S, w, G = wl.S, wl.window, wl.G
@@ -176,6 +178,14 @@ def cpu_baseline(wl, li0, n_heads: int, gpu=None, max_pairs: float = 4.5e9) -> d
            "kind": "oracle", "seconds": round(dt, 3),
            "sample": (f"layer 0, batch 0, KV heads 0..{n_heads - 1} ({n_heads * G} query heads), "
                       f"{rows} {S} query rows: {pairs} future-mass pairs, LSE included")}
+    if pairs <= single_thread_pairs and threads > 1:
+        # small samples (the tiny and 4K workloads) are also timed on one thread
+        t1 = time.perf_counter()
+        for h in range(n_heads):
+            oracle.future_mass(li0.q, li0.k, w, b_only=0, h_only=h, row_lo=row_lo, nthreads=1,
+                               f32_exact=wl.dtype == "f32")
+        d1 = time.perf_counter() - t1
+        out["single_thread"] = {"value": pairs / d1 / 1e9, "cores": 1, "seconds": round(d1, 3)}
     if gpu is not None:
         lse_g, mass_g, keep_g = gpu
         lse_err, rel_err, n_bad, statuses = 0.0, 0.0, 0, []

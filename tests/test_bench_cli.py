@@ -72,3 +72,40 @@ def test_cpu_baseline_sample_is_bounded():
     tail = sum(i - wl.window + 1 for i in range(wl.S - rows, wl.S) if i >= wl.window)
     assert pairs == tail <= full / 4
     assert tail + (wl.S - rows - 1 - wl.window + 1) > full / 4
+
+
+def test_cpu_baseline_parity_leg_and_single_thread():
+    """The parity leg against the oracle's own values is ok; a perturbed mass
+    is counted; small samples are also timed on one thread."""
+    import numpy as np
+    import kvp_inputs
+    import oracle
+    wl = kvp_inputs.workload(1)
+    li = kvp_inputs.make_layer(wl, 0)
+    ref = oracle.future_mass(li.q, li.k, wl.window, f32_exact=True)
+    keep = oracle.select(ref["mass"], wl.window, wl.n_sink, wl.top_k)
+    gpu = (ref["lse"].astype(np.float32), ref["mass"].astype(np.float32), keep)
+    out = bench.cpu_baseline(wl, li, 1, gpu=gpu)
+    p = out["parity"]
+    assert p["ok"] and p["keep"] == ["exact"] and p["mass_violations"] == 0
+    assert p["lse_max_abs_err"] < 1e-6
+    assert out["single_thread"]["cores"] == 1 and out["single_thread"]["value"] > 0
+    bad = ref["mass"].astype(np.float32).copy()
+    bad[0, 0, 7] *= 1.01
+    out = bench.cpu_baseline(wl, li, 1, gpu=(gpu[0], bad, keep))
+    assert not out["parity"]["ok"] and out["parity"]["mass_violations"] == 1
+
+
+def test_keep_status_rules():
+    import numpy as np
+    S, w, s, k = 20, 2, 2, 4
+    mass = np.linspace(1.0, 0.1, S)            # strictly decreasing: the top-k are 2..5
+    exact = np.array(sorted(set(range(s)) | set(range(S - w, S)) | {2, 3, 4, 5}))
+    assert bench.keep_status(exact, mass, S, w, s, k, exact) == "exact"
+    other = np.array(sorted(set(range(s)) | set(range(S - w, S)) | {2, 3, 4, 6}))
+    assert bench.keep_status(other, mass, S, w, s, k, exact) == "differs"
+    tied = mass.copy()
+    tied[5] = tied[6] = 0.7                    # the k-th and (k+1)-th tie
+    ex2 = np.array(sorted(set(range(s)) | set(range(S - w, S)) | {2, 3, 4, 5}))
+    alt = np.array(sorted(set(range(s)) | set(range(S - w, S)) | {2, 3, 4, 6}))
+    assert bench.keep_status(alt, tied, S, w, s, k, ex2) == "tie-band"
