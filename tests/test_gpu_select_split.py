@@ -105,3 +105,17 @@ def test_split_many_rows_batched_layers():
     keep = kvp.select_topk(dev, 300, 4, 1000).cpu().numpy()
     ref = oracle.select(m.reshape(24, 1, S).astype(np.float64), 300, 4, 1000).reshape(3, 8, -1)
     assert np.array_equal(keep, ref)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_split_random_shapes(seed):
+    """Seeded random rows, lengths, windows, sinks, budgets and score kinds."""
+    rng = np.random.default_rng(7700 + seed)
+    S = int(rng.integers(32769, 300001))
+    rows = int(rng.integers(1, 6))
+    kind = ["normal", "ties", "mass", "signed", "constant", "two"][seed]
+    w = int(rng.integers(0, S // 4))
+    s = int(rng.integers(0, 64))
+    k = int(rng.integers(0, S))
+    say(f"[select split] random {kind} rows={rows} S={S} w={w} s={s} k={k}")
+    check(scores(kind, rows, S, rng), w, s, k, f"random {seed}")
