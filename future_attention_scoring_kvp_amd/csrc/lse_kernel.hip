@@ -111,7 +111,8 @@ struct LTile<true> {
 
 template <int D, typename T, int W, bool kSp, bool kPair, int NB>
 __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
-  static_assert(NB >= 2 && NB <= lse_query_blocks<T, kSp>(), "query blocks per wave");
+  static_assert(NB >= 1 && NB <= lse_query_blocks<T, kSp>(), "query blocks per wave");
+  static_assert(NB >= 2 || !kSp, "one query block per wave: dense pass only");
   using C = LseCfg<D, W, NB>;
   using Tile = LTile<kSp>;
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[C::kStageBytes];
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
     for (int ks = 0; ks < C::kKSteps; ++ks) {
       const u32x4_t ak = *reinterpret_cast<const u32x4_t*>(src + ks * C::kFragBytes);
       t.s0 = mfma_32x32x16(ak, qf[0][ks], ks ? t.s0 : f32x16_t{});
-      t.s1 = mfma_32x32x16(ak, qf[1][ks], ks ? t.s1 : f32x16_t{});
+      if constexpr (NB >= 2) t.s1 = mfma_32x32x16(ak, qf[NB >= 2 ? 1 : 0][ks], ks ? t.s1 : f32x16_t{});
       if constexpr (NB == 3) t.s2 = mfma_32x32x16(ak, qf[2][ks], ks ? t.s2 : f32x16_t{});
     }
     if constexpr (kSp) {
@@ -270,11 +271,11 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       t0 += fast_exp2(__builtin_fmaf(t.s0[v], c, -u0));
-      t1 += fast_exp2(__builtin_fmaf(t.s1[v], c, -u1));
+      if constexpr (NB >= 2) t1 += fast_exp2(__builtin_fmaf(t.s1[v], c, -u1));
       if constexpr (NB == 3) t2 += fast_exp2(__builtin_fmaf(t.s2[v], c, -u2));
     }
     sum0 += t0;
-    sum1 += t1;
+    if constexpr (NB >= 2) sum1 += t1;
     if constexpr (NB == 3) sum2 += t2;
   };
   // sparse mode, blocks outside every window: a key counts iff its rank is
@@ -334,16 +335,18 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
     for (int v = 0; v < 16; ++v) {
       const int r = 8 * (v >> 2) + (v & 3);
       const float x0 = __builtin_fmaf(t.s0[v], c, -u0);
-      const float x1 = __builtin_fmaf(t.s1[v], c, -u1);
       t0 += fast_exp2(r <= lim0 ? x0 : -__builtin_inff());
-      t1 += fast_exp2(r <= lim1 ? x1 : -__builtin_inff());
+      if constexpr (NB >= 2) {
+        const float x1 = __builtin_fmaf(t.s1[v], c, -u1);
+        t1 += fast_exp2(r <= lim1 ? x1 : -__builtin_inff());
+      }
       if constexpr (NB == 3) {
         const float x2 = __builtin_fmaf(t.s2[v], c, -u2);
         t2 += fast_exp2(r <= lim2 ? x2 : -__builtin_inff());
       }
     }
     sum0 += t0;
-    sum1 += t1;
+    if constexpr (NB >= 2) sum1 += t1;
     if constexpr (NB == 3) sum2 += t2;
   };
   // Shifts from the first key block (key 0 is valid for every row).
@@ -353,7 +356,8 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
     for (int v = 0; v < 16; ++v) {
       const int j = mfma_row(v, lane);
       if (j <= iq0 && j < S) m0 = fmaxf(m0, t.s0[v]);
-      if (j <= iq1 && j < S) m1 = fmaxf(m1, t.s1[v]);
+      if constexpr (NB >= 2)
+        if (j <= iq1 && j < S) m1 = fmaxf(m1, t.s1[v]);
       if constexpr (NB == 3)
         if (j <= iq2 && j < S) m2 = fmaxf(m2, t.s2[v]);
     }
@@ -380,14 +384,17 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
         exp_rank(cur);
       else
         exp_full(cur);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      // operand reads issued ahead: four with one block per wave (each read
+      // then feeds a single MFMA), else two
+      constexpr int kAhead = NB == 1 ? 4 : 2;
+      __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
       for (int m = 0; m < C::kMfmaPerBlock; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
         __builtin_amdgcn_sched_group_barrier(0x400, kTransPerMfma, 0);
         // one operand read per key slice, i.e. after every NB-th MFMA
-        if (m % NB == NB - 1 && m < NB * C::kKSteps - NB)
+        if (NB == 1 ? m < C::kKSteps - kAhead : (m % NB == NB - 1 && m < NB * C::kKSteps - NB))
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         if (kSp && m == C::kKSteps - 1)  // the next block's four rank reads
           __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -459,7 +466,7 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
 
   // Combine the two half-columns (lanes l and l^32 hold the same query).
   sum0 += __shfl_xor(sum0, 32);
-  sum1 += __shfl_xor(sum1, 32);
+  if constexpr (NB >= 2) sum1 += __shfl_xor(sum1, 32);
   if constexpr (NB == 3) sum2 += __shfl_xor(sum2, 32);
   if (active && lane < 32) {
     float* out = a.lse + (size_t)(b * a.Hq + h * G + g) * S;
@@ -472,7 +479,7 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
     const bool ok0 = sum0 < __builtin_inff() && l0 == l0 && (!kSp || sum0 >= lo);
     const bool ok1 = sum1 < __builtin_inff() && l1 == l1 && (!kSp || sum1 >= lo);
     if (iq0 < S) out[iq0] = ok0 ? l0 : __builtin_inff();
-    if (iq1 < S) out[iq1] = ok1 ? l1 : __builtin_inff();
+    if (NB >= 2 && iq1 < S) out[iq1] = ok1 ? l1 : __builtin_inff();
     if constexpr (NB == 3) {
       const float l2 = (u2 + __log2f(sum2)) * kLn2;
       const bool ok2 = sum2 < __builtin_inff() && l2 == l2;
@@ -605,8 +612,10 @@ hipError_t launch_lse_w(const void* q, const void* k, const Shape& sh, float sca
   return hipGetLastError();
 }
 
-// 8-wave workgroups (one per CU) when the grid holds at least two per CU,
-// else 4-wave workgroups (two per CU) with two query blocks per wave.  Three
+// 8-wave workgroups (one per CU) when the grid holds at least two per CU;
+// else 8-wave workgroups of one query block per wave, each taking a long and
+// a short tile, when those pairs fill whole rounds of the CUs; else 4-wave
+// workgroups (two per CU) with two query blocks per wave.  Three
 // query blocks per wave only where they still give such a grid.  The number
 // of blocks per wave does not change the result: every row sums the same key
 // blocks in the same order.
@@ -623,6 +632,15 @@ hipError_t launch_lse_t(const void* q, const void* k, const Shape& sh, float sca
   }
   if (blocks8(LseCfg<D, 8, 2>::kQueriesPerWave) >= 2 * kNumCUs)
     return launch_lse_w<D, T, 8, kSp, 2>(q, k, sh, scale, lse, sp, stream);
+  if constexpr (!kSp) {
+    // one query block per wave, workgroups pairing the longest rows with the
+    // shortest, when those pairs fill whole rounds of the CUs
+    const int64_t n_wg = (((int64_t)sh.S + kBlk - 1) / kBlk * sh.G + 7) / 8;
+    const int64_t pairs = (int64_t)sh.B * sh.Hkv * ((n_wg + 1) / 2);
+    const int64_t rounds = (pairs + kNumCUs - 1) / kNumCUs;
+    if (n_wg >= 2 && pairs * 20 >= rounds * kNumCUs * 19)
+      return launch_lse_w<D, T, 8, kSp, 1>(q, k, sh, scale, lse, sp, stream);
+  }
   return launch_lse_w<D, T, 4, kSp, 2>(q, k, sh, scale, lse, sp, stream);
 }
 

@@ -52,21 +52,28 @@
 namespace kvp {
 namespace {
 
-template <int D, int W>
+template <int D, int W, int KB>
 struct MassCfg {
   static constexpr int kWaves = W;
   static constexpr int kThreads = kWaves * kWave;
-  static constexpr int kKeysPerWave = 64;
+  static constexpr int kKeyBlocks = KB;                 // 32-row key blocks per wave
+  static constexpr int kKeysPerWave = 32 * KB;
   static constexpr int kKeysPerWG = kWaves * kKeysPerWave;
   static constexpr int kKSteps = D / 16;                // 16-wide slices of d
   static constexpr int kFragBytes = kWave * 16;         // one B operand (1 KB)
   static constexpr int kSlotBytes = kKSteps * kFragBytes;
   static constexpr int kSlots = kWaves;                 // wave w stages slot w
   static constexpr int kStageBytes = kSlots * kSlotBytes;
-  static constexpr int kMfmaPerPair = 2 * kKSteps;
+  static constexpr int kMfmaPerPair = KB * kKSteps;
   // per value: fma and add on the VALU, exp2 on the transcendental unit
-  static constexpr int kAluPerPair = 2 * 32;
-  static constexpr int kTransPerPair = 32;
+  static constexpr int kAluPerPair = 2 * 16 * KB;
+  static constexpr int kTransPerPair = 16 * KB;
+  // LDS reads issued before a pair's first MFMA (its lse2 and the first
+  // operands); the rest go out one after every KB-th MFMA
+  static constexpr int kReadsAhead = KB == 1 ? 4 : 3;
+  // One key block per wave makes a step half as long, too short to cover
+  // the copies' latency: they are issued two stages ahead instead.
+  static constexpr bool kDeep = KB == 1;
   static constexpr int kRedStride = 33;                 // column partials per key (+1 pad)
   static constexpr int kRedWaveFloats = kKeysPerWave * kRedStride;
   // the final reduction reuses the two stage buffers when they hold every
@@ -99,8 +106,10 @@ struct MassArgs {
 };
 
 struct Tile {
-  f32x16_t s0, s1;  // logits of key blocks 0 / 1 (rows) x 32 queries (columns)
-  float l2;         // lse2 of this lane's query column
+  f32x16_t s0, s1;  // logits of key blocks 0 / 1 (rows) x 32 queries (columns);
+                    // one key block per wave: key block 0 x slots A / B
+  float l2;         // lse2 of this lane's query column (slot A)
+  float l2b;        // one key block per wave: the same for slot B
 };
 
 // Sum of a 16-value register row over the 32 lanes of a wave half (lanes
@@ -122,9 +131,10 @@ __device__ __forceinline__ float reduce_columns(f32x16_t& x, int l32) {
   return x[0] + __shfl_xor(x[0], 1);
 }
 
-template <int D, typename T, int W, bool kSeg, bool kPair>
+template <int D, typename T, int W, int KB, bool kSeg, bool kPair>
 __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
-  using C = MassCfg<D, W>;
+  static_assert(KB == 2 || (KB == 1 && !kSeg), "one key block per wave: mass mode only");
+  using C = MassCfg<D, W, KB>;
   __shared__ __attribute__((aligned(1024))) unsigned char q_lds0[C::kStageBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char q_lds1[C::kStageBytes];
   __shared__ float l_lds0[C::kSlots * kBlk];
@@ -176,12 +186,12 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
   const float* __restrict__ lgroup = a.lse + (size_t)(b * a.Hq + g0) * S;
   const uint32_t head_bytes = (uint32_t)S * D * sizeof(T);
 
-  // Stationary keys: A operands of the two 32-row blocks, all slices of d.
-  u32x4_t kf[2][C::kKSteps];
+  // Stationary keys: A operands of the wave's 32-row blocks, all slices of d.
+  u32x4_t kf[KB][C::kKSteps];
   {
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase, head_bytes);
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < KB; ++rb)
 #pragma unroll
       for (int ks = 0; ks < C::kKSteps; ++ks)  // keys >= S read 0
         kf[rb][ks] = buf_load8(kr, (uint32_t)(key0 + 32 * rb + l32) * D + 16 * ks + 8 * h32,
@@ -328,6 +338,48 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
       }
       advance(ld_qb, ld_g);  // the pair this wave stages in the next stage
     };
+    // Two stages ahead (one key block per wave): a stage's copies are issued
+    // whole at the start of the stage two before it, into one of two register
+    // sets, and stored to LDS just before the barrier of the stage before it.
+    // Loads and stores are unconditional (a pair past the sweep reads zeros
+    // through an empty resource and fills a slot no MFMA reads), so the
+    // store waits only for its own set.
+    u32x4_t deep_regs[2][C::kDeep ? C::kKSteps : 1];
+    float deep_lse[2] = {0.f, 0.f};
+    int deep_qb[2] = {0, 0};
+    auto deep_issue = [&](auto setc, int st) __attribute__((always_inline)) {
+      if constexpr (C::kDeep) {
+        constexpr int kSet = decltype(setc)::value;
+        const bool valid = st * C::kSlots + wave < n_pairs;
+        deep_qb[kSet] = ld_qb;
+        const __amdgpu_buffer_rsrc_t lr =
+            make_rsrc(lgroup + (size_t)ld_g * S, valid ? (uint32_t)S * 4u : 0u);
+        deep_lse[kSet] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(lr, (uint32_t)(ld_qb * kBlk + l32) * 4u, 0, 0));
+        const __amdgpu_buffer_rsrc_t qr =
+            make_rsrc(qgroup + (size_t)ld_g * S * D, valid ? head_bytes : 0u);
+        const uint32_t e0 = (uint32_t)(ld_qb * kBlk + l32) * D + 8 * h32;
+#pragma unroll
+        for (int t = 0; t < C::kKSteps; ++t)  // rows >= S read 0
+          deep_regs[kSet][t] = buf_load8(qr, e0 + 16 * t, static_cast<const T*>(nullptr));
+        advance(ld_qb, ld_g);
+      }
+    };
+    auto deep_store = [&](auto setc, int st, unsigned char* qdst, float* ldst)
+                          __attribute__((always_inline)) {
+      if constexpr (C::kDeep) {
+        constexpr int kSet = decltype(setc)::value;
+        const bool valid = st * C::kSlots + wave < n_pairs;
+        unsigned char* slot = qdst + wave * C::kSlotBytes + lane * 16;
+#pragma unroll
+        for (int t = 0; t < C::kKSteps; ++t)
+          *reinterpret_cast<u32x4_t*>(slot + t * C::kFragBytes) = deep_regs[kSet][t];
+        if (lane < kBlk) {
+          const int i = deep_qb[kSet] * kBlk + lane;
+          ldst[wave * kBlk + lane] = (valid && i < S) ? deep_lse[kSet] * kLog2e : __builtin_inff();
+        }
+      }
+    };
 
     // ---- compute
     auto mfma_pair = [&](Tile& t, const unsigned char* qsrc, const float* lsrc, int slot)
@@ -338,14 +390,14 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
       for (int ks = 0; ks < C::kKSteps; ++ks) {
         const u32x4_t bq = *reinterpret_cast<const u32x4_t*>(src + ks * C::kFragBytes);
         t.s0 = mfma_32x32x16(kf[0][ks], bq, ks ? t.s0 : f32x16_t{});
-        t.s1 = mfma_32x32x16(kf[1][ks], bq, ks ? t.s1 : f32x16_t{});
+        if constexpr (KB == 2) t.s1 = mfma_32x32x16(kf[KB >= 2 ? 1 : 0][ks], bq, ks ? t.s1 : f32x16_t{});
       }
     };
     auto exp_full = [&](const Tile& t) __attribute__((always_inline)) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         acc0[v] += fast_exp2(__builtin_fmaf(t.s0[v], c, -t.l2));
-        acc1[v] += fast_exp2(__builtin_fmaf(t.s1[v], c, -t.l2));
+        if constexpr (KB == 2) acc1[v] += fast_exp2(__builtin_fmaf(t.s1[v], c, -t.l2));
       }
     };
     auto exp_masked = [&](const Tile& t, int p) __attribute__((always_inline)) {
@@ -356,9 +408,11 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
       for (int v = 0; v < 16; ++v) {
         const int r = 8 * (v >> 2) + (v & 3);
         const float x0 = __builtin_fmaf(t.s0[v], c, -t.l2);
-        const float x1 = __builtin_fmaf(t.s1[v], c, -t.l2);
         acc0[v] += fast_exp2(r <= lim ? x0 : -__builtin_inff());
-        acc1[v] += fast_exp2(r + 32 <= lim ? x1 : -__builtin_inff());
+        if constexpr (KB == 2) {
+          const float x1 = __builtin_fmaf(t.s1[v], c, -t.l2);
+          acc1[v] += fast_exp2(r + 32 <= lim ? x1 : -__builtin_inff());
+        }
       }
     };
     // Exponentials of pair p (in cur) and MFMAs of pair p + 1 (into nxt).
@@ -371,17 +425,17 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
         exp_full(cur);
         // issue order: operand reads ahead, then each MFMA followed by its
         // share of the VALU work (at d = 128: two fma, two add, two exp2),
-        // one more operand read after every second MFMA.  The scheduler
+        // one more operand read after every KB-th MFMA.  The scheduler
         // counts exp2 as transcendental (0x400), not VALU (0x002): without
         // its own group the exps ride along and the last MFMAs of the pair
         // go out with no VALU work beside them.
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, C::kReadsAhead, 0);
 #pragma unroll
         for (int m = 0; m < C::kMfmaPerPair; ++m) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, C::kAluPerPair / C::kMfmaPerPair, 0);
           __builtin_amdgcn_sched_group_barrier(0x400, C::kTransPerPair / C::kMfmaPerPair, 0);
-          if ((m & 1) == 1 && m < 2 * C::kKSteps - 4)
+          if (m % KB == KB - 1 && m < KB * (C::kKSteps + 1 - C::kReadsAhead))
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
       } else {
@@ -390,6 +444,77 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
           exp_full(cur);
         else if (p >= p_vis_lo && p < p_vis_hi)
           exp_masked(cur, p);
+      }
+    };
+
+    // One key block per wave: a step takes two pairs (two staged slots), so
+    // that each step has two independent MFMA chains (one per slot) like the
+    // two key blocks of the other configurations; a single wave per SIMD
+    // issues a lone accumulation chain about 40% slower.  The exponentials of
+    // slot B go to the second set of accumulators.
+    auto mfma_two = [&](Tile& t, const unsigned char* qsrc, const float* lsrc, int slot)
+                        __attribute__((always_inline)) {
+      const unsigned char* src = qsrc + slot * C::kSlotBytes + lane * 16;
+      t.l2 = lsrc[slot * kBlk + l32];
+      t.l2b = lsrc[(slot + 1) * kBlk + l32];
+#pragma unroll
+      for (int ks = 0; ks < C::kKSteps; ++ks) {
+        const u32x4_t ba = *reinterpret_cast<const u32x4_t*>(src + ks * C::kFragBytes);
+        const u32x4_t bb = *reinterpret_cast<const u32x4_t*>(src + C::kSlotBytes + ks * C::kFragBytes);
+        t.s0 = mfma_32x32x16(kf[0][ks], ba, ks ? t.s0 : f32x16_t{});
+        t.s1 = mfma_32x32x16(kf[0][ks], bb, ks ? t.s1 : f32x16_t{});
+      }
+    };
+    auto exp_two_full = [&](const Tile& t) __attribute__((always_inline)) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        acc0[v] += fast_exp2(__builtin_fmaf(t.s0[v], c, -t.l2));
+        acc1[v] += fast_exp2(__builtin_fmaf(t.s1[v], c, -t.l2b));
+      }
+    };
+    // one slot of a two-slot tile: B selects s1 / l2b / acc1
+    auto exp_one = [&](const Tile& t, bool b_slot, int p, bool full) __attribute__((always_inline)) {
+      const int lim = (qb_first + qb_step * (p / G)) * kBlk + l32 - key0 - w - 4 * h32;
+      const float l2 = b_slot ? t.l2b : t.l2;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + (v & 3);
+        const float x = __builtin_fmaf(b_slot ? t.s1[v] : t.s0[v], c, -l2);
+        const float e = fast_exp2(full || r <= lim ? x : -__builtin_inff());
+        if (b_slot)
+          acc1[v] += e;
+        else
+          acc0[v] += e;
+      }
+    };
+    // Exponentials of pairs p, p + 1 (in cur) and MFMAs of pairs p + 2, p + 3
+    // (slots nslot, nslot + 1, into nxt).
+    auto step2 = [&](Tile& cur, Tile& nxt, int p, const unsigned char* nq, const float* nl,
+                     int nslot) __attribute__((always_inline)) {
+      if constexpr (KB == 1) {
+        auto vis = [&](int x) { return x >= p_vis_lo && x < p_vis_hi; };
+        auto ful = [&](int x) { return x >= p_full_lo && x < p_full_hi; };
+        const bool m_a = vis(p + 2), m_b = vis(p + 3);
+        if (m_a && m_b && ful(p) && ful(p + 1)) {
+          mfma_two(nxt, nq, nl, nslot);
+          exp_two_full(cur);
+          // issue order: six reads ahead (both lse2 and the first two
+          // slices of each slot), then each MFMA with its share of the VALU
+          // work and one more read
+          __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+          for (int m = 0; m < 2 * C::kKSteps; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);
+            if (m < 2 * C::kKSteps - 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+        } else {
+          // pairs past the sweep compute on whatever the slot holds, unused
+          if (m_a || m_b) mfma_two(nxt, nq, nl, nslot);
+          if (vis(p)) exp_one(cur, false, p, ful(p));
+          if (vis(p + 1)) exp_one(cur, true, p + 1, ful(p + 1));
+        }
       }
     };
 
@@ -411,8 +536,22 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
       float* cl = kBuf ? l_lds1 : l_lds0;
       float* nl = kBuf ? l_lds0 : l_lds1;
       const bool more = st + 1 < n_stages;
-      if (more) issue_loads(st + 1, 0);
       const int p0 = st * C::kSlots;
+      if constexpr (C::kDeep) {
+        // register set kBuf is free (stored at the end of the previous
+        // stage); set 1 - kBuf holds the next stage's copies.  No condition
+        // on either: past the last stage they read and store nothing used.
+        deep_issue(bufc, st + 2);
+        // two steps of two slots: the first's MFMAs take slots 2 and 3, the
+        // second's slots 0 and 1 of the next stage, after the barrier
+        static_assert(C::kSlots == 4, "one key block per wave: four-wave workgroups");
+        step2(t0, t1, p0, cq, cl, 2);
+        deep_store(std::integral_constant<int, 1 - kBuf>{}, st + 1, nq, nl);
+        __syncthreads();
+        step2(t1, t0, p0 + 2, nq, nl, 0);
+        return;
+      }
+      if (more) issue_loads(st + 1, 0);
 #pragma unroll
       for (int j = 0; j < C::kSlots - 1; ++j) {
         if (j & 1)
@@ -434,13 +573,23 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
       maybe_flush(p0 + C::kSlots - 1);
     };
 
-    issue_loads(0, 0);
-    store_half(0, 0, q_lds0);
-    issue_loads(0, 1);
-    store_half(0, 1, q_lds0);
-    finish_loads(0, l_lds0);
+    if constexpr (C::kDeep) {
+      deep_issue(std::integral_constant<int, 0>{}, 0);
+      deep_issue(std::integral_constant<int, 1>{}, 1);
+      deep_store(std::integral_constant<int, 0>{}, 0, q_lds0, l_lds0);
+    } else {
+      issue_loads(0, 0);
+      store_half(0, 0, q_lds0);
+      issue_loads(0, 1);
+      store_half(0, 1, q_lds0);
+      finish_loads(0, l_lds0);
+    }
     __syncthreads();
-    if (p_vis_lo <= 0 && 0 < p_vis_hi) mfma_pair(t0, q_lds0, l_lds0, 0);
+    if constexpr (C::kDeep) {
+      if (p_vis_lo <= 1 && 0 < p_vis_hi) mfma_two(t0, q_lds0, l_lds0, 0);
+    } else {
+      if (p_vis_lo <= 0 && 0 < p_vis_hi) mfma_pair(t0, q_lds0, l_lds0, 0);
+    }
     for (int st = 0; st < n_stages; st += 2) {
       stage(std::integral_constant<int, 0>{}, st);
       if (st + 1 >= n_stages) break;
@@ -497,15 +646,20 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int kl = mfma_row(v, lane);
-    red[kl * C::kRedStride + l32] = acc0[v];
-    red[(kl + 32) * C::kRedStride + l32] = acc1[v];
+    if constexpr (KB == 2) {
+      red[kl * C::kRedStride + l32] = acc0[v];
+      red[(kl + 32) * C::kRedStride + l32] = acc1[v];
+    } else {
+      red[kl * C::kRedStride + l32] = acc0[v] + acc1[v];  // slots A and B
+    }
   }
   __syncthreads();
-  float tot = 0.f;
-#pragma unroll
-  for (int col = 0; col < 32; ++col) tot += red[lane * C::kRedStride + col];
+  // lane = key within the wave's keys
   const int key = key0 + lane;
-  if (key < S) {
+  if (lane < C::kKeysPerWave && key < S) {
+    float tot = 0.f;
+#pragma unroll
+    for (int col = 0; col < 32; ++col) tot += red[lane * C::kRedStride + col];
     float* dst = a.mass + (size_t)(b * n_heads_out + ho) * S + key;
     if (split > 1)
       atomicAdd(dst, tot);
@@ -520,11 +674,11 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(float* p, int64_t n) {
     p[i] = 0.f;
 }
 
-template <int D, typename T, int W, bool kSeg>
+template <int D, typename T, int W, int KB, bool kSeg>
 hipError_t launch_mass_w(const void* q, const void* k, const float* lse, const Shape& sh,
                          float scale, int window, int per_head, int split, float* mass,
                          const SegOut& seg, hipStream_t stream) {
-  using C = MassCfg<D, W>;
+  using C = MassCfg<D, W, KB>;
   MassArgs a;
   a.q = q;
   a.k = k;
@@ -547,10 +701,11 @@ hipError_t launch_mass_w(const void* q, const void* k, const float* lse, const S
   const int64_t n_tiles = (sh.S + C::kKeysPerWG - 1) / C::kKeysPerWG;
   const int64_t units = (int64_t)sh.B * (per_head ? sh.Hq : sh.Hkv) * split;
   a.n_tiles = (int)n_tiles;
-  // One-workgroup-per-CU grids pair each long key tile with a short one when
-  // the equal-work pairs fill whole rounds of the CUs (at least 95%).
+  // One-workgroup-per-CU grids (and the one-block-per-wave grids) pair each
+  // long key tile with a short one when the equal-work pairs fill whole
+  // rounds of the CUs (at least 95%).
   bool pair = false;
-  if (W == 8 && n_tiles >= 2) {
+  if ((W == 8 || KB == 1) && n_tiles >= 2) {
     const int64_t pairs = units * ((n_tiles + 1) / 2);
     const int64_t rounds = (pairs + kNumCUs - 1) / kNumCUs;
     pair = pairs * 20 >= rounds * kNumCUs * 19;
@@ -561,38 +716,54 @@ hipError_t launch_mass_w(const void* q, const void* k, const float* lse, const S
     const int64_t fill_blocks = min((n + 255) / 256, (int64_t)4 * kNumCUs);
     hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)fill_blocks), dim3(256), 0, stream, mass, n);
   }
-  if constexpr (W == 8) {
+  if constexpr (W == 8 || KB == 1) {
     if (pair) {
-      hipLaunchKernelGGL((mass_kernel<D, T, W, kSeg, true>), dim3((unsigned)blocks),
+      hipLaunchKernelGGL((mass_kernel<D, T, W, KB, kSeg, true>), dim3((unsigned)blocks),
                          dim3(C::kThreads), 0, stream, a);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((mass_kernel<D, T, W, kSeg, false>), dim3((unsigned)blocks),
-                     dim3(C::kThreads), 0, stream, a);
-  return hipGetLastError();
+  if constexpr (KB == 2) {
+    hipLaunchKernelGGL((mass_kernel<D, T, W, KB, kSeg, false>), dim3((unsigned)blocks),
+                       dim3(C::kThreads), 0, stream, a);
+    return hipGetLastError();
+  }
+  return hipErrorInvalidValue;  // one block per wave is chosen for paired grids only
 }
 
-// 512-key workgroups (one per CU) when the grid has at least two per CU;
-// otherwise 256-key workgroups (two per CU), which double the workgroup count
-// of short sequences.  Group sums whose 256-key grid still has fewer than two
+// 512-key workgroups (one per CU) when the grid has at least two per CU.
+// Shorter sequences: 128-key workgroups of four waves with one key block per
+// wave, each taking a long and a short tile, when those pairs fill whole
+// rounds of the CUs (every wave then has the same work); otherwise 256-key
+// workgroups (two per CU).  Group sums whose 256-key grid has fewer than two
 // workgroups per CU also split each group's heads in two halves.
 template <int D, typename T, bool kSeg>
 hipError_t launch_mass_t(const void* q, const void* k, const float* lse, const Shape& sh,
                          float scale, int window, int per_head, float* mass, const SegOut& seg,
                          hipStream_t stream) {
+  using C4 = MassCfg<D, 4, 2>;
+  using C8 = MassCfg<D, 8, 2>;
+  using C1 = MassCfg<D, 4, 1>;
   int64_t units = (int64_t)sh.B * (per_head ? sh.Hq : sh.Hkv);
   int split = 1;
   if (!kSeg && !per_head && sh.G % 2 == 0 &&
-      units * ((sh.S + MassCfg<D, 4>::kKeysPerWG - 1) / MassCfg<D, 4>::kKeysPerWG) < 2 * kNumCUs)
+      units * ((sh.S + C4::kKeysPerWG - 1) / C4::kKeysPerWG) < 2 * kNumCUs)
     split = 2;
   units *= split;
-  const int64_t blocks8 = units * ((sh.S + MassCfg<D, 8>::kKeysPerWG - 1) / MassCfg<D, 8>::kKeysPerWG);
+  const int64_t blocks8 = units * ((sh.S + C8::kKeysPerWG - 1) / C8::kKeysPerWG);
   if (blocks8 >= 2 * kNumCUs)
-    return launch_mass_w<D, T, 8, kSeg>(q, k, lse, sh, scale, window, per_head, split, mass, seg,
-                                        stream);
-  return launch_mass_w<D, T, 4, kSeg>(q, k, lse, sh, scale, window, per_head, split, mass, seg,
-                                      stream);
+    return launch_mass_w<D, T, 8, 2, kSeg>(q, k, lse, sh, scale, window, per_head, split, mass,
+                                           seg, stream);
+  if constexpr (!kSeg) {
+    const int64_t tiles1 = (sh.S + C1::kKeysPerWG - 1) / C1::kKeysPerWG;
+    const int64_t pairs = units * ((tiles1 + 1) / 2);
+    const int64_t rounds = (pairs + kNumCUs - 1) / kNumCUs;
+    if (tiles1 >= 2 && pairs * 20 >= rounds * kNumCUs * 19)
+      return launch_mass_w<D, T, 4, 1, kSeg>(q, k, lse, sh, scale, window, per_head, split, mass,
+                                             seg, stream);
+  }
+  return launch_mass_w<D, T, 4, 2, kSeg>(q, k, lse, sh, scale, window, per_head, split, mass, seg,
+                                         stream);
 }
 
 }  // namespace

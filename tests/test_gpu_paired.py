@@ -162,3 +162,42 @@ def test_paired_random_shapes(family):
     rb = oracle.block_scores(li.q, li.k, w, start, L)
     assert_mass(blk.cpu().numpy(), rb["block"], what + " block")
     assert_mass(fut.cpu().numpy(), rb["future"], what + " future")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,w,D", [
+    # LSE: 63 tiles of 8 x 32 query rows per unit (the middle one alone);
+    # mass: the group heads split in halves, 32 key tiles of 128; S % 32 = 22
+    (2, 16, 4, 3990, 100, 128),
+    (2, 16, 4, 3990, 100, 64),
+    # odd group (no head split), 64 key tiles of 128 per KV head
+    (1, 24, 8, 8100, 257, 128),
+])
+def test_one_block_per_wave_grids(B, Hq, Hkv, S, w, D):
+    """Short sequences whose grids give every wave one 32-row block and every
+    workgroup a long and a short tile (LSE: 8 waves of 32 query rows; mass: 4
+    waves of 32 keys).  Two units against the oracle, every unit through the
+    w = 0 row-sum identity and the per-head sums."""
+    wl = kvp_inputs.workload(2).with_(B=B, Hq=Hq, Hkv=Hkv, S=S, D=D, window=w,
+                                      seed=5151 + S + D + Hq)
+    say(f"[one block per wave] B={B} Hq={Hq} Hkv={Hkv} S={S} w={w} D={D}")
+    li = kvp_inputs.make_layer(wl)
+    q, k = to_dev(li.q), to_dev(li.k)
+    lse = kvp.lse_fwd(q, k)
+    mass = kvp.future_mass(q, k, lse, w)
+    per_head = kvp.future_mass_per_head(q, k, lse, w)
+    total0 = kvp.future_mass(q, k, lse, 0).double().sum(dim=2)
+    torch.cuda.synchronize()
+    lse_h, mass_h, ph_h = lse.cpu().numpy(), mass.cpu().numpy(), per_head.cpu().numpy()
+    G = Hq // Hkv
+    assert np.all(mass_h[:, :, S - w:] == 0)
+    np.testing.assert_allclose(total0.cpu().numpy(), G * S, rtol=1e-4)
+    np.testing.assert_allclose(ph_h.reshape(B, Hkv, G, S).astype(np.float64).sum(axis=2),
+                               mass_h, rtol=1e-5, atol=1e-6)
+    for b, h in ((0, 0), (B - 1, Hkv - 1)):
+        say(f"[one block per wave] S={S} D={D}: oracle unit b={b} h={h}")
+        ref = oracle.future_mass(li.q, li.k, w, b_only=b, h_only=h, want_per_head=True)
+        g0 = h * G
+        assert_lse(lse_h[b, g0:g0 + G], ref["lse"][b, g0:g0 + G], f"S={S} lse b={b} h={h}")
+        assert_mass(mass_h[b, h], ref["mass"][b, h], f"S={S} mass b={b} h={h}")
+        assert_mass(ph_h[b, g0:g0 + G], ref["mass_heads"][b, g0:g0 + G],
+                    f"S={S} per-head b={b} h={h}")
