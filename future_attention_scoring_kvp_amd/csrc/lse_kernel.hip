@@ -9,7 +9,8 @@
 //     too small to give every CU two); each wave owns 96 consecutive query
 //     positions of one query head (three 32-column MFMA blocks kept as bf16 B
 //     operands in registers; two blocks, 64 positions, in the sparse pass and
-//     for fp32 input); the waves cover (position block, head) pairs
+//     for grids too small for three; one block, 32 positions, in paired
+//     8-wave grids of short sequences); the waves cover (position block, head) pairs
 //     of one GQA group, heads fastest, so the group's shared keys are staged
 //     once for all of them;
 //   * keys are streamed in blocks of 32 from position 0 upwards, one block

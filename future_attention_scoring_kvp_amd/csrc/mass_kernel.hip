@@ -13,9 +13,12 @@
 //     one workgroup per CU (two waves of the same workgroup per SIMD, so the
 //     co-resident waves advance together and a tile's time follows its work;
 //     two workgroups on one CU issue at very different rates, oldest first);
-//     grids too small for two workgroups per CU use 4 waves = 256 keys;
-//     each wave keeps its 64 keys (two 32-row MFMA blocks, all of d) as bf16
-//     A operands in registers for the whole sweep;
+//     grids too small for two workgroups per CU use 4 waves = 256 keys, or,
+//     where paired tiles fill whole rounds, 4 waves of one 32-row block
+//     each = 128 keys (each step then takes two staged pairs, and the copies
+//     go two stages ahead: one wave per SIMD has nothing to cover a wait);
+//     each wave keeps its 64 (32) keys (32-row MFMA blocks, all of d) as
+//     bf16 A operands in registers for the whole sweep;
 //   * the workgroup sweeps the future (query block, head) pairs of its group
 //     -- query blocks of 32 from the end of the sequence backwards, the G
 //     heads of a block consecutively -- one pair per wave per LDS stage,
