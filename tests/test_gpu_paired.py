@@ -169,6 +169,8 @@ def test_paired_random_shapes(family):
     # mass: the group heads split in halves, 32 key tiles of 128; S % 32 = 22
     (2, 16, 4, 3990, 100, 128),
     (2, 16, 4, 3990, 100, 64),
+    # odd tile counts: 31 key tiles of 128 (tile 15 alone), 61 LSE tiles
+    (2, 16, 4, 3900, 64, 128),
     # odd group (no head split), 64 key tiles of 128 per KV head
     (1, 24, 8, 8100, 257, 128),
 ])
