@@ -18,9 +18,11 @@ from parity import LSE_ATOL, assert_lse, assert_mass, say, to_dev
 pytestmark = pytest.mark.gpu
 
 # (B, Hkv, G, S range): one query head; small ragged groups; a 4-wave grid;
-# one-workgroup-per-CU grids with paired tiles (the last three)
+# one-workgroup-per-CU grids with paired tiles (the next three); short grids
+# of one 32-row block per wave with paired tiles in both passes (the last)
 FAMILIES = [(1, 1, 1, 1, 700), (2, 2, 3, 33, 1500), (1, 8, 4, 1000, 3000), (3, 8, 1, 1, 600),
-            (2, 32, 2, 3585, 4096), (1, 64, 1, 3585, 4096), (1, 16, 8, 1537, 2048)]
+            (2, 32, 2, 3585, 4096), (1, 64, 1, 3585, 4096), (1, 16, 8, 1537, 2048),
+            (2, 4, 4, 3841, 4096)]
 
 
 @pytest.mark.parametrize("family", range(len(FAMILIES)))
