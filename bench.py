@@ -474,6 +474,9 @@ def main() -> int:
     keep_all = torch.empty((L * B, Hkv, n_keep), dtype=torch.int32, device=dev)
     sel_ws_bytes = kvp.select_workspace_bytes(L * B * Hkv, S, k)
     sel_ws = torch.empty(sel_ws_bytes, dtype=torch.uint8, device=dev) if sel_ws_bytes else None
+    # short sequences: the chunked mass launch, with its workspace allocated here
+    mass_ws_bytes = kvp.future_mass_workspace_bytes(q_all[0], k_all[0], w)
+    mass_ws = torch.empty(mass_ws_bytes, dtype=torch.uint8, device=dev) if mass_ws_bytes else None
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -485,7 +488,11 @@ def main() -> int:
             kvp.lse_fwd(q_all[l], k_all[l], out=lse_all[l])
             if events is not None:
                 events[l][1].record(stream)
-            kvp.future_mass(q_all[l], k_all[l], lse_all[l], w, out=mass_all[l])
+            if mass_ws is not None:
+                kvp.future_mass_chunked(q_all[l], k_all[l], lse_all[l], w, workspace=mass_ws,
+                                        out=mass_all[l])
+            else:
+                kvp.future_mass(q_all[l], k_all[l], lse_all[l], w, out=mass_all[l])
             if events is not None:
                 events[l][2].record(stream)
         kvp.select_topk(mass_all.view(L * B, Hkv, S), w, s, k, out=keep_all, workspace=sel_ws)
@@ -551,6 +558,7 @@ def main() -> int:
         "stages_ms": {"lse_per_layer": round(lse_launch_ms, 4),
                       "mass_per_layer": round(mass_launch_ms, 4),
                       "select_all_layers": round(sel_launch_ms, 4)},
+        "mass_entry_point": "kvp_future_mass_chunked" if mass_ws is not None else "kvp_future_mass",
         "mass_pass_gpairs_per_s": round(pairs_layer / (mass_launch_ms * 1e-3) / 1e9, 3),
         "lse_pass_gpairs_per_s": round(lse_pairs / (lse_launch_ms * 1e-3) / 1e9, 3),
         "select_gbs": round(sel_bytes / (sel_launch_ms * 1e-3) / 1e9, 2),

@@ -39,7 +39,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["lse_fwd", "lse_sparse", "future_mass", "future_mass_per_head", "target_scores",
+__all__ = ["lse_fwd", "lse_sparse", "future_mass", "future_mass_per_head", "future_mass_chunked",
+           "future_mass_workspace_bytes", "target_scores",
            "static_priority", "select_topk", "select_topk_noalloc", "select_workspace_bytes", "keep_count",
            "running_cutoff", "block_count", "block_future_scores", "soft_topk",
            "soft_topk_backward", "KvpError", "library_path", "load_library", "AGG_LOG_MEAN",
@@ -84,6 +85,11 @@ def load_library():
             lib.kvp_future_mass.restype = ctypes.c_int
             lib.kvp_future_mass.argtypes = [vp, vp, vp, ctypes.c_int, _Dims, f32, i32, vp, vp]
             lib.kvp_future_mass_per_head.restype = ctypes.c_int
+            lib.kvp_future_mass_workspace_bytes.restype = ctypes.c_size_t
+            lib.kvp_future_mass_workspace_bytes.argtypes = [_Dims, ctypes.c_int, i32, i32]
+            lib.kvp_future_mass_chunked.restype = ctypes.c_int
+            lib.kvp_future_mass_chunked.argtypes = [vp, vp, vp, ctypes.c_int, _Dims, f32, i32, i32,
+                                                    vp, vp, ctypes.c_size_t, vp]
             lib.kvp_future_mass_per_head.argtypes = [vp, vp, vp, ctypes.c_int, _Dims, f32, i32,
                                                      vp, vp]
             lib.kvp_target_scores.restype = ctypes.c_int
@@ -222,6 +228,47 @@ def future_mass(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, window: int
     _check(lib.kvp_future_mass(q.data_ptr(), k.data_ptr(), lse.data_ptr(), _dtype_code(q), d,
                                float(scale), int(window), out.data_ptr(), _stream_ptr(stream)),
            "kvp_future_mass")
+    return out
+
+
+def future_mass_workspace_bytes(q: torch.Tensor, k: torch.Tensor, window: int,
+                                per_head: bool = False) -> int:
+    """Bytes of workspace ``future_mass_chunked`` needs for these inputs (0: none)."""
+    lib = load_library()
+    return int(lib.kvp_future_mass_workspace_bytes(_dims(q, k), _dtype_code(q), int(window),
+                                                   int(bool(per_head))))
+
+
+def future_mass_chunked(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, window: int,
+                        per_head: bool = False, scale: float = 0.0,
+                        workspace: Optional[torch.Tensor] = None,
+                        out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The masses of ``future_mass`` (or ``future_mass_per_head``), short sequences
+    spread over more workgroups through a workspace (allocated here when not given:
+    a uint8 device tensor of ``future_mass_workspace_bytes`` bytes)."""
+    lib = load_library()
+    _require_device(q, k, lse)
+    d = _dims(q, k)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (d.batch, d.n_q_heads, d.seq_len):
+        raise KvpError("lse must be fp32 [B, Hq, S]")
+    heads = d.n_q_heads if per_head else d.n_kv_heads
+    if out is None:
+        out = torch.empty((d.batch, heads, d.seq_len), dtype=torch.float32, device=q.device)
+    _require_device(out)
+    if out.dtype != torch.float32 or tuple(out.shape) != (d.batch, heads, d.seq_len):
+        raise KvpError("mass out must be fp32 [B, Hkv or Hq, S]")
+    need = int(lib.kvp_future_mass_workspace_bytes(d, _dtype_code(q), int(window),
+                                                   int(bool(per_head))))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        _require_device(workspace)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(lib.kvp_future_mass_chunked(q.data_ptr(), k.data_ptr(), lse.data_ptr(), _dtype_code(q),
+                                       d, float(scale), int(window), int(bool(per_head)),
+                                       out.data_ptr(), ws_ptr or None, ws_bytes,
+                                       _stream_ptr(stream)), "kvp_future_mass_chunked")
     return out
 
 

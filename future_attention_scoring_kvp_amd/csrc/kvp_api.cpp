@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 7;
+constexpr int32_t kAbiVersion = 8;
 // Limits that keep every index the kernels form in 32-bit ints, and the bytes
 // of one head (S * d * 4 at most) within a 32-bit buffer range.
 constexpr int64_t kMaxSeq = int64_t(1) << 22;
@@ -136,6 +136,39 @@ kvp_status_t kvp_future_mass_per_head(const void* q, const void* k, const float*
   const int w = window > sh.S ? sh.S : window;
   return from_hip(kvp::launch_mass(q, k, lse, dtype == KVP_BF16 ? 0 : 1, sh,
                                    resolve_scale(scale, sh.D), w, 1, mass, stream));
+}
+
+size_t kvp_future_mass_workspace_bytes(kvp_dims_t dims, kvp_dtype_t dtype, int32_t window,
+                                       int32_t per_head) {
+  kvp::Shape sh;
+  if (check_dims(dims, true, sh) != KVP_OK || !valid_dtype(dtype) || window < 0) return 0;
+  if (per_head != 0 && per_head != 1) return 0;
+  if (sh.B == 0 || sh.S == 0) return 0;
+  const int w = window > sh.S ? sh.S : window;
+  return kvp::mass_workspace_bytes(dtype == KVP_BF16 ? 0 : 1, sh, w, per_head);
+}
+
+kvp_status_t kvp_future_mass_chunked(const void* q, const void* k, const float* lse,
+                                     kvp_dtype_t dtype, kvp_dims_t dims, float scale,
+                                     int32_t window, int32_t per_head, float* mass, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  kvp::Shape sh;
+  const kvp_status_t st = check_dims(dims, true, sh);
+  if (st != KVP_OK) return st;
+  if (!valid_dtype(dtype)) return KVP_EUNSUPPORTED;
+  if (std::isnan(scale) || std::isinf(scale) || window < 0) return KVP_EINVAL;
+  if (per_head != 0 && per_head != 1) return KVP_EINVAL;
+  if (sh.B == 0 || sh.S == 0) return KVP_OK;
+  if (!q || !k || !lse || !mass || !aligned(q, 16) || !aligned(k, 16) || !aligned(lse, 4) ||
+      !aligned(mass, 4))
+    return KVP_EINVAL;
+  const int w = window > sh.S ? sh.S : window;
+  const int dt = dtype == KVP_BF16 ? 0 : 1;
+  const size_t need = kvp::mass_workspace_bytes(dt, sh, w, per_head);
+  if (workspace_bytes < need) return KVP_EWORKSPACE;
+  if (need > 0 && (!workspace || !aligned(workspace, 256))) return KVP_EINVAL;
+  return from_hip(kvp::launch_mass_ws(q, k, lse, dt, sh, resolve_scale(scale, sh.D), w, per_head,
+                                      mass, need > 0 ? workspace : nullptr, stream));
 }
 
 kvp_status_t kvp_target_scores(const float* mass, int32_t per_head, kvp_dims_t dims, int32_t window,

@@ -23,6 +23,14 @@ hipError_t launch_lse_sparse(const void* q, const void* k, int dtype, const Shap
 // per_head = 0: mass [B, Hkv, S] summed over each group; 1: mass [B, Hq, S].
 hipError_t launch_mass(const void* q, const void* k, const float* lse, int dtype, const Shape& sh,
                        float scale, int window, int per_head, float* mass, hipStream_t stream);
+// The same pass with a workspace: short sequences cut each key tile's query
+// sweep into chunks whose partial masses go to the workspace and are added in
+// chunk order by a second kernel.  mass_workspace_bytes is 0 where no launch
+// is cut; launch_mass_ws then (or with a null workspace) runs launch_mass.
+size_t mass_workspace_bytes(int dtype, const Shape& sh, int window, int per_head);
+hipError_t launch_mass_ws(const void* q, const void* k, const float* lse, int dtype,
+                          const Shape& sh, float scale, int window, int per_head, float* mass,
+                          void* workspace, hipStream_t stream);
 // Query-block mode of the mass pass (Golden-Eviction scores): blocks
 // [start + t len, start + (t+1) len) clipped to S, start and len multiples of
 // 32, n blocks; block (may be null) and future are [B, U, n, S] with U = Hkv

@@ -106,7 +106,23 @@ struct MassArgs {
   int seg_start, seg_len, n_seg;
   float* seg_block;
   float* seg_future;
+  // query-chunk mode (chunk_pairs > 0, one tile per block, no head split):
+  // the sweep of key tile t, n_t = (query blocks it sees) * G pairs, is cut
+  // into ceil(n_t / chunk_pairs) chunks of chunk_pairs pairs (a multiple of
+  // G: whole query blocks), from the last query block down; block x of the
+  // grid takes chunk x / n_units of unit x % n_units (chunks of a unit
+  // numbered tile by tile) and writes its tile's partial masses to
+  // partial[(unit * chunks_per_unit + chunk) * kKeysPerWG + key - tile start]
+  int chunk_pairs, chunks_per_unit;
+  float* partial;
 };
+
+// Query blocks seen by key tile `tile` of kpt keys: [qb_lo, qb_hi], or none
+// (returns 0).  Pairs = blocks * heads.
+__host__ __device__ __forceinline__ int tile_query_blocks(int tile, int kpt, int S, int window) {
+  const int q_first = tile * kpt + window;
+  return q_first < S ? (S - 1) / kBlk - q_first / kBlk + 1 : 0;
+}
 
 struct Tile {
   f32x16_t s0, s1;  // logits of key blocks 0 / 1 (rows) x 32 queries (columns);
@@ -151,12 +167,35 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
   const int split = a.head_split;
   const int G = a.per_head ? 1 : a.G / split;  // query heads swept per unit
   int unit, tile;
+  // query-chunk mode: this block's chunk, its first query block from the
+  // top of the tile's sweep and its number of query blocks
+  int chunk_id = 0, chunk_qb_skip = 0, chunk_qbs = 0;
   // paired grids carry equal work per block: whole units per round of an
   // XCD; otherwise longest tiles first
-  if constexpr (kPair)
+  if constexpr (kPair) {
     xcd_map_units(blockIdx.x, a.B * n_heads_out * split, (a.n_tiles + 1) / 2, unit, tile);
-  else
+  } else if (!kSeg && KB == 2 && a.chunk_pairs > 0) {
+    const int n_units = a.B * n_heads_out;
+    unit = (int)blockIdx.x % n_units;
+    int local = (int)blockIdx.x / n_units;
+    chunk_id = unit * a.chunks_per_unit + local;
+    const int qb_per_chunk = a.chunk_pairs / G;
+    tile = 0;
+    for (int t = 0; t < a.n_tiles; ++t) {
+      const int qbs = tile_query_blocks(t, C::kKeysPerWG, S, w);
+      const int nc = (qbs + qb_per_chunk - 1) / qb_per_chunk;
+      if (local < nc) {
+        tile = t;
+        chunk_qb_skip = local * qb_per_chunk;
+        chunk_qbs = min(qb_per_chunk, qbs - chunk_qb_skip);
+        break;
+      }
+      local -= nc;
+    }
+  } else {
     xcd_map(blockIdx.x, a.B * n_heads_out * split, unit, tile);
+  }
+  const bool chunked = !kSeg && !kPair && KB == 2 && a.chunk_pairs > 0;
   const int part = unit % split;
   unit /= split;
   const int b = unit / n_heads_out;
@@ -267,9 +306,11 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
     seg_low = min(seg_low, t);
   };
 
-  if (q_first < S) {
-    const int qb_hi = (S - 1) / kBlk;
-    const int qb_lo = q_first / kBlk;
+  if (q_first < S && (!chunked || chunk_qbs > 0)) {
+    // a chunk sweeps query blocks [qb_hi - skip - qbs + 1, qb_hi - skip]
+    const int qb_last = (S - 1) / kBlk;
+    const int qb_hi = chunked ? qb_last - chunk_qb_skip : qb_last;
+    const int qb_lo = chunked ? qb_hi - chunk_qbs + 1 : q_first / kBlk;
     const int n_pairs = (qb_hi - qb_lo + 1) * G;
     // Pair p is (query block qb_first + qb_step * (p / G), head p % G).
     const int qb_step = asc ? 1 : -1;
@@ -290,7 +331,7 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
     // those in [p_full_lo, p_full_hi) see every key with every query (no
     // mask), the others need the mask.  A partial last block (rows >= S) is
     // masked too.
-    const int p_part = (S % kBlk) ? G : 0;
+    const int p_part = (S % kBlk) && qb_hi == qb_last ? G : 0;
     const int qb_full = (key0 + C::kKeysPerWave - 1 + w + kBlk - 1) / kBlk;
     const int qb_min = (key0 + w) / kBlk;  // first block with a query i >= key0 + w
     const int p_vis_lo = asc ? min(n_pairs, (qb_min - qb_lo) * G) : 0;
@@ -663,13 +704,39 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
     float tot = 0.f;
 #pragma unroll
     for (int col = 0; col < 32; ++col) tot += red[lane * C::kRedStride + col];
-    float* dst = a.mass + (size_t)(b * n_heads_out + ho) * S + key;
-    if (split > 1)
-      atomicAdd(dst, tot);
-    else
-      *dst = tot;
+    if (chunked) {
+      if (chunk_qbs > 0) a.partial[(size_t)chunk_id * C::kKeysPerWG + (key - tile_key0)] = tot;
+    } else {
+      float* dst = a.mass + (size_t)(b * n_heads_out + ho) * S + key;
+      if (split > 1)
+        atomicAdd(dst, tot);
+      else
+        *dst = tot;
+    }
   }
   }  // tiles of the workgroup
+}
+
+// Query-chunk mode: the mass of every key is the sum of its tile's chunk
+// partials, added in chunk order (bitwise reproducible).  Keys of tiles with
+// no chunk (no future query) get 0.
+template <int kKeysPerTile>
+__global__ __launch_bounds__(256) void mass_chunk_sum_kernel(MassArgs a, int n_units) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)n_units * a.S) return;
+  const int unit = (int)(i / a.S);
+  const int key = (int)(i - (int64_t)unit * a.S);
+  const int t = key / kKeysPerTile;
+  const int qpc = a.chunk_pairs / (a.per_head ? 1 : a.G);  // query blocks per chunk
+  int off = 0;
+  for (int u = 0; u < t; ++u)
+    off += (tile_query_blocks(u, kKeysPerTile, a.S, a.window) + qpc - 1) / qpc;
+  const int nc = (tile_query_blocks(t, kKeysPerTile, a.S, a.window) + qpc - 1) / qpc;
+  const float* p = a.partial + ((size_t)unit * a.chunks_per_unit + off) * kKeysPerTile +
+                   (key - t * kKeysPerTile);
+  float sum = 0.f;
+  for (int c = 0; c < nc; ++c) sum += p[(size_t)c * kKeysPerTile];
+  a.mass[i] = sum;
 }
 
 __global__ __launch_bounds__(256) void zero_fill_kernel(float* p, int64_t n) {
@@ -701,6 +768,9 @@ hipError_t launch_mass_w(const void* q, const void* k, const float* lse, const S
   a.n_seg = seg.n;
   a.seg_block = seg.block;
   a.seg_future = seg.future;
+  a.chunk_pairs = 0;
+  a.chunks_per_unit = 0;
+  a.partial = nullptr;
   const int64_t n_tiles = (sh.S + C::kKeysPerWG - 1) / C::kKeysPerWG;
   const int64_t units = (int64_t)sh.B * (per_head ? sh.Hq : sh.Hkv) * split;
   a.n_tiles = (int)n_tiles;
@@ -769,7 +839,125 @@ hipError_t launch_mass_t(const void* q, const void* k, const float* lse, const S
                                          stream);
 }
 
+// Query-chunk plan of a short-sequence launch of group sums: key tiles whose
+// sweeps are cut into chunks of equal query blocks.  For one to four rounds
+// of the CUs (kChunkPerRound workgroups each) the smallest chunk that fits is
+// found; the plan taken has the least rounds x (chunk + a per-workgroup
+// overhead of two query blocks).  chunk_qbs = 0: no chunking (large grids,
+// fp32 input, or nothing to sweep).
+struct ChunkPlan {
+  int chunk_qbs, chunks_per_unit;
+  int64_t units, n_tiles;
+};
+// waves per chunk workgroup (two key blocks each): 4 -> 256-key tiles, two
+// workgroups per CU (measured a little faster at 4K tokens than 8 waves and
+// 512-key tiles, one per CU)
+constexpr int kChunkWaves = 4;
+constexpr int kChunkTile = kChunkWaves * 64;
+constexpr int kChunkPerRound = kNumCUs * (8 / kChunkWaves);
+
+ChunkPlan mass_chunk_plan(int dtype, const Shape& sh, int window, int per_head) {
+  ChunkPlan pl{0, 0, 0, 0};
+  // per-head masses already spread over G times the units (the paired
+  // one-block grid, two workgroups per CU): no chunking
+  if (dtype != 0 || sh.S <= 0 || per_head) return pl;
+  pl.units = (int64_t)sh.B * (per_head ? sh.Hq : sh.Hkv);
+  pl.n_tiles = (sh.S + kChunkTile - 1) / kChunkTile;
+  // grids of at least two 512-key tiles per CU run the paired 8-wave launch
+  if (pl.units * ((sh.S + 511) / 512) >= 2 * kNumCUs) return pl;
+  int64_t qmax = 0;
+  for (int64_t t = 0; t < pl.n_tiles; ++t)
+    qmax = max(qmax, (int64_t)tile_query_blocks((int)t, kChunkTile, sh.S, window));
+  if (qmax == 0) return pl;
+  auto chunks = [&](int64_t qpc) {
+    int64_t n = 0;
+    for (int64_t t = 0; t < pl.n_tiles; ++t)
+      n += (tile_query_blocks((int)t, kChunkTile, sh.S, window) + qpc - 1) / qpc;
+    return n;
+  };
+  int64_t best_q = qmax, best_cost = -1;
+  for (int64_t rounds = 1; rounds <= 4; ++rounds) {
+    // smallest chunk (in query blocks) whose grid fits `rounds` rounds;
+    // the chunk count does not grow with the chunk size
+    int64_t lo = 1, hi = qmax;
+    if (pl.units * chunks(hi) > rounds * kChunkPerRound) continue;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) / 2;
+      if (pl.units * chunks(mid) <= rounds * kChunkPerRound)
+        hi = mid;
+      else
+        lo = mid + 1;
+    }
+    const int64_t cost = rounds * (lo + 2);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best_q = lo;
+    }
+  }
+  pl.chunk_qbs = (int)best_q;
+  pl.chunks_per_unit = (int)chunks(best_q);
+  return pl;
+}
+
+template <int D, typename T>
+hipError_t launch_mass_chunked_t(const void* q, const void* k, const float* lse, const Shape& sh,
+                                 float scale, int window, int per_head, float* mass,
+                                 const ChunkPlan& pl, void* workspace, hipStream_t stream) {
+  using C = MassCfg<D, kChunkWaves, 2>;
+  static_assert(C::kKeysPerWG == kChunkTile, "chunk tiles: two key blocks per wave");
+  MassArgs a;
+  a.q = q;
+  a.k = k;
+  a.lse = lse;
+  a.mass = mass;
+  a.B = sh.B;
+  a.Hq = sh.Hq;
+  a.Hkv = sh.Hkv;
+  a.S = sh.S;
+  a.G = sh.G;
+  a.window = window;
+  a.per_head = per_head;
+  a.head_split = 1;
+  a.n_tiles = (int)pl.n_tiles;
+  a.c = scale * kLog2e;
+  a.seg_start = 0;
+  a.seg_len = 32;
+  a.n_seg = 0;
+  a.seg_block = nullptr;
+  a.seg_future = nullptr;
+  a.chunk_pairs = pl.chunk_qbs * (per_head ? 1 : sh.G);
+  a.chunks_per_unit = pl.chunks_per_unit;
+  a.partial = static_cast<float*>(workspace);
+  const int64_t blocks = pl.units * pl.chunks_per_unit;
+  hipLaunchKernelGGL((mass_kernel<D, T, kChunkWaves, 2, false, false>), dim3((unsigned)blocks),
+                     dim3(C::kThreads), 0, stream, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t n = pl.units * sh.S;
+  hipLaunchKernelGGL((mass_chunk_sum_kernel<kChunkTile>), dim3((unsigned)((n + 255) / 256)),
+                     dim3(256), 0, stream, a, (int)pl.units);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+size_t mass_workspace_bytes(int dtype, const Shape& sh, int window, int per_head) {
+  const ChunkPlan pl = mass_chunk_plan(dtype, sh, window, per_head);
+  if (pl.chunk_qbs == 0) return 0;
+  return (size_t)pl.units * pl.chunks_per_unit * kChunkTile * sizeof(float);
+}
+
+hipError_t launch_mass_ws(const void* q, const void* k, const float* lse, int dtype,
+                          const Shape& sh, float scale, int window, int per_head, float* mass,
+                          void* workspace, hipStream_t stream) {
+  const ChunkPlan pl = mass_chunk_plan(dtype, sh, window, per_head);
+  if (pl.chunk_qbs == 0 || workspace == nullptr)
+    return launch_mass(q, k, lse, dtype, sh, scale, window, per_head, mass, stream);
+  return sh.D == 128 ? launch_mass_chunked_t<128, uint16_t>(q, k, lse, sh, scale, window, per_head,
+                                                            mass, pl, workspace, stream)
+                     : launch_mass_chunked_t<64, uint16_t>(q, k, lse, sh, scale, window, per_head,
+                                                           mass, pl, workspace, stream);
+}
 
 hipError_t launch_mass(const void* q, const void* k, const float* lse, int dtype, const Shape& sh,
                        float scale, int window, int per_head, float* mass, hipStream_t stream) {

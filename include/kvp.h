@@ -11,6 +11,10 @@
  *   kvp_select_topk  per-KV-head keep-set: sinks, recent window and the top-k
  *                    older tokens by mass.
  *
+ * kvp_future_mass_chunked computes the same masses with a caller workspace,
+ * which lets short sequences spread each key tile's queries over several
+ * workgroups.
+ *
  * Two more turn the masses into KVpop's training target:
  *
  *   kvp_future_mass_per_head  the future mass of every key for each query head
@@ -162,6 +166,32 @@ kvp_status_t kvp_future_mass(const void* q, const void* k, const float* lse, kvp
 kvp_status_t kvp_future_mass_per_head(const void* q, const void* k, const float* lse,
                                       kvp_dtype_t dtype, kvp_dims_t dims, float scale,
                                       int32_t window, float* mass, hipStream_t stream);
+
+/* Stage 2 with a caller workspace, for short sequences.
+ * The same masses as kvp_future_mass (per_head = 0, mass [B, Hkv, S]) or
+ * kvp_future_mass_per_head (per_head = 1, mass [B, Hq, S]), same definition
+ * ([KVpop] §3.1 Eq. 2 / App. B.1, recovered from the LSE as in §3.2 Eq. 8).
+ * Where the one-tile-per-workgroup launch would leave compute units idle,
+ * each key tile's sweep over its future queries is cut into chunks of equal
+ * length, one workgroup each; the chunks' partial masses go to the workspace
+ * and a second kernel adds them per key in chunk order.  The result is
+ * bitwise reproducible; it can differ from kvp_future_mass's in the last bits
+ * (another order of the same sum).
+ *   workspace : device memory of at least kvp_future_mass_workspace_bytes(
+ *               dims, dtype, window, per_head) bytes, 256-byte aligned, owned
+ *               by the caller, clobbered; may be null when that size is 0
+ *               (long sequences, fp32 input and per-head masses, whose grid
+ *               already has G times the units: the call then runs the
+ *               kvp_future_mass / kvp_future_mass_per_head launch).
+ * Errors as kvp_future_mass; per_head not 0 or 1 -> KVP_EINVAL;
+ * workspace_bytes below the size -> KVP_EWORKSPACE; a null or misaligned
+ * workspace where the size is not 0 -> KVP_EINVAL. */
+size_t kvp_future_mass_workspace_bytes(kvp_dims_t dims, kvp_dtype_t dtype, int32_t window,
+                                       int32_t per_head);
+kvp_status_t kvp_future_mass_chunked(const void* q, const void* k, const float* lse,
+                                     kvp_dtype_t dtype, kvp_dims_t dims, float scale,
+                                     int32_t window, int32_t per_head, float* mass, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
 
 /* Aggregation of the per-head log masses over the query heads of a group
  * ([KVpop] §3.1 Eq. 3 leaves Agg open; App. B.1 uses the log of the mean). */

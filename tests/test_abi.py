@@ -37,7 +37,8 @@ def test_header_declares_the_three_stages():
               "kvp_target_scores", "kvp_running_cutoff", "kvp_running_cutoff_workspace_bytes",
               "kvp_block_count", "kvp_block_future_scores", "kvp_soft_topk_fwd",
               "kvp_soft_topk_bwd", "kvp_lse_sparse", "kvp_select_workspace_bytes",
-              "kvp_static_priority"):
+              "kvp_static_priority", "kvp_future_mass_chunked",
+              "kvp_future_mass_workspace_bytes"):
         assert n in names
 
 
@@ -47,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.kvp_abi_version() == 7
+    assert lib.kvp_abi_version() == 8
     for code in range(5):
         assert lib.kvp_status_string(code)
     assert lib.kvp_status_string(99) == b"unknown status"
@@ -120,6 +121,37 @@ def test_select_validation(lib):
     assert sel(FAKE, long_d, 1024, 4, 2048, FAKE, None, need - 1) == WORKSPACE
     assert sel(FAKE, long_d, 1024, 4, 2048, FAKE, None, need) == INVALID      # null workspace
     assert sel(FAKE, long_d, 1024, 4, 2048, FAKE, FAKE + 16, need) == INVALID  # not 256-aligned
+
+
+def test_mass_chunked_workspace_and_validation(lib):
+    ws = lib.kvp_future_mass_workspace_bytes
+    short = dims(B=1, Hq=32, Hkv=8, S=4096)
+    need = ws(short, 0, 128, 0)
+    # 8 KV heads x chunks of one 256-key tile's sweep, 256 fp32 partials each,
+    # at most two workgroups per compute unit per round, at most four rounds
+    assert need > 0 and need % (256 * 4 * 8) == 0 and need <= 4 * 512 * 256 * 4
+    assert ws(short, 0, 128, 1) == 0                                 # per head: not chunked
+    assert ws(short, 1, 128, 0) == 0                                 # fp32 input: no chunks
+    assert ws(dims(B=1, Hq=32, Hkv=8, S=32768), 0, 512, 0) == 0      # grid already full
+    assert ws(short, 0, 4096, 0) == 0                                # no future query
+    assert ws(short, 0, 128, 2) == 0 and ws(short, 0, -1, 0) == 0    # invalid arguments
+    assert ws(dims(Hq=3, Hkv=2), 0, 4, 0) == 0
+
+    def call(q=FAKE, k=FAKE, lse=FAKE, dtype=0, d=short, w=128, per_head=0, mass=FAKE,
+             wsp=None, wsb=0):
+        return lib.kvp_future_mass_chunked(q, k, lse, dtype, d, 0.0, w, per_head, mass, wsp, wsb,
+                                           None)
+    assert call(q=None, wsp=FAKE, wsb=need) == INVALID
+    assert call(mass=FAKE + 2, wsp=FAKE, wsb=need) == INVALID
+    assert call(per_head=2, wsp=FAKE, wsb=need) == INVALID
+    assert call(w=-1, wsp=FAKE, wsb=need) == INVALID
+    assert call(dtype=7, wsp=FAKE, wsb=need) == UNSUPPORTED
+    assert call(d=dims(D=96)) == UNSUPPORTED
+    assert call() == WORKSPACE                                       # no workspace given
+    assert call(wsp=FAKE, wsb=need - 1) == WORKSPACE
+    assert call(wsp=None, wsb=need) == INVALID                       # null workspace
+    assert call(wsp=FAKE + 16, wsb=need) == INVALID                  # not 256-aligned
+    assert call(d=dims(B=0, Hq=32, Hkv=8, S=4096)) == OK             # empty
 
 
 def test_select_noalloc_validation(lib):
