@@ -100,9 +100,10 @@ def test_reproducible_and_workspace_independent():
     assert_mass(a.cpu().numpy(), plain.cpu().numpy().astype(np.float64), "chunked vs unchunked")
 
 
-def test_long_sequences_and_per_head_take_the_plain_launch():
-    """Where the grid is already full, and for per-head masses, the size is 0
-    and the call (with no workspace) gives the unchunked pass's bits."""
+def test_long_sequences_per_head_and_fp32_take_the_plain_launch():
+    """Where the grid is already full, for per-head masses and for fp32 input
+    the size is 0 and the call (with no workspace) gives the unchunked pass's
+    bits."""
     wl = kvp_inputs.workload(4).with_(B=2, S=16384, window=256, seed=77)   # 2 x 8 x 32 tiles
     li = kvp_inputs.make_layer(wl)
     q, k = to_dev(li.q), to_dev(li.k)
@@ -121,3 +122,13 @@ def test_long_sequences_and_per_head_take_the_plain_launch():
     d = kvp.future_mass_per_head(q2, k2, lse2, wl2.window)
     torch.cuda.synchronize()
     assert torch.equal(c, d)
+    # fp32 input (the tiny workload) keeps its exact fp32 launch
+    wl1 = kvp_inputs.workload(1)
+    li1 = kvp_inputs.make_layer(wl1)
+    q1, k1 = to_dev(li1.q), to_dev(li1.k)
+    assert kvp.future_mass_workspace_bytes(q1, k1, wl1.window) == 0
+    lse1 = kvp.lse_fwd(q1, k1)
+    e = kvp.future_mass_chunked(q1, k1, lse1, wl1.window)
+    f = kvp.future_mass(q1, k1, lse1, wl1.window)
+    torch.cuda.synchronize()
+    assert torch.equal(e, f)
