@@ -132,3 +132,32 @@ def test_long_sequences_per_head_and_fp32_take_the_plain_launch():
     f = kvp.future_mass(q1, k1, lse1, wl1.window)
     torch.cuda.synchronize()
     assert torch.equal(e, f)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_short_shapes(seed):
+    """Seeded random short shapes (any grid the chunk plan makes: one to four
+    rounds, tiles with no future query, ragged S and windows), one unit
+    against the oracle and every unit through the w = 0 identity."""
+    rng = np.random.default_rng(9900 + seed)
+    B = int(rng.integers(1, 4))
+    Hkv = int(rng.integers(1, 9))
+    G = int(rng.integers(1, 5))
+    S = int(rng.integers(33, 9001))
+    D = int(rng.choice([64, 128]))
+    w = int(rng.integers(0, S // 2 + 1))
+    wl = kvp_inputs.workload(2).with_(B=B, Hq=Hkv * G, Hkv=Hkv, S=S, D=D, window=w,
+                                      seed=9900 + seed)
+    li = kvp_inputs.make_layer(wl)
+    q, k = to_dev(li.q), to_dev(li.k)
+    need = kvp.future_mass_workspace_bytes(q, k, w)
+    say(f"[chunked] random {seed}: B={B} Hkv={Hkv} G={G} S={S} D={D} w={w} workspace={need}")
+    lse = kvp.lse_fwd(q, k)
+    m = kvp.future_mass_chunked(q, k, lse, w)
+    m0 = kvp.future_mass_chunked(q, k, lse, 0).double().sum(dim=2).cpu().numpy()
+    torch.cuda.synchronize()
+    b, h = B - 1, int(rng.integers(0, Hkv))
+    ref = oracle.future_mass(li.q, li.k, w, b_only=b, h_only=h)
+    assert_mass(m.cpu().numpy()[b, h], ref["mass"][b, h], f"random {seed} b={b} h={h}")
+    assert np.all(m.cpu().numpy()[:, :, S - w:] == 0)
+    np.testing.assert_allclose(m0, G * S, rtol=1e-4)
