@@ -161,3 +161,17 @@ def test_random_short_shapes(seed):
     assert_mass(m.cpu().numpy()[b, h], ref["mass"][b, h], f"random {seed} b={b} h={h}")
     assert np.all(m.cpu().numpy()[:, :, S - w:] == 0)
     np.testing.assert_allclose(m0, G * S, rtol=1e-4)
+
+
+@pytest.mark.parametrize("S,w", [(1, 0), (2, 1), (31, 0), (32, 5), (33, 0), (257, 16), (600, 599)])
+def test_tiny_and_degenerate(S, w):
+    """Sequences of one to a few hundred tokens, windows up to S - 1: the whole
+    output against the oracle."""
+    wl = kvp_inputs.workload(2).with_(B=2, Hq=4, Hkv=2, S=S, D=64, window=w, seed=77 + S + w)
+    li = kvp_inputs.make_layer(wl)
+    q, k = to_dev(li.q), to_dev(li.k)
+    lse = kvp.lse_fwd(q, k)
+    m = kvp.future_mass_chunked(q, k, lse, w)
+    torch.cuda.synchronize()
+    ref = oracle.future_mass(li.q, li.k, w)
+    assert_mass(m.cpu().numpy(), ref["mass"], f"S={S} w={w}")
