@@ -101,23 +101,4 @@ __device__ __forceinline__ void xcd_map_units(int bid, int n_units, int n_per_un
   }
 }
 
-// Grids of exactly two 4-wave workgroups per CU, all resident at once: the
-// hardware hands out blocks 0 .. kNumCUs-1 one per CU, round-robin over the
-// XCDs, and blocks kNumCUs .. 2 kNumCUs-1 to the same CUs in the same order
-// (block b and block b + kNumCUs share a CU; measured on MI355X).  The first
-// half takes an XCD's tiles longest first and the second half the same list
-// in reverse, so every CU holds one long and one short tile of equal total
-// work.  Tiles are ranked as in xcd_map (tile 0 the longest); requires
-// n_units % 8 == 0 and n_units * n_tiles == 2 * kNumCUs.
-__host__ __device__ __forceinline__ void xcd_map_complement(int bid, int n_units, int& unit,
-                                                            int& tile) {
-  const int xcd = bid & 7;
-  const int per_xcd = n_units >> 3;
-  const int slot = (bid % kNumCUs) >> 3;              // CU slot within the XCD
-  const int items = 2 * kNumCUs / 8;                  // items of one XCD
-  const int i = bid < kNumCUs ? slot : items - 1 - slot;
-  tile = i / per_xcd;
-  unit = (i - tile * per_xcd) * 8 + xcd;
-}
-
 }  // namespace kvp

@@ -84,8 +84,6 @@ struct LseArgs {
   int n_wg;  // tiles of 8 (or 4) waves per (batch, KV head); paired mode:
              // block x takes tiles x' and n_wg - 1 - x' of its unit (x' the
              // tile index the block mapping gives)
-  int complement;  // 4-wave grids of exactly two workgroups per CU: the two
-                   // workgroups of a CU take a long and a short tile
   float c;   // scale * log2(e)
   // sparse mode (running top-k pattern): key j counts for query i iff
   // j <= i and (i - j < window or rank[j] <= cutoff[i]); [B, Hkv, S] each
@@ -128,8 +126,6 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
   // XCD; otherwise longest tiles first
   if constexpr (kPair)
     xcd_map_units(blockIdx.x, a.B * a.Hkv, (a.n_wg + 1) / 2, unit, tile);
-  else if (W == 4 && a.complement)
-    xcd_map_complement(blockIdx.x, a.B * a.Hkv, unit, tile);
   else
     xcd_map(blockIdx.x, a.B * a.Hkv, unit, tile);
   const int b = unit / a.Hkv;
@@ -590,9 +586,6 @@ hipError_t launch_lse_w(const void* q, const void* k, const Shape& sh, float sca
     pair = pairs * 20 >= rounds * kNumCUs * 19;
   }
   const int64_t blocks = units * (pair ? (a.n_wg + 1) / 2 : a.n_wg);
-  // two 4-wave workgroups per CU, all resident: pair a long and a short tile
-  // on every CU
-  a.complement = W == 4 && units % 8 == 0 && blocks == 2 * kNumCUs;
   if constexpr (W == 8) {
     if (pair)
       hipLaunchKernelGGL((lse_kernel<D, T, W, kSp, true, NB>), dim3((unsigned)blocks),
