@@ -42,8 +42,9 @@
 // The shift u of a row is the largest logit of its first key block (which
 // always holds key 0, valid for every row), so the running sum is >= 1 and
 // cannot underflow; it could only overflow if a later logit exceeded that by
-// more than ~88 (natural units).  Such rows are flagged (LSE = +inf) and
-// recomputed exactly by lse_fix_kernel, a max-then-sum pass per row.
+// more than ~88 (natural units).  Such rows are flagged and recomputed
+// exactly, after the sweep, by the wave that swept them: a max-then-sum pass
+// over the row's keys.
 #include <type_traits>
 
 #include "kvp_device.h"
@@ -85,6 +86,7 @@ struct LseArgs {
              // block x takes tiles x' and n_wg - 1 - x' of its unit (x' the
              // tile index the block mapping gives)
   float c;   // scale * log2(e)
+  float scale;  // the logit scale itself (the exact recomputation of flagged rows)
   // sparse mode (running top-k pattern): key j counts for query i iff
   // j <= i and (i - j < window or rank[j] <= cutoff[i]); [B, Hkv, S] each
   const int32_t* rank;
@@ -107,6 +109,49 @@ struct LTile<true> {
     return __uint_as_float(q[v & 3]);
   }
 };
+
+// Exact LSE of row i of query head gq (batch bb, KV head hh), by the 64
+// lanes of one wave: a max pass then a sum pass over the row's counted keys
+// (all of j <= i, or the sparse pattern), one key per lane at a time, in
+// fp32; an empty pattern gives -inf.  Lane 0 writes the result.
+template <int D, typename T, bool kSp>
+__device__ __forceinline__ void exact_row(const LseArgs& a, int bb, int hh, int gq, int i,
+                                          int lane) {
+  const int S = a.S;
+  const size_t row = (size_t)(bb * a.Hq + gq) * S + i;
+  const T* qi = static_cast<const T*>(a.q) + row * D;
+  const T* kh = static_cast<const T*>(a.k) + (size_t)(bb * a.Hkv + hh) * S * D;
+  u32x4_t q8[D / 8];  // the query row, bf16
+#pragma unroll
+  for (int c8 = 0; c8 < D / 8; ++c8) q8[c8] = load8(qi + c8 * 8);
+  auto logit = [&](int j) {
+    const T* kj = kh + (size_t)j * D;
+    float dot = 0.f;
+#pragma unroll
+    for (int c8 = 0; c8 < D / 8; ++c8) {
+      const bf16x8_t qe = __builtin_bit_cast(bf16x8_t, q8[c8]);
+      const bf16x8_t ke = __builtin_bit_cast(bf16x8_t, load8(kj + c8 * 8));
+#pragma unroll
+      for (int e8 = 0; e8 < 8; ++e8) dot = __builtin_fmaf((float)qe[e8], (float)ke[e8], dot);
+    }
+    return dot * a.scale;
+  };
+  const size_t kv_row = (size_t)(bb * a.Hkv + hh) * S;
+  const int cut = kSp ? a.cutoff[kv_row + i] : 0;
+  auto counts = [&](int j) {
+    if constexpr (kSp) return (i - j < a.window) || (a.rank[kv_row + j] <= cut);
+    return true;
+  };
+  float m = -__builtin_inff();
+  for (int j = lane; j <= i; j += 64)
+    if (counts(j)) m = fmaxf(m, logit(j));
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  float s = 0.f;
+  for (int j = lane; j <= i; j += 64)
+    if (counts(j)) s += __expf(logit(j) - m);
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  if (lane == 0) a.lse[row] = s > 0.f ? m + __logf(s) : -__builtin_inff();
+}
 
 template <int D, typename T, int W, bool kSp, bool kPair, int NB>
 __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
@@ -465,89 +510,44 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void lse_kernel(LseArgs a) {
   sum0 += __shfl_xor(sum0, 32);
   if constexpr (NB >= 2) sum1 += __shfl_xor(sum1, 32);
   if constexpr (NB == 3) sum2 += __shfl_xor(sum2, 32);
-  if (active && lane < 32) {
-    float* out = a.lse + (size_t)(b * a.Hq + h * G + g) * S;
-    const float l0 = (u0 + __log2f(sum0)) * kLn2;
-    const float l1 = (u1 + __log2f(sum1)) * kLn2;
-    // A non-finite sum (overflow) is flagged as +inf for the exact fallback;
-    // in sparse mode so is a sum too small to trust (the shift comes from
-    // every key of the first block, kept or not) or an empty pattern.
-    const float lo = kSp ? 0x1p-60f : 0.f;
-    const bool ok0 = sum0 < __builtin_inff() && l0 == l0 && (!kSp || sum0 >= lo);
-    const bool ok1 = sum1 < __builtin_inff() && l1 == l1 && (!kSp || sum1 >= lo);
-    if (iq0 < S) out[iq0] = ok0 ? l0 : __builtin_inff();
-    if (NB >= 2 && iq1 < S) out[iq1] = ok1 ? l1 : __builtin_inff();
-    if constexpr (NB == 3) {
-      const float l2 = (u2 + __log2f(sum2)) * kLn2;
-      const bool ok2 = sum2 < __builtin_inff() && l2 == l2;
-      if (iq2 < S) out[iq2] = ok2 ? l2 : __builtin_inff();
+  // A non-finite sum (overflow) flags the row; in sparse mode so does a sum
+  // too small to trust (the shift comes from every key of the first block,
+  // kept or not) or an empty pattern.  Flagged rows are written below.
+  const float lo = kSp ? 0x1p-60f : 0.f;
+  const float l0 = (u0 + __log2f(sum0)) * kLn2;
+  const bool ok0 = sum0 < __builtin_inff() && l0 == l0 && (!kSp || sum0 >= lo);
+  float l1 = 0.f, l2 = 0.f;
+  bool ok1 = true, ok2 = true;
+  if constexpr (NB >= 2) {
+    l1 = (u1 + __log2f(sum1)) * kLn2;
+    ok1 = sum1 < __builtin_inff() && l1 == l1 && (!kSp || sum1 >= lo);
+  }
+  if constexpr (NB == 3) {
+    l2 = (u2 + __log2f(sum2)) * kLn2;
+    ok2 = sum2 < __builtin_inff() && l2 == l2;
+  }
+  const int gq = h * G + g;  // query head
+  const bool own = active && lane < 32;
+  if (own) {
+    float* out = a.lse + (size_t)(b * a.Hq + gq) * S;
+    if (iq0 < S && ok0) out[iq0] = l0;
+    if (NB >= 2 && iq1 < S && ok1) out[iq1] = l1;
+    if (NB == 3 && iq2 < S && ok2) out[iq2] = l2;
+  }
+  // The wave's flagged rows, one after another, recomputed exactly.
+  uint64_t flagged[3] = {__ballot(own && iq0 < S && !ok0),
+                         NB >= 2 ? __ballot(own && iq1 < S && !ok1) : 0ull,
+                         NB == 3 ? __ballot(own && iq2 < S && !ok2) : 0ull};
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) {
+    uint64_t m = flagged[cb];
+    while (m) {
+      const int bit = __builtin_ctzll(m);
+      m &= m - 1;
+      exact_row<D, T, kSp>(a, b, h, gq, p0 + 32 * cb + bit, lane);
     }
   }
   }  // tiles of the workgroup
-}
-
-// Exact recomputation of the rows flagged +inf (or NaN) by lse_kernel: one
-// wave per flagged row, max pass then sum pass over the row's counted keys
-// (all of j <= i, or the sparse pattern), fp32; an empty pattern gives -inf.
-// Rows that are finite are left as they are; the kernel only reads them when
-// nothing is flagged.
-template <int D, typename T, bool kSp>
-__global__ __launch_bounds__(256) void lse_fix_kernel(LseArgs a, float scale) {
-  const int64_t rows = (int64_t)a.B * a.Hq * a.S;
-  const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int lane = threadIdx.x & 63;
-  bool flagged = false;
-  if (row < rows) {
-    const float v = a.lse[row];
-    flagged = !(v < __builtin_inff());
-  }
-  uint64_t mask = __ballot(flagged);
-  const int64_t wave_row0 = row - lane;
-  while (mask) {
-    const int bit = __builtin_ctzll(mask);
-    mask &= mask - 1;
-    const int64_t r = wave_row0 + bit;
-    const int i = (int)(r % a.S);
-    const int64_t bg = r / a.S;
-    const int gq = (int)(bg % a.Hq);
-    const int bb = (int)(bg / a.Hq);
-    const int hh = gq / a.G;
-    const T* qi = static_cast<const T*>(a.q) + ((size_t)(bb * a.Hq + gq) * a.S + i) * D;
-    const T* kh = static_cast<const T*>(a.k) + (size_t)(bb * a.Hkv + hh) * a.S * D;
-    float qv[D];
-#pragma unroll
-    for (int c8 = 0; c8 < D / 8; ++c8) {
-      const bf16x8_t e = __builtin_bit_cast(bf16x8_t, load8(qi + c8 * 8));
-#pragma unroll
-      for (int e8 = 0; e8 < 8; ++e8) qv[c8 * 8 + e8] = (float)e[e8];
-    }
-    auto logit = [&](int j) {
-      const T* kj = kh + (size_t)j * D;
-      float dot = 0.f;
-#pragma unroll
-      for (int c8 = 0; c8 < D / 8; ++c8) {
-        const bf16x8_t e = __builtin_bit_cast(bf16x8_t, load8(kj + c8 * 8));
-#pragma unroll
-        for (int e8 = 0; e8 < 8; ++e8) dot = __builtin_fmaf(qv[c8 * 8 + e8], (float)e[e8], dot);
-      }
-      return dot * scale;
-    };
-    const size_t kv_row = (size_t)(bb * a.Hkv + hh) * a.S;
-    const int cut = kSp ? a.cutoff[kv_row + i] : 0;
-    auto counts = [&](int j) {
-      if constexpr (kSp) return (i - j < a.window) || (a.rank[kv_row + j] <= cut);
-      return true;
-    };
-    float m = -__builtin_inff();
-    for (int j = lane; j <= i; j += 64)
-      if (counts(j)) m = fmaxf(m, logit(j));
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    float s = 0.f;
-    for (int j = lane; j <= i; j += 64)
-      if (counts(j)) s += __expf(logit(j) - m);
-    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == 0) a.lse[r] = s > 0.f ? m + __logf(s) : -__builtin_inff();
-  }
 }
 
 struct SparseIn {
@@ -573,6 +573,7 @@ hipError_t launch_lse_w(const void* q, const void* k, const Shape& sh, float sca
   a.S = sh.S;
   a.G = sh.G;
   a.c = scale * kLog2e;
+  a.scale = scale;
   const int64_t n_pb = (sh.S + C::kQueriesPerWave - 1) / C::kQueriesPerWave;
   a.n_wg = (int)((n_pb * sh.G + C::kWaves - 1) / C::kWaves);
   const int64_t units = (int64_t)sh.B * sh.Hkv;
@@ -597,12 +598,6 @@ hipError_t launch_lse_w(const void* q, const void* k, const Shape& sh, float sca
     hipLaunchKernelGGL((lse_kernel<D, T, W, kSp, false, NB>), dim3((unsigned)blocks),
                        dim3(C::kThreads), 0, stream, a);
   }
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const int64_t rows = (int64_t)sh.B * sh.Hq * sh.S;
-  const int64_t fix_blocks = (rows + 255) / 256;
-  hipLaunchKernelGGL((lse_fix_kernel<D, T, kSp>), dim3((unsigned)fix_blocks), dim3(256), 0, stream,
-                     a, scale);
   return hipGetLastError();
 }
 
