@@ -150,7 +150,12 @@ __device__ __forceinline__ float reduce_columns(f32x16_t& x, int l32) {
   return x[0] + __shfl_xor(x[0], 1);
 }
 
-template <int D, typename T, int W, int KB, bool kSeg, bool kPair>
+// kSeg: 0 future masses; 1 query-block mode, a block's sums reduced and
+// written after the step that ends it; 2 query-block mode with every block
+// edge after the last step of a stage (blocks of whole stages of pairs; the
+// sweep starts with as many uncomputed query blocks as that takes), so the
+// steps carry no reduction and keep their MFMA/VALU interleave.
+template <int D, typename T, int W, int KB, int kSeg, bool kPair>
 __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
   static_assert(KB == 2 || (KB == 1 && !kSeg), "one key block per wave: mass mode only");
   using C = MassCfg<D, W, KB>;
@@ -209,7 +214,11 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
   // hardware hands out workgroups.
   const int tile_last = kPair ? a.n_tiles - 1 - tile : tile;
   const int n_rep = tile_last != tile ? 2 : 1;
-  for (int rep = 0; rep < n_rep; ++rep) {
+  // unrolled: each tile's sweep is compiled for its own direction, which
+  // leaves the query-block modes room for their column reductions
+#pragma unroll
+  for (int rep = 0; rep < 2; ++rep) {
+  if (rep == n_rep) break;
   // the previous tile's column reduction has read the stage buffers
   if (rep) __syncthreads();
   // lane indices are re-derived per tile from an opaque copy of the thread
@@ -311,19 +320,48 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
     const int qb_last = (S - 1) / kBlk;
     const int qb_hi = chunked ? qb_last - chunk_qb_skip : qb_last;
     const int qb_lo = chunked ? qb_hi - chunk_qbs + 1 : q_first / kBlk;
-    const int n_pairs = (qb_hi - qb_lo + 1) * G;
+    // Stage-aligned query-block mode: pad_qb query blocks beyond the sweep's
+    // start (rows past S going down, below the first seen row going up),
+    // staged but computed by no wave, make the first block's pairs, and so
+    // every later block edge, end a stage.  seg_first: the block swept first.
+    int pad_qb = 0, seg_first = 0;
+    if constexpr (kSeg == 2) {
+      seg_first = ((asc ? qb_lo : qb_hi) * kBlk - a.seg_start) / a.seg_len;
+      const int edge_qb = (a.seg_start + (seg_first + (asc ? 1 : 0)) * a.seg_len) / kBlk;
+      const int first_qbs = asc ? edge_qb - qb_lo : qb_hi - edge_qb + 1;
+      while (((pad_qb + first_qbs) * G) % C::kSlots) ++pad_qb;  // < kSlots steps
+    }
+    const int n_pairs = (qb_hi - qb_lo + 1 + pad_qb) * G;
+    const int pad_pairs = pad_qb * G;
     // Pair p is (query block qb_first + qb_step * (p / G), head p % G).
     const int qb_step = asc ? 1 : -1;
-    const int qb_first = asc ? qb_lo : qb_hi;
+    const int qb_first = asc ? qb_lo - pad_qb : qb_hi + pad_qb;
     // query-block mode: after the last pair of a block (its last head, and
     // its first query block going down or its last going up) or the last
     // pair of the sweep, reduce and write
     auto maybe_flush = [&](int p) __attribute__((always_inline)) {
-      if constexpr (kSeg) {
+      if constexpr (kSeg == 1) {
         if (p >= n_pairs) return;
         const int qrow = (qb_first + qb_step * (p / G)) * kBlk - a.seg_start;
         const bool edge = asc ? (qrow + kBlk) % a.seg_len == 0 : qrow % a.seg_len == 0;
         if (p == n_pairs - 1 || (p % G == G - 1 && edge)) flush_seg(qrow / a.seg_len);
+      }
+    };
+    // stage-aligned query-block mode: after the last step of a stage, the
+    // block whose last pair that is, or the sweep's last block
+    int next_edge = 0, seg_cur = seg_first;
+    if constexpr (kSeg == 2) {
+      const int edge_qb = (a.seg_start + (seg_first + (asc ? 1 : 0)) * a.seg_len) / kBlk;
+      next_edge = (pad_qb + (asc ? edge_qb - qb_lo : qb_hi - edge_qb + 1)) * G - 1;
+    }
+    const int pairs_per_seg = a.seg_len / kBlk * G;
+    auto stage_flush = [&](int p_end) __attribute__((always_inline)) {
+      if constexpr (kSeg == 2) {
+        if (p_end >= next_edge || p_end >= n_pairs - 1) {
+          flush_seg(seg_cur);
+          seg_cur += qb_step;
+          next_edge += pairs_per_seg;
+        }
       }
     };
     const int n_stages = (n_pairs + C::kSlots - 1) / C::kSlots;
@@ -331,13 +369,15 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
     // those in [p_full_lo, p_full_hi) see every key with every query (no
     // mask), the others need the mask.  A partial last block (rows >= S) is
     // masked too.
+    // (the padding pairs lie before p_vis_lo)
     const int p_part = (S % kBlk) && qb_hi == qb_last ? G : 0;
     const int qb_full = (key0 + C::kKeysPerWave - 1 + w + kBlk - 1) / kBlk;
     const int qb_min = (key0 + w) / kBlk;  // first block with a query i >= key0 + w
-    const int p_vis_lo = asc ? min(n_pairs, (qb_min - qb_lo) * G) : 0;
-    const int p_vis_hi = asc ? n_pairs : max(0, min(n_pairs, (qb_hi - qb_min + 1) * G));
-    const int p_full_lo = asc ? min(n_pairs, (qb_full - qb_lo) * G) : p_part;
-    const int p_full_hi = asc ? n_pairs - p_part : max(0, min(n_pairs, (qb_hi - qb_full + 1) * G));
+    const int p_vis_lo = asc ? min(n_pairs, pad_pairs + max(0, qb_min - qb_lo) * G) : pad_pairs;
+    const int p_vis_hi = asc ? n_pairs : max(0, min(n_pairs, (qb_first - qb_min + 1) * G));
+    const int p_full_lo = asc ? min(n_pairs, pad_pairs + max(0, qb_full - qb_lo) * G)
+                              : pad_pairs + p_part;
+    const int p_full_hi = asc ? n_pairs - p_part : max(0, min(n_pairs, (qb_first - qb_full + 1) * G));
 
     // ---- staging: this wave copies pair kSlots * st + wave of stage st
     int ld_qb = qb_first + qb_step * (wave / G);
@@ -357,8 +397,8 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
     auto issue_loads = [&](int st, int half) __attribute__((always_inline)) {
       if (st * C::kSlots + wave >= n_pairs) return;
       if (half == 0 && lane < kBlk) {
-        const int i = ld_qb * kBlk + lane;
-        lse_pref = i < S ? lgroup[(size_t)ld_g * S + i] : 0.f;
+        const int i = ld_qb * kBlk + lane;  // < 0: padding below the sweep
+        lse_pref = (kSeg != 2 || i >= 0) && i < S ? lgroup[(size_t)ld_g * S + i] : 0.f;
       }
       const __amdgpu_buffer_rsrc_t qr = make_rsrc(qgroup + (size_t)ld_g * S * D, head_bytes);
       const uint32_t e0 = (uint32_t)(ld_qb * kBlk + l32) * D + 8 * h32;
@@ -378,7 +418,8 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
       if (lane < kBlk) {
         const int i = ld_qb * kBlk + lane;
         // no query (row beyond S or no pair): exp2(x - inf) = 0
-        ldst[wave * kBlk + lane] = (valid && i < S) ? lse_pref * kLog2e : __builtin_inff();
+        ldst[wave * kBlk + lane] =
+            (valid && (kSeg != 2 || i >= 0) && i < S) ? lse_pref * kLog2e : __builtin_inff();
       }
       advance(ld_qb, ld_g);  // the pair this wave stages in the next stage
     };
@@ -615,6 +656,7 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
       __syncthreads();
       step(t1, t0, p0 + C::kSlots - 1, nq, nl, 0);
       maybe_flush(p0 + C::kSlots - 1);
+      stage_flush(p0 + C::kSlots - 1);
     };
 
     if constexpr (C::kDeep) {
@@ -789,19 +831,32 @@ hipError_t launch_mass_w(const void* q, const void* k, const float* lse, const S
     const int64_t fill_blocks = min((n + 255) / 256, (int64_t)4 * kNumCUs);
     hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)fill_blocks), dim3(256), 0, stream, mass, n);
   }
-  if constexpr (W == 8 || KB == 1) {
-    if (pair) {
-      hipLaunchKernelGGL((mass_kernel<D, T, W, KB, kSeg, true>), dim3((unsigned)blocks),
+  // query-block mode with blocks of whole stages of pairs: the stage-aligned
+  // kernel (block edges after the last step of a stage)
+  const int g_unit = per_head ? 1 : sh.G / split;
+  const bool aligned = kSeg && (int64_t)seg.len / kBlk * g_unit % C::kSlots == 0;
+  auto go = [&](auto modec) -> hipError_t {
+    constexpr int kMode = decltype(modec)::value;
+    if constexpr (W == 8 || KB == 1) {
+      if (pair) {
+        hipLaunchKernelGGL((mass_kernel<D, T, W, KB, kMode, true>), dim3((unsigned)blocks),
+                           dim3(C::kThreads), 0, stream, a);
+        return hipGetLastError();
+      }
+    }
+    if constexpr (KB == 2) {
+      hipLaunchKernelGGL((mass_kernel<D, T, W, KB, kMode, false>), dim3((unsigned)blocks),
                          dim3(C::kThreads), 0, stream, a);
       return hipGetLastError();
     }
+    return hipErrorInvalidValue;  // one block per wave is chosen for paired grids only
+  };
+  if constexpr (kSeg) {
+    if (aligned) return go(std::integral_constant<int, 2>{});
+    return go(std::integral_constant<int, 1>{});
+  } else {
+    return go(std::integral_constant<int, 0>{});
   }
-  if constexpr (KB == 2) {
-    hipLaunchKernelGGL((mass_kernel<D, T, W, KB, kSeg, false>), dim3((unsigned)blocks),
-                       dim3(C::kThreads), 0, stream, a);
-    return hipGetLastError();
-  }
-  return hipErrorInvalidValue;  // one block per wave is chosen for paired grids only
 }
 
 // 512-key workgroups (one per CU) when the grid has at least two per CU.
