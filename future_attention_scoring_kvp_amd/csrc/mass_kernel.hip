@@ -323,12 +323,13 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
     // Stage-aligned query-block mode: pad_qb query blocks beyond the sweep's
     // start (rows past S going down, below the first seen row going up),
     // staged but computed by no wave, make the first block's pairs, and so
-    // every later block edge, end a stage.  seg_first: the block swept first.
-    int pad_qb = 0, seg_first = 0;
+    // every later block edge, end a stage.  seg_first: the block swept
+    // first; first_qbs: its query blocks in the sweep.
+    int pad_qb = 0, seg_first = 0, first_qbs = 0;
     if constexpr (kSeg == 2) {
       seg_first = ((asc ? qb_lo : qb_hi) * kBlk - a.seg_start) / a.seg_len;
       const int edge_qb = (a.seg_start + (seg_first + (asc ? 1 : 0)) * a.seg_len) / kBlk;
-      const int first_qbs = asc ? edge_qb - qb_lo : qb_hi - edge_qb + 1;
+      first_qbs = asc ? edge_qb - qb_lo : qb_hi - edge_qb + 1;
       while (((pad_qb + first_qbs) * G) % C::kSlots) ++pad_qb;  // < kSlots steps
     }
     const int n_pairs = (qb_hi - qb_lo + 1 + pad_qb) * G;
@@ -349,11 +350,7 @@ __global__ __launch_bounds__(kWave * W, 8 / W) void mass_kernel(MassArgs a) {
     };
     // stage-aligned query-block mode: after the last step of a stage, the
     // block whose last pair that is, or the sweep's last block
-    int next_edge = 0, seg_cur = seg_first;
-    if constexpr (kSeg == 2) {
-      const int edge_qb = (a.seg_start + (seg_first + (asc ? 1 : 0)) * a.seg_len) / kBlk;
-      next_edge = (pad_qb + (asc ? edge_qb - qb_lo : qb_hi - edge_qb + 1)) * G - 1;
-    }
+    int next_edge = (pad_qb + first_qbs) * G - 1, seg_cur = seg_first;
     const int pairs_per_seg = a.seg_len / kBlk * G;
     auto stage_flush = [&](int p_end) __attribute__((always_inline)) {
       if constexpr (kSeg == 2) {
