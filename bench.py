@@ -259,6 +259,34 @@ def mfma_probe(torch, blocks: int = 256, iters: int = 20000, reps: int = 5) -> d
                       f"register operands; best of {reps}"}
 
 
+def graph_replay(torch, step, reps: int, pairs_step: int, outs) -> dict:
+    """The same step captured once into a HIP graph and replayed: two checked
+    replays (outputs cleared first, then compared bit for bit with the eager
+    step's), then `reps` timed replays.  Reported beside the eager figures; the
+    JSON line's value stays the eager one."""
+    ref = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    equal = True
+    for _ in range(2):
+        for o in outs:
+            o.fill_(-3 if o.dtype == torch.int32 else float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        equal &= all(torch.equal(o, r) for o, r in zip(outs, ref))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / reps
+    equal &= all(torch.equal(o, r) for o, r in zip(outs, ref))
+    log(f"bench: graph replay {ms:.3f} ms per step, outputs equal to the eager step: {equal}")
+    return {"ms_per_step": round(ms, 4), "gpairs_per_s": round(pairs_step / (ms * 1e-3) / 1e9, 3),
+            "replays": reps, "outputs_equal_eager": bool(equal)}
+
+
 def keep_status(keep, mass, S, w, s, k, exact) -> str:
     """'exact' when the GPU keep-set equals the oracle's; 'tie-band' when it
     differs only among tokens whose oracle masses lie within the mass
@@ -408,6 +436,8 @@ def main() -> int:
                     help="whole KV heads of layer 0 in the oracle sample")
     ap.add_argument("--no-extras", action="store_true", help="skip the next_rows timings")
     ap.add_argument("--no-probe", action="store_true", help="skip the MFMA peak probe")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay of the step (timed after the eager steps)")
     for name, field, what in (("batch", "B", "batch"), ("hq", "Hq", "query heads"),
                               ("hkv", "Hkv", "KV heads"), ("seq", "S", "sequence length"),
                               ("dim", "D", "head dimension"), ("window", "window", "window w"),
@@ -567,6 +597,9 @@ def main() -> int:
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(wl.name)},
     }
+    if not args.no_graph:
+        out["graph"] = graph_replay(torch, step, args.steps, pairs_step,
+                                    (lse_all, mass_all, keep_all))
     if not args.no_probe:
         probe = mfma_probe(torch)
         out["mfma_probe"] = probe
