@@ -65,8 +65,9 @@
  *   - Logits are l(i, j) = scale * <q_i, k_j> with scale = 1/sqrt(d) when the
  *     `scale` argument is <= 0 ([LKV] §3 Eq. 1).
  *   - bf16 inputs are multiplied exactly and accumulated in fp32 on the
- *     matrix cores; fp32 inputs are first rounded to bf16 (round to nearest
- *     even) as they are loaded, so both dtypes run the same bf16 arithmetic.
+ *     matrix cores.  fp32 inputs are used as given: their logits are fp32
+ *     dot products on the vector ALUs (fused multiply-adds), for callers who
+ *     need the fp32 problem exactly rather than the matrix cores' speed.
  *   - Validation is synchronous and happens before any launch; a rejected
  *     call enqueues nothing.  No function prints, throws or aborts, and all
  *     are thread-safe; only kvp_select_topk_noalloc keeps state (its
