@@ -1,6 +1,6 @@
-"""Build tests/c_abi_driver (plain C against include/kvp.h, linked to the
+"""Build tests/c_abi_client (plain C against include/kvp.h, linked to the
 in-tree libkvp.so and the HIP runtime) with gcc.  Test infrastructure: the
-C-ABI driver tests run the binary; they never build it."""
+C-ABI client tests run the binary; they never build it."""
 from __future__ import annotations
 
 import os
@@ -9,8 +9,8 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "c_abi_driver.c")
-BIN = os.path.join(HERE, "c_abi_driver")
+SRC = os.path.join(HERE, "c_abi_client.c")
+BIN = os.path.join(HERE, "c_abi_client")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 
@@ -27,7 +27,7 @@ def build() -> str:
            "-Wl,-rpath," + os.path.join(ROCM, "lib")]
     proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if proc.returncode != 0:
-        raise RuntimeError(f"c_abi_driver build failed:\n{proc.stdout}")
+        raise RuntimeError(f"c_abi_client build failed:\n{proc.stdout}")
     os.replace(tmp, BIN)
     return BIN
 

@@ -1,14 +1,14 @@
 /*
- * c_abi_driver — libkvp.so used from C through include/kvp.h alone: no
- * Python, no torch.  Test infrastructure: tests/test_c_abi_driver.py builds
+ * c_abi_client — libkvp.so used from C through include/kvp.h alone: no
+ * Python, no torch.  Test infrastructure: tests/test_c_abi_client.py builds
  * nothing and runs the binary that the build step compiles next to this file.
  *
- *   c_abi_driver host
+ *   c_abi_client host
  *       Host-side checks only (no GPU call): ABI version, keep count,
  *       workspace sizes, status strings, and arguments that every stage
  *       rejects before launching anything.  Exit status 0 when all hold.
  *
- *   c_abi_driver run B Hq Hkv S D window n_sink top_k q.bin k.bin out_dir
+ *   c_abi_client run B Hq Hkv S D window n_sink top_k q.bin k.bin out_dir
  *       Reads Q [B,Hq,S,D] and K [B,Hkv,S,D] as bf16 bit patterns, runs the
  *       path on a stream of its own with device memory from hipMalloc —
  *       kvp_lse_fwd, kvp_future_mass, kvp_future_mass_chunked (with its
@@ -187,7 +187,7 @@ static int run(int argc, char** argv) {
   if (dmws) hipFree(dmws);
   if (dsws) hipFree(dsws);
   HIP_OK(hipStreamDestroy(st));
-  printf("c_abi_driver: ran %d x %d/%d heads x %d, workspaces %zu and %zu bytes\n", B, Hq, Hkv, S,
+  printf("c_abi_client: ran %d x %d/%d heads x %d, workspaces %zu and %zu bytes\n", B, Hq, Hkv, S,
          mws, sws);
   return failures;
 }
@@ -195,7 +195,7 @@ static int run(int argc, char** argv) {
 int main(int argc, char** argv) {
   if (argc >= 2 && strcmp(argv[1], "host") == 0) {
     const int f = host_checks();
-    printf("c_abi_driver: host checks %s\n", f ? "FAILED" : "ok");
+    printf("c_abi_client: host checks %s\n", f ? "FAILED" : "ok");
     return f ? 1 : 0;
   }
   if (argc >= 2 && strcmp(argv[1], "run") == 0) return run(argc, argv) ? 1 : 0;

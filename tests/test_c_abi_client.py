@@ -1,12 +1,12 @@
-"""libkvp.so from plain C (tests/c_abi_driver.c): the boundary needs nothing
+"""libkvp.so from plain C (tests/c_abi_client.c): the boundary needs nothing
 but include/kvp.h, device pointers from hipMalloc and a HIP stream.  On the
-CPU the driver checks the host functions and the argument checks that every
+CPU the client checks the host functions and the argument checks that every
 stage makes before launching anything; on the GPU it runs the path (causal
 LSE, LKV §3 Eq. 1 as reused by KVpop §3.2 Eq. 8; future mass, KVpop §3.1
 Eq. 2; keep-set, KVpop §3 Eq. 1 / Eq. 4 / Fig. 1) on inputs written by this
 test, and its outputs must equal the Python binding's bit for bit and the
 oracle's within the tolerances.  The binary is built by the build step
-(tests/build_c_driver.py), never by a test."""
+(tests/build_c_client.py), never by a test."""
 import os
 import subprocess
 
@@ -18,20 +18,20 @@ import oracle
 from parity import assert_keep, assert_lse, assert_mass, say
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-DRIVER = os.path.join(HERE, "c_abi_driver")
+CLIENT = os.path.join(HERE, "c_abi_client")
 
 
-def driver():
-    if not os.path.exists(DRIVER):
-        pytest.fail("tests/c_abi_driver is not built (run the build step)")
-    return DRIVER
+def client():
+    if not os.path.exists(CLIENT):
+        pytest.fail("tests/c_abi_client is not built (run the build step)")
+    return CLIENT
 
 
 def test_host_checks_from_c():
-    if not os.path.exists(DRIVER):   # on the CPU a missing build is made here
+    if not os.path.exists(CLIENT):   # on the CPU a missing build is made here
         import __graft_entry__
         __graft_entry__.build()
-    proc = subprocess.run([driver(), "host"], capture_output=True, text=True, timeout=60)
+    proc = subprocess.run([client(), "host"], capture_output=True, text=True, timeout=60)
     assert proc.returncode == 0, proc.stdout + proc.stderr
     assert "host checks ok" in proc.stdout
 
@@ -54,8 +54,8 @@ def test_path_from_c(tmp_path, B, Hq, Hkv, S, w, s, k):
     qf, kf = tmp_path / "q.bin", tmp_path / "k.bin"
     li.q.tofile(qf)
     li.k.tofile(kf)
-    say(f"[c driver] B={B} Hq={Hq} Hkv={Hkv} S={S} w={w} s={s} k={k}")
-    proc = subprocess.run([driver(), "run", *map(str, (B, Hq, Hkv, S, D, w, s, k)), str(qf),
+    say(f"[c client] B={B} Hq={Hq} Hkv={Hkv} S={S} w={w} s={s} k={k}")
+    proc = subprocess.run([client(), "run", *map(str, (B, Hq, Hkv, S, D, w, s, k)), str(qf),
                            str(kf), str(tmp_path)], capture_output=True, text=True, timeout=120)
     assert proc.returncode == 0, proc.stdout + proc.stderr
     n_keep = kvp.keep_count(S, w, s, k)
@@ -80,8 +80,8 @@ def test_path_from_c(tmp_path, B, Hq, Hkv, S, w, s, k):
     h = Hkv - 1
     ref = oracle.future_mass(li.q, li.k, w, b_only=0, h_only=h)
     G = Hq // Hkv
-    assert_lse(lse_c[:, h * G:(h + 1) * G], ref["lse"][:, h * G:(h + 1) * G], "C driver lse")
-    assert_mass(mass_c[:, h], ref["mass"][:, h], "C driver mass")
-    assert_mass(mass_cc[:, h], ref["mass"][:, h], "C driver chunked mass")
+    assert_lse(lse_c[:, h * G:(h + 1) * G], ref["lse"][:, h * G:(h + 1) * G], "C client lse")
+    assert_mass(mass_c[:, h], ref["mass"][:, h], "C client mass")
+    assert_mass(mass_cc[:, h], ref["mass"][:, h], "C client chunked mass")
     exact = oracle.select(ref["mass"][:, h:h + 1], w, s, k)
-    assert_keep(keep_c[:, h:h + 1], ref["mass"][:, h:h + 1], w, s, k, exact, "C driver keep")
+    assert_keep(keep_c[:, h:h + 1], ref["mass"][:, h:h + 1], w, s, k, exact, "C client keep")
