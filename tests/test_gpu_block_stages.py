@@ -68,3 +68,41 @@ def test_block_sums_attribute_to_rows(layer, start, L, per_head):
                         f"start={start} L={L} per head, rows >= {r0}")
         else:
             assert_mass(tail[h], ref["mass"][b, h], f"start={start} L={L}, rows >= {r0}")
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_blocks_on_paired_grids(seed):
+    """Seeded random block starts and lengths, windows and group sizes on
+    grids of paired tiles (two batches of 8 KV heads at S = 16384, or per
+    head): every result checked as above."""
+    rng = np.random.default_rng(6600 + seed)
+    G_ = int(rng.choice([1, 2, 4]))
+    per_head = bool(rng.integers(0, 2))
+    w = int(rng.integers(0, 600))
+    start = int(rng.integers(0, 200)) * 32
+    L = int(rng.choice([32, 64, 96, 128, 160, 256, 512, 1024]))
+    wl = kvp_inputs.workload(2).with_(B=2, Hq=8 * G_, Hkv=8, S=S, window=w, seed=6700 + seed)
+    li = kvp_inputs.make_layer(wl)
+    q, k = to_dev(li.q), to_dev(li.k)
+    lse = kvp.lse_fwd(q, k)
+    n = kvp.block_count(S, start, L)
+    say(f"[block stages] random {seed}: G={G_} per_head={per_head} w={w} start={start} L={L} "
+        f"({n} blocks)")
+    blk, fut = kvp.block_future_scores(q, k, lse, start, L, window=w, per_head=per_head)
+    torch.cuda.synchronize()
+    blk, fut = blk.cpu().numpy(), fut.cpu().numpy()
+    assert np.all(np.isfinite(blk)) and np.all(blk >= 0)
+    assert np.array_equal(fut, np.maximum.accumulate(blk[:, :, ::-1], axis=2)[:, :, ::-1])
+    rows = np.array([min(S, start + (t + 1) * L) - (start + t * L) for t in range(n)], np.float64)
+    heads = 1 if per_head else G_
+    b, h = 1, int(rng.integers(0, 8))
+    for t in sorted({0, n - 1}):
+        r0 = start + t * L
+        ref = oracle.future_mass(li.q, li.k, w, b_only=b, h_only=h, row_lo=r0,
+                                 want_per_head=per_head)
+        tail = (blk[b, :, t:].astype(np.float64) * (rows[t:] * heads)[None, :, None]).sum(axis=1)
+        if per_head:
+            assert_mass(tail[h * G_:(h + 1) * G_], ref["mass_heads"][b, h * G_:(h + 1) * G_],
+                        f"random {seed} per head, rows >= {r0}")
+        else:
+            assert_mass(tail[h], ref["mass"][b, h], f"random {seed}, rows >= {r0}")
