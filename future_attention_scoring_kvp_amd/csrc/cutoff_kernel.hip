@@ -52,16 +52,43 @@ constexpr int kDigits = 1 << kDigitBits;
 constexpr int kPasses = 32 / kDigitBits;
 
 // Stable LSD radix sort of one row, 4-bit digits.  One counting pass builds
-// the digit histograms of all eight passes; each pass then scatters the keys
-// chunk by chunk (one element per thread, in order): an element's slot is its digit's
-// running base + the count of equal digits in earlier waves of the chunk +
-// its rank among equal digits in its wave (four ballots give the lanes with
-// the same digit).  Passes whose digit is the same for every key are skipped.
-__global__ __launch_bounds__(kRankThreads) void rank_kernel(CutoffArgs a) {
+// the digit histograms of all eight passes; each pass then reorders the keys
+// chunk by chunk, kRows elements per thread (element c + 1024 e + thread of
+// chunk c).  An element's place among the chunk's equal digits is the count
+// of equal digits earlier in the chunk (earlier rows, and earlier waves of
+// its row: one exclusive scan per digit over the chunk's (row, wave) counts,
+// wave d scanning digit d) + its rank among equal digits in its wave (four
+// ballots give the lanes with the same digit).  The chunk is first ordered by
+// digit in LDS and then written out in that order, so each digit's run is
+// one contiguous, coalesced store.  Passes whose digit is the same for every
+// key are skipped.  The inverse permutation rank[pos[r]] = r is assembled in
+// LDS, a window of tokens at a time, and stored contiguously.
+constexpr int kRows = 4;
+constexpr int kChunkElems = kRows * kRankThreads;
+constexpr int kBatch = 8;        // global loads per thread in flight in the copy loops
+constexpr int kHistCopies = 4;   // histogram copies per wave (lane % 4): fewer same-address atomics
+constexpr int kRankWindow = 8192;       // tokens per LDS window of the inverse permutation
+constexpr int kRankWindowsMax = 4;      // longer rows scatter the ranks directly
+// one LDS buffer: the histogram copies, then a chunk's keys and indices, then
+// a window of ranks
+constexpr int kBigWords = kRankWindow > 2 * kChunkElems ? kRankWindow : 2 * kChunkElems;
+static_assert(kBigWords >= kRankWaves * kHistCopies * kPasses * kDigits, "histogram copies fit");
+static_assert(kRows * kRankWaves == kWave && kDigits == kRankWaves,
+              "one wave per digit scans the chunk's (row, wave) counts across its lanes");
+// Barrier for LDS traffic only: the global loads and stores in flight (the
+// next chunk's keys, the last chunk's stores) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+__global__ __launch_bounds__(kRankThreads, 8) void rank_kernel(CutoffArgs a) {
+  __shared__ uint32_t big[kBigWords];
   __shared__ int hist[kPasses][kDigits];
-  __shared__ int whist[kRankWaves][kPasses][kDigits];  // per-wave copies: fewer atomic collisions
-  __shared__ int wave_cnt[kRankWaves][kDigits];
-  __shared__ int base[kDigits];
+  __shared__ int cnt[kDigits][kRows * kRankWaves];  // per digit: count of each (row, wave)
+  __shared__ int loc[kDigits][kRows * kRankWaves];  // per digit: equal digits before each (row, wave)
+  __shared__ int tot[kDigits];                      // per digit: count in the chunk
+  __shared__ int base[2][kDigits];                  // per digit: first output slot (by chunk parity)
   const int S = a.S, s = a.s, n = S - s;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -75,26 +102,44 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(CutoffArgs a) {
   uint32_t* kb = ia + n;
   uint32_t* ib = kb + n;
 
-  for (int i = tid; i < kRankWaves * kPasses * kDigits; i += kRankThreads) (&whist[0][0][0])[i] = 0;
+  // ---- digit histograms of all passes
+  int* whist = reinterpret_cast<int*>(big);  // [wave][copy][pass][digit]
+  for (int i = tid; i < kRankWaves * kHistCopies * kPasses * kDigits; i += kRankThreads) whist[i] = 0;
   for (int t = tid; t < s; t += kRankThreads) rk[t] = -1;
   __syncthreads();
-  for (int i = tid; i < n; i += kRankThreads) {
-    const uint32_t key = order_key(m[s + i]);
-    ka[i] = key;
-    ia[i] = (uint32_t)(s + i);
+  int* my_hist = whist + (wave * kHistCopies + (lane & (kHistCopies - 1))) * kPasses * kDigits;
+  for (int i0 = tid; i0 < n; i0 += kBatch * kRankThreads) {
+    float mv[kBatch];
 #pragma unroll
-    for (int p = 0; p < kPasses; ++p)
-      atomicAdd(&whist[wave][p][(key >> (kDigitBits * p)) & (kDigits - 1)], 1);
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + u * kRankThreads;
+      mv[u] = i < n ? m[s + i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + u * kRankThreads;
+      if (i < n) {
+        const uint32_t key = order_key(mv[u]);
+        ka[i] = key;
+        ia[i] = (uint32_t)(s + i);
+#pragma unroll
+        for (int p = 0; p < kPasses; ++p)
+          atomicAdd(&my_hist[p * kDigits + ((key >> (kDigitBits * p)) & (kDigits - 1))], 1);
+      }
+    }
   }
   __syncthreads();
   if (tid < kPasses * kDigits) {
-    int tot = 0;
-    for (int w2 = 0; w2 < kRankWaves; ++w2) tot += (&whist[w2][0][0])[tid];
-    (&hist[0][0])[tid] = tot;
+    int t = 0;
+    for (int c = 0; c < kRankWaves * kHistCopies; ++c) t += whist[c * kPasses * kDigits + tid];
+    (&hist[0][0])[tid] = t;
   }
   __syncthreads();
 
-  for (int i = tid; i < kRankWaves * kDigits; i += kRankThreads) (&wave_cnt[0][0])[i] = 0;
+  // ---- the passes
+  uint32_t* lk = big;                // a chunk's keys, ordered by digit
+  uint32_t* li = big + kChunkElems;  // and their token indices
+  for (int i = tid; i < kDigits * kRows * kRankWaves; i += kRankThreads) (&cnt[0][0])[i] = 0;
   for (int p = 0; p < kPasses; ++p) {
     const int shift = kDigitBits * p;
     bool trivial = false;
@@ -104,59 +149,155 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(CutoffArgs a) {
     if (tid < kDigits) {
       int acc = 0;
       for (int d = 0; d < tid; ++d) acc += hist[p][d];
-      base[tid] = acc;
+      base[0][tid] = acc;
     }
-    // the next chunk's key and index are loaded while this one is scattered
-    uint32_t nkey = tid < n ? ka[tid] : 0u;
-    uint32_t nidx = tid < n ? ia[tid] : 0u;
-    for (int c = 0; c < n; c += kRankThreads) {
-      const int i = c + tid;
-      const bool valid = i < n;
-      const uint32_t key = nkey;
-      const uint32_t idx = nidx;
-      if (i + kRankThreads < n) {
-        nkey = ka[i + kRankThreads];
-        nidx = ia[i + kRankThreads];
-      }
-      const int d = (int)((key >> shift) & (kDigits - 1));
-      uint64_t same = __ballot(valid);
+    // the next chunk's keys and indices are loaded while this one is reordered
+    uint32_t nkey[kRows], nidx[kRows];
 #pragma unroll
-      for (int bbit = 0; bbit < kDigitBits; ++bbit) {
-        const uint64_t bal = __ballot(valid && ((d >> bbit) & 1));
-        same &= ((d >> bbit) & 1) ? bal : ~bal;
-      }
-      const int in_rank = __popcll(same & lt_mask);
-      // bases of this chunk final and the counts cleared (by wave 0, below)
-      __syncthreads();
-      if (valid && in_rank == 0) wave_cnt[wave][d] = __popcll(same);
-      __syncthreads();
-      if (valid) {
-        int before = base[d];
-        for (int w2 = 0; w2 < wave; ++w2) before += wave_cnt[w2][d];
-        kb[before + in_rank] = key;
-        ib[before + in_rank] = idx;
-      }
-      __syncthreads();
-      // wave 0 alone advances the bases and then clears the counts: both in
-      // its own program order, before the next chunk's first barrier
-      if (wave == 0) {
-        if (lane < kDigits) {
-          int tot = 0;
+    for (int e = 0; e < kRows; ++e) {
+      const int i = e * kRankThreads + tid;
+      nkey[e] = i < n ? ka[i] : 0u;
+      nidx[e] = i < n ? ia[i] : 0u;
+    }
+    int par = 0;
+    for (int c = 0; c < n; c += kChunkElems, par ^= 1) {
+      uint32_t key[kRows], idx[kRows];
+      int dig[kRows], in_rank[kRows];
+      uint64_t same[kRows];
 #pragma unroll
-          for (int w2 = 0; w2 < kRankWaves; ++w2) tot += wave_cnt[w2][lane];
-          base[lane] += tot;
+      for (int e = 0; e < kRows; ++e) {
+        const int i = c + e * kRankThreads + tid;
+        key[e] = nkey[e];
+        idx[e] = nidx[e];
+        if (i + kChunkElems < n) {
+          nkey[e] = ka[i + kChunkElems];
+          nidx[e] = ia[i + kChunkElems];
         }
-        for (int e = lane; e < kRankWaves * kDigits; e += kWave) (&wave_cnt[0][0])[e] = 0;
+        const bool valid = i < n;
+        dig[e] = (int)((key[e] >> shift) & (kDigits - 1));
+        same[e] = __ballot(valid);
+#pragma unroll
+        for (int bbit = 0; bbit < kDigitBits; ++bbit) {
+          const uint64_t bal = __ballot(valid && ((dig[e] >> bbit) & 1));
+          same[e] &= ((dig[e] >> bbit) & 1) ? bal : ~bal;
+        }
+        in_rank[e] = __popcll(same[e] & lt_mask);
+      }
+      // the previous chunk has read its counts (cleared them), its places and
+      // its LDS keys
+      lds_barrier();
+#pragma unroll
+      for (int e = 0; e < kRows; ++e)
+        if (c + e * kRankThreads + tid < n && in_rank[e] == 0)
+          cnt[dig[e]][e * kRankWaves + wave] = __popcll(same[e]);
+      lds_barrier();
+      {
+        // wave d: exclusive scan of digit d's counts over the chunk's
+        // (row, wave) pairs in element order
+        const int d = wave;
+        const int v = cnt[d][lane];
+        cnt[d][lane] = 0;
+        int incl = v;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+          const int u = __shfl_up(incl, off);
+          if (lane >= off) incl += u;
+        }
+        loc[d][lane] = incl - v;
+        if (lane == kWave - 1) tot[d] = incl;
+      }
+      lds_barrier();
+      // every wave: the chunk's digit runs start at lstart[d] in LDS and go to
+      // base[d] + (place - lstart[d]) in the output (lanes d < 16 hold digit d)
+      int lstart = 0, delta = 0;
+      {
+        const int t = lane < kDigits ? tot[lane] : 0;
+        int incl = t;
+#pragma unroll
+        for (int off = 1; off < kDigits; off <<= 1) {
+          const int u = __shfl_up(incl, off);
+          if (lane >= off) incl += u;
+        }
+        lstart = incl - t;
+        const int b = lane < kDigits ? base[par][lane] : 0;
+        delta = b - lstart;
+        if (wave == 0 && lane < kDigits) base[par ^ 1][lane] = b + t;
+      }
+#pragma unroll
+      for (int e = 0; e < kRows; ++e) {
+        // (the shuffle runs on every lane: a lane past the row still holds
+        // a digit's start for the others)
+        const int ls = __shfl(lstart, dig[e]);
+        if (c + e * kRankThreads + tid < n) {
+          const int place = ls + loc[dig[e]][e * kRankWaves + wave] + in_rank[e];
+          lk[place] = key[e];
+          li[place] = idx[e];
+        }
+      }
+      lds_barrier();
+      const int len = min(kChunkElems, n - c);
+#pragma unroll
+      for (int e = 0; e < kRows; ++e) {
+        const int place = e * kRankThreads + tid;
+        const uint32_t k2 = place < len ? lk[place] : 0u;
+        const int d = (int)((k2 >> shift) & (kDigits - 1));
+        const int slot = __shfl(delta, d) + place;
+        if (place < len) {
+          kb[slot] = k2;
+          ib[slot] = li[place];
+        }
       }
     }
     __syncthreads();
     uint32_t* tk = ka; ka = kb; kb = tk;
     uint32_t* ti = ia; ia = ib; ib = ti;
   }
-  for (int r = tid; r < n; r += kRankThreads) {
-    const uint32_t t = ia[r];
-    pos[r] = t;
-    rk[t] = r;
+
+  // ---- pos[r] = token of rank r; rank[token] = r
+  const int n_windows = (n + kRankWindow - 1) / kRankWindow;
+  if (n_windows > kRankWindowsMax) {
+    for (int r0 = tid; r0 < n; r0 += kBatch * kRankThreads) {
+      uint32_t tv[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int r = r0 + u * kRankThreads;
+        tv[u] = r < n ? ia[r] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int r = r0 + u * kRankThreads;
+        if (r < n) {
+          pos[r] = tv[u];
+          rk[tv[u]] = r;
+        }
+      }
+    }
+    return;
+  }
+  int* wrank = reinterpret_cast<int*>(big);
+  for (int wdw = 0; wdw < n_windows; ++wdw) {
+    const int t_lo = s + wdw * kRankWindow;  // tokens [t_lo, t_lo + kRankWindow)
+    for (int r0 = tid; r0 < n; r0 += kBatch * kRankThreads) {
+      uint32_t tv[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int r = r0 + u * kRankThreads;
+        tv[u] = r < n ? ia[r] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int r = r0 + u * kRankThreads;
+        if (r < n) {
+          if (wdw == 0) pos[r] = tv[u];
+          const int o = (int)tv[u] - t_lo;
+          if (o >= 0 && o < kRankWindow) wrank[o] = r;
+        }
+      }
+    }
+    __syncthreads();
+    const int w_len = min(kRankWindow, S - t_lo);
+    for (int o = tid; o < w_len; o += kRankThreads) rk[t_lo + o] = wrank[o];
+    __syncthreads();
   }
 }
 
@@ -238,69 +379,100 @@ __global__ __launch_bounds__(256) void cutoff_kernel(CutoffArgs a, int rows, int
   };
   int pchunk = 1 << 30, pnext_base = -(1 << 30);  // no window yet
   uint32_t plane = 0, pnext = 0;
+  // The cutoff after a new token ranked r_new < tau enters at query q (more
+  // than k eligible): the largest rank in (r_new, tau) whose token is
+  // already eligible (pos <= q - w), else r_new itself (the new token
+  // qualifies).
+  auto walk = [&](int r_new, int q) __attribute__((always_inline)) {
+    if constexpr (kWindowWalk) {
+      // long walks (k << n): 64 ranks per ballot, from the top window down
+      int hi_r = tau, result = r_new;
+      for (;;) {
+        const int want = hi_r - 1;  // highest untested rank
+        if (want <= r_new) break;
+        if (want < pchunk || want >= pchunk + 64) {
+          if (want >= pnext_base && want < pnext_base + 64) {  // the window loaded ahead
+            pchunk = pnext_base;
+            plane = pnext;
+          } else {  // place the window to end at want
+            pchunk = max(0, want - 63);
+            plane = load_win(pchunk);
+          }
+          pnext_base = pchunk - 64;
+          pnext = load_win(pnext_base);
+        }
+        const int r = pchunk + lane;
+        const uint64_t hit = __ballot(r > r_new && r < hi_r && r < n && (int)plane <= q - w);
+        if (hit) {
+          result = pchunk + 63 - (int)__builtin_clzll(hit);
+          break;
+        }
+        hi_r = pchunk;  // nothing in [pchunk, hi_r)
+        if (pchunk <= 0) break;
+      }
+      tau = result;
+    } else {
+      // short walks: rank by rank; the walk ends at r_new at the latest
+      // (also the loop bound)
+      for (;;) {
+        --tau;
+        if (tau <= r_new) break;
+        if (tau < pchunk) {
+          pchunk = max(0, tau - 63);
+          plane = load_win(pchunk);
+        }
+        const int p = (int)__builtin_amdgcn_readlane((int)plane, tau - pchunk);
+        if (p <= q - w) break;
+      }
+    }
+  };
   for (int q0 = q_begin; q0 < q_end; q0 += 64) {
     // ranks of the tokens that enter at q0 .. q0 + 63 (t = q - w), -2 if none
     const int t_l = q0 + lane - w;
     const int r_l = (t_l >= s && t_l < S && q0 + lane < q_end) ? rk[t_l] : -2;
-    int my_out = 0;
     const int nq = min(64, q_end - q0);
-    for (int j = 0; j < nq; ++j) {
-      const int q = q0 + j;
-      const int r_new = __builtin_amdgcn_readlane(r_l, j);
-      if (r_new >= 0) {
-        ++eligible;
-        if (eligible <= k) {
-          tau = max(tau, r_new);
-        } else if (r_new < tau) {
-          // The new cutoff: the largest rank in (r_new, tau) whose token is
-          // already eligible (pos <= q - w), else r_new itself (the new token
-          // qualifies).
-          if constexpr (kWindowWalk) {
-            // long walks (k << n): 64 ranks per ballot, from the top window
-            // down
-            int hi_r = tau, result = r_new;
-            for (;;) {
-              const int want = hi_r - 1;  // highest untested rank
-              if (want <= r_new) break;
-              if (want < pchunk || want >= pchunk + 64) {
-                if (want >= pnext_base && want < pnext_base + 64) {  // the window loaded ahead
-                  pchunk = pnext_base;
-                  plane = pnext;
-                } else {  // place the window to end at want
-                  pchunk = max(0, want - 63);
-                  plane = load_win(pchunk);
-                }
-                pnext_base = pchunk - 64;
-                pnext = load_win(pnext_base);
-              }
-              const int r = pchunk + lane;
-              const uint64_t hit = __ballot(r > r_new && r < hi_r && r < n && (int)plane <= q - w);
-              if (hit) {
-                result = pchunk + 63 - (int)__builtin_clzll(hit);
-                break;
-              }
-              hi_r = pchunk;  // nothing in [pchunk, hi_r)
-              if (pchunk <= 0) break;
-            }
-            tau = result;
-          } else {
-            // short walks: rank by rank; the walk ends at r_new at the latest
-            // (also the loop bound)
-            for (;;) {
-              --tau;
-              if (tau <= r_new) break;
-              if (tau < pchunk) {
-                pchunk = max(0, tau - 63);
-                plane = load_win(pchunk);
-              }
-              const int p = (int)__builtin_amdgcn_readlane((int)plane, tau - pchunk);
-              if (p <= q - w) break;
-            }
-          }
-        }
+    const int n_new = __popcll(__ballot(r_l >= 0));
+    if (eligible + n_new < k) {
+      // fewer than k eligible through the whole group: every query keeps
+      // all (cutoff S), and tau is the largest eligible rank so far
+      int mx = r_l;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off));
+      tau = max(tau, __builtin_amdgcn_readfirstlane(mx));
+      eligible += n_new;
+      if (lane < nq) out[q0 + lane] = S;
+      continue;
+    }
+    int my_out = 0;
+    if (eligible >= k) {
+      // more than k eligible at every new token: only a token ranked below
+      // the current cutoff moves it, so the sweep jumps from one such token
+      // to the next (a ballot against the cutoff of the moment), the
+      // queries in between keeping it
+      int j = 0;
+      for (;;) {
+        const uint64_t upd = __ballot(lane >= j && r_l >= 0 && r_l < tau);
+        const int jj = upd ? (int)__builtin_ctzll(upd) : nq;
+        my_out = (lane >= j && lane < jj) ? tau : my_out;
+        if (jj >= nq) break;
+        walk(__builtin_amdgcn_readlane(r_l, jj), q0 + jj);
+        my_out = lane == jj ? tau : my_out;
+        j = jj + 1;
       }
-      const int c = eligible < k ? S : tau;
-      my_out = lane == j ? c : my_out;
+      eligible += n_new;
+    } else {
+      for (int j = 0; j < nq; ++j) {
+        const int r_new = __builtin_amdgcn_readlane(r_l, j);
+        if (r_new >= 0) {
+          ++eligible;
+          if (eligible <= k)
+            tau = max(tau, r_new);
+          else if (r_new < tau)
+            walk(r_new, q0 + j);
+        }
+        const int c = eligible < k ? S : tau;
+        my_out = lane == j ? c : my_out;
+      }
     }
     if (lane < nq) out[q0 + lane] = my_out;
   }
