@@ -310,8 +310,13 @@ constexpr int kChunk = 1024;  // queries swept by one wave
 // order whose token pos[r] <= q0 - 1 - w, counted 64 ranks at a time with
 // ballots.  The chunk then runs the sequential update: a new token ranked
 // below the cutoff moves it down to the next rank whose token is eligible.
+constexpr int kDepth = 256;      // ranks below the cutoff a group step examines at most
+constexpr int kBackoffMax = 64;  // most groups swept token by token after too-deep ones
 template <bool kWindowWalk>
 __global__ __launch_bounds__(256) void cutoff_kernel(CutoffArgs a, int rows, int n_chunks) {
+  // per wave: the query within the current group at which each of the
+  // kDepth ranks below the cutoff becomes eligible
+  __shared__ int t_enter[4][kDepth];
   // wave-uniform state lives in scalar registers (readfirstlane tells the
   // compiler so), and the sweep's branches are scalar
   const int gw = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
@@ -319,6 +324,7 @@ __global__ __launch_bounds__(256) void cutoff_kernel(CutoffArgs a, int rows, int
   if (row >= rows) return;
   const int chunk = gw - row * n_chunks;
   const int lane = threadIdx.x & 63;
+  const int wave_in_wg = threadIdx.x >> 6;
   const int S = a.S, s = a.s, w = a.window, k = a.top_k, n = S - s;
   const int32_t* __restrict__ rk = a.rank + (size_t)row * S;
   const uint32_t* __restrict__ pos = a.ws + (size_t)row * 5 * n;
@@ -378,6 +384,7 @@ __global__ __launch_bounds__(256) void cutoff_kernel(CutoffArgs a, int rows, int
     return (r >= 0 && r < n) ? pos[r] : 0u;
   };
   int pchunk = 1 << 30, pnext_base = -(1 << 30);  // no window yet
+  int vec_skip = 0, backoff = 4;  // groups left to sweep token by token, and the next such run
   uint32_t plane = 0, pnext = 0;
   // The cutoff after a new token ranked r_new < tau enters at query q (more
   // than k eligible): the largest rank in (r_new, tau) whose token is
@@ -445,12 +452,63 @@ __global__ __launch_bounds__(256) void cutoff_kernel(CutoffArgs a, int rows, int
     }
     int my_out = 0;
     if (eligible >= k) {
-      // more than k eligible at every new token: only a token ranked below
-      // the current cutoff moves it, so the sweep jumps from one such token
-      // to the next (a ballot against the cutoff of the moment), the
-      // queries in between keeping it
+      // More than k eligible at every new token.  The cutoff c0 at the
+      // group's start is the k-th best eligible rank; at query j the k-th
+      // best is then the one with m_j eligible ranks between it and c0, m_j
+      // the new tokens ranked below c0 up to query j (each pushes the k-th
+      // place down by one).  Each lane (query) counts the eligible ranks
+      // down from c0 over a window of kDepth ranks, with the query at which
+      // each enters; if some query's answer lies deeper, the group is swept
+      // token by token instead, and so are the next few groups (4, doubling
+      // while the windows stay too shallow, at most kBackoffMax).
+      const uint64_t below = __ballot(r_l >= 0 && r_l < tau);
+      bool done = below == 0;  // no new token moves the cutoff
+      if (done) {
+        my_out = tau;
+      } else if (vec_skip > 0) {
+        --vec_skip;
+      } else {
+        const int c0 = tau;
+        const int m = __popcll(below & ((2ull << lane) - 1));  // through this lane's query
+        int hits_last = 0;  // ranks of the window eligible at the group's last query
+#pragma unroll
+        for (int u = 0; u < kDepth / 64; ++u) {
+          const int r = c0 - 64 * u - lane;
+          int t = 1 << 20;  // not eligible within the group
+          if (r >= 0) {
+            const int j = (int)pos[r] + w - q0;  // the query at which its token enters
+            t = j < 0 ? -1 : (j < nq ? j : 1 << 20);
+          }
+          t_enter[wave_in_wg][64 * u + lane] = t;
+          hits_last += __popcll(__ballot(t <= nq - 1));
+        }
+        // the last query needs m + 1 eligible ranks in the window
+        const int m_last = __popcll(below);
+        int cnt = 0, res = -1;  // eligible ranks passed; the answer's depth
+        for (int i0 = 0; i0 < kDepth && hits_last > m_last; i0 += 16) {
+#pragma unroll
+          for (int ii = 0; ii < 16; ++ii) {
+            const bool hit = t_enter[wave_in_wg][i0 + ii] <= lane;
+            res = (hit && cnt == m && res < 0) ? i0 + ii : res;
+            cnt += hit ? 1 : 0;
+          }
+          if (!__any(res < 0 && lane < nq)) break;
+        }
+        if (hits_last > m_last && !__any(res < 0 && lane < nq)) {
+          my_out = c0 - res;
+          tau = __builtin_amdgcn_readlane(c0 - res, nq - 1);
+          done = true;
+          backoff = 4;
+        } else {
+          vec_skip = backoff;
+          backoff = min(2 * backoff, kBackoffMax);
+        }
+      }
+      // otherwise only a token ranked below the current cutoff moves it: the
+      // sweep jumps from one such token to the next (a ballot against the
+      // cutoff of the moment), the queries in between keeping it
       int j = 0;
-      for (;;) {
+      while (!done) {
         const uint64_t upd = __ballot(lane >= j && r_l >= 0 && r_l < tau);
         const int jj = upd ? (int)__builtin_ctzll(upd) : nq;
         my_out = (lane >= j && lane < jj) ? tau : my_out;
