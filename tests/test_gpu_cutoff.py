@@ -53,6 +53,11 @@ def check(score32, window, n_sink, top_k):
     ("ties", 3, 300, 20, 4, 32), ("logmass", 2, 1000, 64, 4, 100), ("signed", 4, 777, 0, 0, 1),
     ("const", 2, 513, 16, 8, 40), ("ties", 1, 1, 0, 0, 1), ("ties", 2, 5, 0, 0, 5),
     ("logmass", 5, 4097, 128, 4, 512), ("signed", 3, 2000, 50, 3, 1999),
+    # long rows past the budget: groups of 64 queries taken one lane per query
+    # from a window of ranks below the cutoff, and (small k: windows too
+    # shallow at first) groups swept token by token
+    ("logmass", 2, 20000, 64, 4, 200), ("ties", 2, 20000, 0, 0, 5000),
+    ("signed", 2, 12345, 300, 2, 40),
 ])
 def test_cutoff_matches_oracle(kind, rows, S, w, s, k):
     check(scores(kind, rows, S, seed=S + k), w, s, k)
