@@ -58,6 +58,9 @@ def check(score32, window, n_sink, top_k):
     # shallow at first) groups swept token by token
     ("logmass", 2, 20000, 64, 4, 200), ("ties", 2, 20000, 0, 0, 5000),
     ("signed", 2, 12345, 300, 2, 40),
+    # the sort's inverse permutation: four LDS windows exactly, and past them
+    # (written directly)
+    ("logmass", 1, 32772, 100, 4, 3000), ("ties", 1, 40000, 64, 4, 20000),
 ])
 def test_cutoff_matches_oracle(kind, rows, S, w, s, k):
     check(scores(kind, rows, S, seed=S + k), w, s, k)
