@@ -55,21 +55,24 @@ __device__ __forceinline__ float dot_f32(const float (&x)[D], const float* y) {
   return (p[0] + p[1]) + (p[2] + p[3]);
 }
 
-// Online log-sum-exp state (running maximum m, sum s relative to it).
-__device__ __forceinline__ void lse_add(float& m, float& s, float x) {
+// Online log-sum-exp state (running maximum m, sum s relative to it).  The
+// sum is kept in fp64: with one dominant term (s near 1) a row's thousands of
+// terms below half an fp32 ulp of s would each be rounded away in an fp32 sum,
+// a relative loss of up to their total (1e-4 seen on a 7.5K-key row).
+__device__ __forceinline__ void lse_add(float& m, double& s, float x) {
   if (x > m) {
-    s = s * expf(m - x) + 1.f;
+    s = s * (double)expf(m - x) + 1.0;
     m = x;
   } else {
-    s += expf(x - m);
+    s += (double)expf(x - m);
   }
 }
-__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+__device__ __forceinline__ void lse_merge(float& m, double& s, float m2, double s2) {
   if (m2 > m) {
-    s = s * expf(m - m2) + s2;
+    s = s * (double)expf(m - m2) + s2;
     m = m2;
-  } else if (s2 > 0.f) {
-    s += s2 * expf(m2 - m);
+  } else if (s2 > 0.0) {
+    s += s2 * (double)expf(m2 - m);
   }
 }
 
@@ -99,7 +102,8 @@ __global__ __launch_bounds__(kF32Threads) void f32_lse_kernel(F32LseArgs a) {
   }
   int cut = 0;
   if (kSp && valid) cut = a.cutoff[(size_t)(b * a.Hkv + h) * S + i];
-  float m = -__builtin_inff(), s = 0.f;
+  float m = -__builtin_inff();
+  double s = 0.0;
   const int j_end = min(S, i0 + kRows);  // keys any row of the block reaches
   for (int j0 = 0; j0 < j_end; j0 += kF32Tile) {
     __syncthreads();
@@ -122,18 +126,20 @@ __global__ __launch_bounds__(kF32Threads) void f32_lse_kernel(F32LseArgs a) {
   }
 #pragma unroll
   for (int off = 1; off < R; off <<= 1) {
-    const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off);
+    const float m2 = __shfl_xor(m, off);
+    const double s2 = __shfl_xor(s, off);
     // lanes merge in the same order on both sides of each exchange
     if ((r & off) == 0)
       lse_merge(m, s, m2, s2);
     else {
-      float mm = m2, ss = s2;
+      float mm = m2;
+      double ss = s2;
       lse_merge(mm, ss, m, s);
       m = mm;
       s = ss;
     }
   }
-  if (valid && r == 0) a.lse[(size_t)bg * S + i] = s > 0.f ? m + logf(s) : -__builtin_inff();
+  if (valid && r == 0) a.lse[(size_t)bg * S + i] = s > 0.0 ? (float)((double)m + log(s)) : -__builtin_inff();
 }
 
 struct F32MassArgs {

@@ -64,3 +64,22 @@ def test_f32_differs_from_rounding_its_inputs():
     exact = oracle.future_mass(li.q, li.k, wl.window, f32_exact=True)["lse"]
     rounded = oracle.future_mass(li.q, li.k, wl.window)["lse"]
     assert np.abs(lse - exact).max() < 1e-5 < np.abs(lse - rounded).max()
+
+
+def test_f32_lse_with_one_dominant_key():
+    """A row whose sink key dominates (a logit about 13 above the rest) over
+    thousands of keys: each other term is below half an fp32 ulp of the
+    running sum, so the sum is kept in fp64.  An fp32 sum loses those terms:
+    2.8e-5 on this input (emulated on the CPU), 1e-4 on a 7.5K-key row of a
+    64-head layer; the fp64 sum stays below 1e-6."""
+    wl = kvp_inputs.workload(2).with_(B=1, Hq=2, Hkv=1, S=7886, D=128, window=100, n_sink=6,
+                                      top_k=3660, dtype="f32", seed=4343)
+    li = kvp_inputs.make_layer(wl)
+    say("[f32] one dominant key: B=1 Hq=2 Hkv=1 S=7886 D=128")
+    q, kk = to_dev(li.q), to_dev(li.k)
+    lse = kvp.lse_fwd(q, kk)
+    mass = kvp.future_mass(q, kk, lse, wl.window)
+    torch.cuda.synchronize()
+    ref = oracle.future_mass(li.q, li.k, wl.window, f32_exact=True)
+    assert np.abs(lse.cpu().numpy() - ref["lse"]).max() <= 1e-5
+    assert_mass(mass.cpu().numpy(), ref["mass"], "f32 mass, one dominant key")
