@@ -14,14 +14,17 @@
 //   rank_kernel    one workgroup per row: stable LSD radix sort of the
 //                  order-preserving keys in 4-bit digits (see below); then
 //                  rank[pos[r]] = r;
-//   cutoff_kernel  one wave per chunk of 1024 queries of a row.  Its first
-//                  state is counted directly from the ranks; then, since the
-//                  cutoff never rises once k tokens are eligible (a new token
-//                  can only push the k-th best to a better rank), a new token
-//                  ranked below the cutoff moves it down to the next rank
-//                  whose token is already eligible (pos[r] <= q - w).  Ranks
-//                  and positions are read 64 at a time into lanes and consumed
-//                  with uniform control flow; when k << n the walks are long
+//   cutoff_kernel  one wave per chunk of 1024 queries of a row, in groups
+//                  of 64.  Its first state is counted directly from the
+//                  ranks.  Groups with fewer than k eligible tokens keep all.
+//                  Past k, the cutoff never rises (a new token can only push
+//                  the k-th best to a better rank): each lane (query) counts
+//                  down from the group's first cutoff to its own k-th best
+//                  over a window of ranks (see the group step below), or,
+//                  where the window is too shallow, a new token ranked below
+//                  the cutoff moves it down to the next rank whose token is
+//                  already eligible (pos[r] <= q - w), token by token with
+//                  uniform control flow; when k << n those walks are long
 //                  and test 64 ranks per ballot.
 #include "kvp_device.h"
 #include "kvp_launch.h"
